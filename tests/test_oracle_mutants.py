@@ -1,0 +1,121 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in the oracle (on the CPU, by swapping one of its
+functions for a wrong version) and checks that at least one of the pins in
+``test_oracle_pins`` then fails.  Nothing here touches the GPU library.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import infini_oracle as orc
+from tests import test_oracle_pins as pins
+
+
+def _retrieval_transposed(q, M, z, eps):
+    sq = orc.elu_plus_one(q)
+    return (sq @ np.asarray(M).T) / (sq @ z + eps)[:, None]
+
+
+def _retrieval_no_z(q, M, z, eps):
+    sq = orc.elu_plus_one(q)
+    return (sq @ M) / (sq.sum(axis=1) + eps)[:, None]
+
+
+def _delta_wrong_sign(k, v, M, z, eps):
+    sk = orc.elu_plus_one(k)
+    r = (sk @ M) / (sk @ z + eps)[:, None]
+    return M + sk.T @ (v + r), z + sk.sum(axis=0)
+
+
+def _delta_reads_new_z(k, v, M, z, eps):
+    sk = orc.elu_plus_one(k)
+    z_new = z + sk.sum(axis=0)
+    r = (sk @ M) / (sk @ z_new + eps)[:, None]
+    return M + sk.T @ (v - r), z_new
+
+
+def _delta_transposed(k, v, M, z, eps):
+    sk = orc.elu_plus_one(k)
+    r = (sk @ np.asarray(M).T) / (sk @ z + eps)[:, None]
+    return M + sk.T @ (v - r), z + sk.sum(axis=0)
+
+
+def _linear_forgets_z(k, v, M, z):
+    sk = orc.elu_plus_one(k)
+    return M + sk.T @ v, np.asarray(z, dtype=np.float64)
+
+
+def _linear_raw_keys(k, v, M, z):
+    k = np.asarray(k, dtype=np.float64)
+    return M + k.T @ v, z + orc.elu_plus_one(k).sum(axis=0)
+
+
+def _attention_off_by_one(q, k, v, scale):
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    s = np.where(np.triu(np.ones((n, n), dtype=bool), k=2), -np.inf, s)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+def _attention_unscaled(q, k, v, scale):
+    return orc.__dict__["_orig_attention"](q, k, v, 1.0)
+
+
+def _gate_swapped(a_mem, a_dot, beta):
+    g = float(orc.sigmoid(np.array([beta]))[0])
+    return g * np.asarray(a_dot) + (1.0 - g) * np.asarray(a_mem)
+
+
+def _elu_without_one(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x, np.expm1(np.minimum(x, 0.0)))
+
+
+MUTANTS = {
+    "retrieval-transposed-M": ("memory_retrieval", _retrieval_transposed),
+    "retrieval-drops-z": ("memory_retrieval", _retrieval_no_z),
+    "delta-wrong-sign": ("memory_update_delta", _delta_wrong_sign),
+    "delta-reads-updated-z": ("memory_update_delta", _delta_reads_new_z),
+    "delta-transposed-M": ("memory_update_delta", _delta_transposed),
+    "linear-forgets-z": ("memory_update_linear", _linear_forgets_z),
+    "linear-binds-raw-keys": ("memory_update_linear", _linear_raw_keys),
+    "attention-mask-off-by-one": ("local_causal_attention", _attention_off_by_one),
+    "attention-unscaled": ("local_causal_attention", _attention_unscaled),
+    "gate-swapped": ("gate", _gate_swapped),
+    "elu-without-plus-one": ("elu_plus_one", _elu_without_one),
+}
+
+
+def _all_pins(rng):
+    """Every pin, called directly (each raises AssertionError on a mismatch)."""
+    yield lambda: pins.test_sigma_matches_torch_elu_plus_one(rng)
+    yield lambda: pins.test_local_attention_is_causal_sdpa(rng, 33, 64)
+    yield lambda: pins.test_local_attention_brute_force(rng)
+    yield lambda: pins.test_retrieval_is_linearised_attention_over_history(rng)
+    for u in ("linear", "delta"):
+        yield lambda u=u: pins.test_first_segment_reads_zero_memory(rng, u)
+        yield lambda u=u: pins.test_gate_limits(rng, u)
+        yield lambda u=u: pins.test_layer_matches_scalar_loops(rng, u)
+    yield lambda: pins.test_linear_state_is_sum_of_outer_products_for_any_segment_length(rng, 5)
+    yield lambda: pins.test_delta_leaves_an_existing_binding_unchanged(rng)
+    yield lambda: pins.test_delta_equals_linear_on_first_segment_and_z_is_shared(rng)
+    yield lambda: pins.test_delta_step_affine_form(rng)
+    yield lambda: pins.test_delta_step_brute_force(rng)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_a_planted_mistake_fails_a_pin(monkeypatch, name):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setitem(orc.__dict__, "_orig_attention", orc.local_causal_attention)
+    monkeypatch.setattr(orc, attr, fn)
+    rng = np.random.default_rng(99)
+    caught = []
+    for pin in _all_pins(rng):
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin)
+    assert caught, f"no pin caught the planted mistake {name!r}"
