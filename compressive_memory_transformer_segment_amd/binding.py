@@ -1,0 +1,222 @@
+"""Python binding of the C-ABI in ``include/infini_attn.h`` (ctypes).
+
+Argument marshalling only: every step of the layer runs in the HIP library.  Torch is
+used for device memory and streams; tensors are passed as raw device pointers together
+with the current HIP stream.  There is no fallback: if ``libinfini_attn.so`` is missing
+or the call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libinfini_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG_DIR), "include", "infini_attn.h")
+
+UPDATE = {"linear": 0, "delta": 1}
+DTYPE = {"bf16": 0, "f32": 1}
+TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OOM = 0, -1, -2, -3, -4
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("segment_len", ctypes.c_int32),
+        ("update", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+        ("max_window_segments", ctypes.c_int32),
+    ]
+
+
+class InfiniAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def exported_names() -> list[str]:
+    """Entry points the header declares (used by the load test)."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(infini_attn_[a-z_]+)\s*\(", text)))
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    fp = ctypes.POINTER(ctypes.c_float)
+    sig = {
+        "infini_attn_create": (ctypes.c_int, [ctypes.POINTER(Config), fp, vp, ctypes.POINTER(vp)]),
+        "infini_attn_forward_segment": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp]),
+        "infini_attn_forward_stream": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp]),
+        "infini_attn_forward_stream_ex": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "infini_attn_reset_state": (ctypes.c_int, [vp, vp]),
+        "infini_attn_get_state": (ctypes.c_int, [vp, vp, vp, vp]),
+        "infini_attn_set_state": (ctypes.c_int, [vp, vp, vp, vp]),
+        "infini_attn_set_beta": (ctypes.c_int, [vp, fp]),
+        "infini_attn_device_bytes": (i64, [vp]),
+        "infini_attn_window_tokens": (i64, [vp]),
+        "infini_attn_destroy": (ctypes.c_int, [vp]),
+        "infini_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().infini_attn_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise InfiniAttnError(fn, status, status_string(status))
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _float_array(values) -> ctypes.Array:
+    vals = [float(x) for x in values]
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+class InfiniAttention:
+    """One Infini-attention layer (per-head part): state M, z and gate on the GPU.
+
+    Q, K, V and outputs are contiguous [B, H, T, d] tensors on the current CUDA (HIP)
+    device, dtype bfloat16 (io_dtype="bf16") or float32 ("f32").
+    """
+
+    def __init__(self, batch: int, heads: int, head_dim: int, segment_len: int,
+                 update: str = "linear", io_dtype: str = "bf16", eps: float = 1e-6,
+                 softmax_scale: float = 0.0, beta=None, max_window_segments: int = 0, stream=None):
+        self._lib = load()
+        self.batch, self.heads, self.head_dim, self.segment_len = batch, heads, head_dim, segment_len
+        self.update, self.io_dtype = update, io_dtype
+        self.dtype = TORCH_DTYPE[io_dtype]
+        cfg = Config(batch, heads, head_dim, segment_len, UPDATE[update], DTYPE[io_dtype],
+                     eps, softmax_scale, max_window_segments)
+        beta = [0.0] * heads if beta is None else list(beta)
+        if len(beta) != heads:
+            raise ValueError("beta needs one value per head")
+        handle = ctypes.c_void_p()
+        _check("infini_attn_create",
+               self._lib.infini_attn_create(ctypes.byref(cfg), _float_array(beta), _stream_ptr(stream),
+                                            ctypes.byref(handle)))
+        self._h = handle
+
+    # ------------------------------------------------------------------ lifecycle
+    def close(self) -> None:
+        if getattr(self, "_h", None) and self._h.value:
+            _check("infini_attn_destroy", self._lib.infini_attn_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    # ------------------------------------------------------------------ compute
+    def _check_io(self, *tensors):
+        for t in tensors:
+            if t is None:
+                continue
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("tensors must be contiguous and on the GPU")
+
+    def _out_like(self, q, out):
+        if out is None:
+            out = torch.empty_like(q)
+        return out
+
+    def forward_stream(self, q, k, v, out=None, a_mem=None, a_dot=None, stream=None):
+        self._check_io(q, k, v, out, a_mem, a_dot)
+        out = self._out_like(q, out)
+        n = q.shape[2]
+        if a_mem is None and a_dot is None:
+            st = self._lib.infini_attn_forward_stream(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), n,
+                                                      _stream_ptr(stream))
+            _check("infini_attn_forward_stream", st)
+        else:
+            st = self._lib.infini_attn_forward_stream_ex(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                         _ptr(a_mem), _ptr(a_dot), n, _stream_ptr(stream))
+            _check("infini_attn_forward_stream_ex", st)
+        return out
+
+    def forward_segment(self, q, k, v, out=None, stream=None):
+        self._check_io(q, k, v, out)
+        out = self._out_like(q, out)
+        st = self._lib.infini_attn_forward_segment(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                   q.shape[2], _stream_ptr(stream))
+        _check("infini_attn_forward_segment", st)
+        return out
+
+    # ------------------------------------------------------------------ state
+    def reset_state(self, stream=None) -> None:
+        _check("infini_attn_reset_state", self._lib.infini_attn_reset_state(self._h, _stream_ptr(stream)))
+
+    def get_state(self, stream=None):
+        B, H, d = self.batch, self.heads, self.head_dim
+        M = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+        z = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        _check("infini_attn_get_state",
+               self._lib.infini_attn_get_state(self._h, _ptr(M), _ptr(z), _stream_ptr(stream)))
+        return M, z
+
+    def set_state(self, M, z, stream=None) -> None:
+        M = M.to(device="cuda", dtype=torch.float32).contiguous()
+        z = z.to(device="cuda", dtype=torch.float32).contiguous()
+        _check("infini_attn_set_state",
+               self._lib.infini_attn_set_state(self._h, _ptr(M), _ptr(z), _stream_ptr(stream)))
+
+    def set_beta(self, beta) -> None:
+        _check("infini_attn_set_beta", self._lib.infini_attn_set_beta(self._h, _float_array(beta)))
+
+    def device_bytes(self) -> int:
+        return int(self._lib.infini_attn_device_bytes(self._h))
+
+    def window_tokens(self) -> int:
+        return int(self._lib.infini_attn_window_tokens(self._h))

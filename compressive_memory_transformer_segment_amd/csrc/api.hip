@@ -1,0 +1,421 @@
+// Host side of the C-ABI declared in include/infini_attn.h: handle, state and workspace
+// ownership, argument validation, windowing of long streams, and the per-window launch
+// sequence (state pass -> chain -> fused attention/retrieval/gate).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "../../include/infini_attn.h"
+#include "kernels.hpp"
+
+#define INFINI_EXPORT extern "C" __attribute__((visibility("default")))
+
+struct infini_attn {
+  infini_attn_config_t cfg;
+  int device;
+  int D, N, NP, BH;
+  bool bf16, delta;
+  float scale;
+  int window;          // segments per window
+  int part_cap;        // chunk-partial slots per (b,h): >= W_call * chk_call
+  float* M;            // [B,H,D,D]
+  float* z;            // [B,H,D]
+  float* gate;         // [2H]: sigmoid(beta), 1 - sigmoid(beta)
+  void* ws_base;
+  size_t ws_bytes;
+  infini::Workspace ws;
+};
+
+namespace {
+
+std::mutex g_live_mu;
+std::unordered_set<const infini_attn*> g_live;
+
+bool live(const infini_attn* h) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return h && g_live.count(h);
+}
+
+constexpr size_t kDefaultWorkspaceBudget = size_t(512) << 20;   // bytes
+constexpr int kMaxWindow = 64;
+constexpr int kStateTargetWorkgroups = 512;
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = prev == dev || hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Bytes of workspace one window needs, per (b,h) pair, excluding the chunk partials.
+size_t unit_bytes(const infini_attn& h) {
+  const size_t D = h.D, DD = D * D;
+  size_t b = 0;
+  b += D * 4;                        // dz
+  b += DD * 4;                       // u_red
+  if (h.delta) b += DD * 4;          // g_red
+  b += 2 * 4;                        // counters
+  if (h.bf16) b += D * h.NP * 2;     // vt
+  b += DD * (h.bf16 ? 2 : 4);        // mt
+  b += D * 4;                        // zb
+  return b;
+}
+size_t part_bytes(const infini_attn& h) {   // one chunk-partial slot
+  const size_t D = h.D, DD = D * D;
+  return D * 4 + DD * 4 + (h.delta ? DD * 4 : 0);
+}
+
+int chunks_for(const infini_attn& h, int w_call) {
+  if (!h.bf16) return 1;
+  const int units = w_call * h.BH;
+  int chk = (kStateTargetWorkgroups + units - 1) / units;
+  chk = std::min(chk, 8);
+  chk = std::min(chk, std::max(1, h.NP / 64));
+  while (chk > 1 && w_call * chk > h.part_cap) --chk;
+  return std::max(chk, 1);
+}
+
+void carve(infini_attn& h) {
+  const size_t U = size_t(h.window) * h.BH;
+  const size_t P = size_t(h.part_cap) * h.BH;
+  const size_t D = h.D, DD = D * D;
+  char* p = static_cast<char*>(h.ws_base);
+  auto take = [&](size_t bytes) { char* r = p; p += align_up(bytes, 256); return r; };
+  h.ws.dz = reinterpret_cast<float*>(take(U * D * 4));
+  h.ws.u_red = reinterpret_cast<float*>(take(U * DD * 4));
+  h.ws.g_red = h.delta ? reinterpret_cast<float*>(take(U * DD * 4)) : nullptr;
+  h.ws.cnt = reinterpret_cast<uint32_t*>(take(2 * U * 4));
+  h.ws.vt = h.bf16 ? reinterpret_cast<uint16_t*>(take(U * D * h.NP * 2)) : nullptr;
+  h.ws.mt = take(U * DD * (h.bf16 ? 2 : 4));
+  h.ws.zb = reinterpret_cast<float*>(take(U * D * 4));
+  if (h.part_cap > 0) {
+    h.ws.dz_part = reinterpret_cast<float*>(take(P * D * 4));
+    h.ws.u_part = reinterpret_cast<float*>(take(P * DD * 4));
+    h.ws.g_part = h.delta ? reinterpret_cast<float*>(take(P * DD * 4)) : nullptr;
+  } else {
+    h.ws.dz_part = h.ws.u_part = h.ws.g_part = nullptr;
+  }
+  h.ws_bytes = static_cast<size_t>(p - static_cast<char*>(h.ws_base));
+}
+
+size_t layout_bytes(const infini_attn& h) {
+  const size_t U = size_t(h.window) * h.BH;
+  const size_t P = size_t(h.part_cap) * h.BH;
+  const size_t D = h.D, DD = D * D;
+  size_t b = 0;
+  auto add = [&](size_t x) { b += align_up(x, 256); };
+  add(U * D * 4);
+  add(U * DD * 4);
+  if (h.delta) add(U * DD * 4);
+  add(2 * U * 4);
+  if (h.bf16) add(U * D * h.NP * 2);
+  add(U * DD * (h.bf16 ? 2 : 4));
+  add(U * D * 4);
+  if (h.part_cap > 0) {
+    add(P * D * 4);
+    add(P * DD * 4);
+    if (h.delta) add(P * DD * 4);
+  }
+  return b;
+}
+
+void gate_values(const float* beta, int H, float* out) {
+  for (int i = 0; i < H; ++i) {
+    const double b = beta[i];
+    double g, omg;
+    if (std::isnan(b)) {
+      g = omg = b;
+    } else if (b >= 0) {
+      const double e = std::exp(-b);
+      g = 1.0 / (1.0 + e);
+      omg = e / (1.0 + e);
+    } else {
+      const double e = std::exp(b);
+      g = e / (1.0 + e);
+      omg = 1.0 / (1.0 + e);
+    }
+    out[i] = static_cast<float>(g);
+    out[H + i] = static_cast<float>(omg);
+  }
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_io(const infini_attn* h, const void* q, const void* k, const void* v, const void* out,
+             int64_t n_tokens) {
+  if (!q || !k || !v || !out) return INFINI_ERR_INVALID_ARG;
+  if (n_tokens < 1) return INFINI_ERR_INVALID_ARG;
+  const size_t esz = h->bf16 ? 2 : 4;
+  const size_t align = h->bf16 ? 16 : 4;
+  for (const void* p : {q, k, v, out})
+    if (reinterpret_cast<uintptr_t>(p) % align) return INFINI_ERR_INVALID_ARG;
+  const double elems = double(h->BH) * double(n_tokens) * double(h->D);
+  if (elems * esz > 9.0e18) return INFINI_ERR_INVALID_ARG;
+  const size_t bytes = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * esz;
+  for (const void* p : {q, k, v})
+    if (overlaps(out, bytes, p, bytes)) return INFINI_ERR_INVALID_ARG;
+  return INFINI_OK;
+}
+
+int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void* out, float* a_mem,
+               float* a_dot, int64_t n_tokens, void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  int rc = check_io(h, q, k, v, out, n_tokens);
+  if (rc) return rc;
+  const size_t part_bytes_out = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * 4;
+  for (const float* p : {a_mem, a_dot}) {
+    if (!p) continue;
+    if (reinterpret_cast<uintptr_t>(p) % 4) return INFINI_ERR_INVALID_ARG;
+    if (overlaps(p, part_bytes_out, out, part_bytes_out / (h->bf16 ? 2 : 1))) return INFINI_ERR_INVALID_ARG;
+  }
+  if (a_mem && a_dot && overlaps(a_mem, part_bytes_out, a_dot, part_bytes_out)) return INFINI_ERR_INVALID_ARG;
+  const int64_t S64 = (n_tokens + h->N - 1) / h->N;
+  if (S64 > (int64_t(1) << 30)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+  infini::WindowArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.a_mem = a_mem;
+  a.a_dot = a_dot;
+  a.B = h->cfg.batch;
+  a.H = h->cfg.heads;
+  a.D = h->D;
+  a.T = n_tokens;
+  a.N = h->N;
+  a.NP = h->NP;
+  a.S = static_cast<int>(S64);
+  a.n_last = static_cast<int>(n_tokens - (S64 - 1) * h->N);
+  a.delta = h->delta;
+  a.bf16 = h->bf16;
+  a.eps = h->cfg.eps;
+  a.scale = h->scale;
+  a.scale_log2 = static_cast<float>(double(h->scale) * 1.4426950408889634);
+  a.gate_g = h->gate;
+  a.gate_omg = h->gate + h->cfg.heads;
+  a.M = h->M;
+  a.z = h->z;
+  a.ws = h->ws;
+  for (int s0 = 0; s0 < a.S; s0 += h->window) {
+    a.s0 = s0;
+    a.W = std::min(h->window, a.S - s0);
+    a.chk = chunks_for(*h, a.W);
+    a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
+    a.chk = (h->N + a.ch - 1) / a.ch;
+    hipError_t e = hipSuccess;
+    if (h->delta) e = infini::launch_key_sums(a, st);
+    if (e == hipSuccess) e = infini::launch_state_pass(a, st);
+    if (e == hipSuccess) e = infini::launch_chain(a, st);
+    if (e == hipSuccess) e = infini::launch_attention(a, st);
+    if (e != hipSuccess) return INFINI_ERR_HIP;
+  }
+  return INFINI_OK;
+}
+
+}  // namespace
+
+INFINI_EXPORT const char* infini_attn_status_string(int status) {
+  switch (status) {
+    case INFINI_OK: return "ok";
+    case INFINI_ERR_INVALID_ARG: return "invalid argument";
+    case INFINI_ERR_UNSUPPORTED: return "unsupported configuration";
+    case INFINI_ERR_HIP: return "HIP runtime error";
+    case INFINI_ERR_OOM: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const float* beta_host,
+                                     void* hip_stream, infini_attn_t* out) {
+  if (!cfg || !beta_host || !out) return INFINI_ERR_INVALID_ARG;
+  *out = nullptr;
+  const infini_attn_config_t c = *cfg;
+  if (c.batch < 1 || c.heads < 1 || c.segment_len < 1) return INFINI_ERR_INVALID_ARG;
+  if (c.update != INFINI_UPDATE_LINEAR && c.update != INFINI_UPDATE_DELTA) return INFINI_ERR_INVALID_ARG;
+  if (c.io_dtype != INFINI_DTYPE_BF16 && c.io_dtype != INFINI_DTYPE_F32) return INFINI_ERR_INVALID_ARG;
+  if (!(c.eps >= 0.f) || !std::isfinite(c.eps)) return INFINI_ERR_INVALID_ARG;
+  if (std::isnan(c.softmax_scale) || std::isinf(c.softmax_scale)) return INFINI_ERR_INVALID_ARG;
+  if (c.head_dim != 64 && c.head_dim != 128) return INFINI_ERR_UNSUPPORTED;
+  if (int64_t(c.batch) * c.heads > (int64_t(1) << 20) || c.segment_len > (1 << 24)) return INFINI_ERR_UNSUPPORTED;
+
+  infini_attn* h = new (std::nothrow) infini_attn{};
+  if (!h) return INFINI_ERR_OOM;
+  h->cfg = c;
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return INFINI_ERR_HIP; }
+  h->D = c.head_dim;
+  h->N = c.segment_len;
+  h->NP = static_cast<int>(align_up(size_t(c.segment_len), 64));
+  h->BH = c.batch * c.heads;
+  h->bf16 = c.io_dtype == INFINI_DTYPE_BF16;
+  h->delta = c.update == INFINI_UPDATE_DELTA;
+  h->scale = c.softmax_scale > 0.f ? c.softmax_scale : static_cast<float>(1.0 / std::sqrt(double(c.head_dim)));
+
+  // window: as many segments as fit the workspace budget (at least one)
+  size_t budget = kDefaultWorkspaceBudget;
+  if (const char* env = std::getenv("INFINI_ATTN_WORKSPACE_MB")) {
+    const long mb = std::strtol(env, nullptr, 10);
+    if (mb > 0) budget = size_t(mb) << 20;
+  }
+  const size_t per_seg = unit_bytes(*h) * h->BH;
+  int w = static_cast<int>(std::max<size_t>(1, budget / std::max<size_t>(per_seg, 1)));
+  w = std::min(w, kMaxWindow);
+  if (c.max_window_segments > 0) w = std::min(w, c.max_window_segments);
+  h->window = w;
+  // chunk partials: enough slots for the chunking chosen at any window size
+  int cap = 0;
+  if (h->bf16) {
+    h->part_cap = 1 << 30;
+    for (int wc = 1; wc <= w; ++wc) {
+      const int chk = chunks_for(*h, wc);
+      if (chk > 1) cap = std::max(cap, wc * chk);
+    }
+  }
+  h->part_cap = cap;
+
+  DeviceGuard dg(h->device);
+  const size_t DD = size_t(h->D) * h->D;
+  const size_t m_bytes = size_t(h->BH) * DD * 4, z_bytes = size_t(h->BH) * h->D * 4;
+  const size_t ws_bytes = layout_bytes(*h);
+  if (hipMalloc(&h->M, m_bytes) != hipSuccess) { delete h; return INFINI_ERR_OOM; }
+  if (hipMalloc(&h->z, z_bytes) != hipSuccess) { (void)hipFree(h->M); delete h; return INFINI_ERR_OOM; }
+  if (hipMalloc(&h->gate, size_t(2) * c.heads * 4) != hipSuccess ||
+      hipMalloc(&h->ws_base, ws_bytes) != hipSuccess) {
+    (void)hipFree(h->M); (void)hipFree(h->z); (void)hipFree(h->gate);
+    delete h;
+    (void)hipGetLastError();
+    return INFINI_ERR_OOM;
+  }
+  carve(*h);
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.insert(h);
+  }
+  float* gv = new (std::nothrow) float[2 * c.heads];
+  if (!gv) { infini_attn_destroy(h); return INFINI_ERR_OOM; }
+  gate_values(beta_host, c.heads, gv);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipMemcpy(h->gate, gv, size_t(2) * c.heads * 4, hipMemcpyHostToDevice);
+  delete[] gv;
+  if (e == hipSuccess) e = hipMemsetAsync(h->M, 0, m_bytes, st);
+  if (e == hipSuccess) e = hipMemsetAsync(h->z, 0, z_bytes, st);
+  if (e == hipSuccess) e = hipMemsetAsync(h->ws.cnt, 0, size_t(2) * h->window * h->BH * 4, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) { infini_attn_destroy(h); return INFINI_ERR_HIP; }
+  *out = h;
+  return INFINI_OK;
+}
+
+INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
+  if (!h) return INFINI_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    if (!g_live.erase(h)) return INFINI_ERR_INVALID_ARG;
+  }
+  DeviceGuard dg(h->device);
+  const hipError_t e = hipDeviceSynchronize();
+  (void)hipFree(h->M);
+  (void)hipFree(h->z);
+  (void)hipFree(h->gate);
+  (void)hipFree(h->ws_base);
+  delete h;
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_forward_stream(infini_attn_t h, const void* q, const void* k, const void* v,
+                                             void* out, int64_t n_tokens, void* hip_stream) {
+  return run_stream(h, q, k, v, out, nullptr, nullptr, n_tokens, hip_stream);
+}
+
+INFINI_EXPORT int infini_attn_forward_stream_ex(infini_attn_t h, const void* q, const void* k, const void* v,
+                                                void* out, float* a_mem, float* a_dot, int64_t n_tokens,
+                                                void* hip_stream) {
+  return run_stream(h, q, k, v, out, a_mem, a_dot, n_tokens, hip_stream);
+}
+
+INFINI_EXPORT int infini_attn_forward_segment(infini_attn_t h, const void* q, const void* k, const void* v,
+                                              void* out, int32_t n_tokens, void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  if (n_tokens < 1 || n_tokens > h->N) return INFINI_ERR_INVALID_ARG;
+  return run_stream(h, q, k, v, out, nullptr, nullptr, n_tokens, hip_stream);
+}
+
+INFINI_EXPORT int infini_attn_reset_state(infini_attn_t h, void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const size_t DD = size_t(h->D) * h->D;
+  hipError_t e = hipMemsetAsync(h->M, 0, size_t(h->BH) * DD * 4, st);
+  if (e == hipSuccess) e = hipMemsetAsync(h->z, 0, size_t(h->BH) * h->D * 4, st);
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_get_state(infini_attn_t h, float* M, float* z, void* hip_stream) {
+  if (!live(h) || (!M && !z)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const size_t DD = size_t(h->D) * h->D;
+  hipError_t e = hipSuccess;
+  if (M) e = hipMemcpyAsync(M, h->M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
+  if (e == hipSuccess && z) e = hipMemcpyAsync(z, h->z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_set_state(infini_attn_t h, const float* M, const float* z, void* hip_stream) {
+  if (!live(h) || (!M && !z)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const size_t DD = size_t(h->D) * h->D;
+  hipError_t e = hipSuccess;
+  if (M) e = hipMemcpyAsync(h->M, M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
+  if (e == hipSuccess && z) e = hipMemcpyAsync(h->z, z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_set_beta(infini_attn_t h, const float* beta_host) {
+  if (!live(h) || !beta_host) return INFINI_ERR_INVALID_ARG;
+  const int H = h->cfg.heads;
+  float* gv = new (std::nothrow) float[2 * H];
+  if (!gv) return INFINI_ERR_OOM;
+  gate_values(beta_host, H, gv);
+  DeviceGuard dg(h->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(h->gate, gv, size_t(2) * H * 4, hipMemcpyHostToDevice);
+  delete[] gv;
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  const int64_t DD = int64_t(h->D) * h->D;
+  return int64_t(h->BH) * DD * 4 + int64_t(h->BH) * h->D * 4 + int64_t(2) * h->cfg.heads * 4 +
+         static_cast<int64_t>(h->ws_bytes);
+}
+
+INFINI_EXPORT int64_t infini_attn_window_tokens(infini_attn_t h) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  return int64_t(h->window) * h->N;
+}

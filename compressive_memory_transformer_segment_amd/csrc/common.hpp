@@ -1,0 +1,75 @@
+// Device helpers shared by the Infini-attention kernels (gfx950 / CDNA4).
+//
+// Conventions used across the kernels:
+//  * bf16 values travel as raw 16-bit patterns (uint16_t); conversion to float is a
+//    shift, conversion from float is round-to-nearest-even (the hardware cvt on gfx950).
+//  * MFMA 32x32x16 bf16 (v_mfma_f32_32x32x16_bf16): operand A is 32 rows x 16 k, lane l
+//    supplies row (l % 32) and the 8 consecutive k values 8*(l / 32) .. +7; operand B is
+//    16 k x 32 columns, lane l supplies column (l % 32) and the same 8 k values.  The
+//    32x32 fp32 result has 16 registers per lane: register r of lane l is row
+//    8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infini {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t packed) {  // element 0 of a pair
+  return __uint_as_float(packed << 16);
+}
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t packed) {  // element 1 of a pair
+  return __uint_as_float(packed & 0xffff0000u);
+}
+
+// float -> bf16 (round to nearest even), as raw bits.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+// Two floats -> one dword holding bf16(a) in the low half and bf16(b) in the high half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// sigma(x) = ELU(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise.
+__device__ __forceinline__ float elu_plus_one(float x) {
+  return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Split x into bf16 hi + bf16 lo with hi + lo == x to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+}  // namespace infini

@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI host code and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infini {
+
+// Device workspace for one window of W segments.  A "unit" is one (batch, head) pair on
+// one segment: u = s_local * (B*H) + b*H + h.
+struct Workspace {
+  float* dz;        // [U][D]        sum_t sigma(k_t) of the unit's segment
+  float* dz_part;   // [U][CHK][D]   per-chunk partial sums (CHK > 1)
+  float* u_part;    // [U][CHK][D][D] per-chunk (sigma(K)^T V)^T (CHK > 1)
+  float* u_red;     // [U][D][D]     (sigma(K)^T V)^T of the segment: [d_value][d_key]
+  float* g_part;    // [U][CHK][D][D] per-chunk sigma(K)^T diag(1/den) sigma(K) (delta, CHK > 1)
+  float* g_red;     // [U][D][D]     the same for the segment (delta): [d_key][d_key]
+  uint32_t* cnt;    // [2][U]        arrival counters of the chunked reductions (kept at 0)
+  uint16_t* vt;     // [U][D][NP]    V of the segment, transposed, bf16 (bf16 path)
+  void* mt;         // [U][D][D]     M_{s-1} transposed ([d_value][d_key]); bf16 or f32
+  float* zb;        // [U][D]        z_{s-1}
+};
+
+struct WindowArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* a_mem;      // optional fp32 [B,H,T,D]
+  float* a_dot;      // optional fp32 [B,H,T,D]
+  int B, H, D;
+  int64_t T;         // tokens in the call
+  int N;             // segment length
+  int NP;            // N rounded up to 64 (row stride of the transposed V)
+  int S;             // segments in the call
+  int n_last;        // tokens of the call's last segment
+  int s0;            // first segment of this window (call-relative)
+  int W;             // segments in this window
+  int chk;           // chunks per segment in the state pass
+  int ch;            // tokens per chunk (multiple of 64)
+  bool delta;
+  bool bf16;
+  float eps;
+  float scale_log2;  // softmax scale * log2(e)
+  float scale;       // softmax scale
+  const float* gate_g;    // [H] sigmoid(beta)
+  const float* gate_omg;  // [H] 1 - sigmoid(beta)
+  float* M;          // state [B,H,D,D]
+  float* z;          // state [B,H,D]
+  Workspace ws;
+
+  __host__ __device__ int units() const { return W * B * H; }
+  __host__ __device__ int seg_tokens(int s_local) const { return (s0 + s_local == S - 1) ? n_last : N; }
+};
+
+hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
+hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T
+hipError_t launch_chain(const WindowArgs& a, hipStream_t st);          // M/z recurrence
+hipError_t launch_attention(const WindowArgs& a, hipStream_t st);      // local attn + retrieval + gate
+
+}  // namespace infini

@@ -1,0 +1,411 @@
+// State pass: the per-segment terms of the memory recurrence, for every segment of a
+// window at once (they depend on the segment's own K and V only; for the delta rule also
+// on z_{s-1}, a prefix sum of the key sums).
+//
+//   dz_s = sum_t sigma(k_t)                                   (Eq. 8, z line)
+//   U_s  = sigma(K_s)^T V_s, stored transposed as U_s^T [d_value][d_key]   (Eq. 8)
+//   G_s  = sigma(K_s)^T diag(1 / (sigma(K_s) z_{s-1} + eps)) sigma(K_s)   (Eq. 9 rearranged)
+//
+// Eq. 9 is M_s = M_{s-1} + sigma(K)^T V - sigma(K)^T diag(1/den) sigma(K) M_{s-1}
+//             = M_{s-1} - G_s M_{s-1} + U_s,
+// an exact rearrangement (associativity of the products) that moves the N-long
+// contractions out of the sequential chain: the chain only multiplies d x d matrices.
+// (Architecture summary of arXiv 2404.07143, section 3.4 "Compressive Memory", Eq. 8-9.)
+//
+// bf16 path: sigma(K) is formed in fp32 and split into bf16 hi + lo, so the bf16 matrix
+// cores give fp32-accurate sums (V is exact in bf16); G uses hi*hi + hi*lo + lo*hi.
+// The pass also writes V transposed ([d][t], bf16) for the attention kernel's P V product.
+// A segment is cut into `chk` chunks, one workgroup each; the last workgroup to finish a
+// unit adds the chunk partials in chunk order (deterministic) and writes the unit's sums.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infini {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSub = 64;                  // tokens per sub-tile
+constexpr int kRowPad = kSub + 8;         // LDS row stride in bf16 elements (144 bytes)
+
+enum Mode { MODE_KEYSUM = 0, MODE_LINEAR = 1, MODE_DELTA = 2 };
+
+struct UnitPos {
+  int s_local, bh, b, h, n;
+  int64_t tok0;  // first token of the segment in the call
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const WindowArgs& a, int u) {
+  UnitPos p;
+  const int BH = a.B * a.H;
+  p.s_local = u / BH;
+  p.bh = u % BH;
+  p.b = p.bh / a.H;
+  p.h = p.bh % a.H;
+  p.n = a.seg_tokens(p.s_local);
+  p.tok0 = static_cast<int64_t>(a.s0 + p.s_local) * a.N;
+  return p;
+}
+
+// z_{s-1} for unit (s_local, bh): the state's z plus the key sums of the window's earlier
+// segments, added in segment order (the chain adds them in the same order).
+template <int D>
+__device__ void z_before(const WindowArgs& a, const UnitPos& p, float* zs) {
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float z = a.z[static_cast<int64_t>(p.bh) * D + d];
+    for (int s = 0; s < p.s_local; ++s) z += a.ws.dz[(static_cast<int64_t>(s) * a.B * a.H + p.bh) * D + d];
+    zs[d] = z;
+  }
+}
+
+// Last-arriver bookkeeping.  Every thread's partial stores are made visible device-wide
+// before thread 0 counts the chunk in; the workgroup that brings the count to chk resets
+// the counter and returns true.
+__device__ bool arrive_last(uint32_t* cnt, int chk) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(cnt, 1u);
+    s_last = (prev == static_cast<uint32_t>(chk - 1));
+    if (s_last) atomicExch(cnt, 0u);
+  }
+  __syncthreads();
+  if (s_last) __threadfence();
+  return s_last != 0;
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
+  constexpr int DQ = D / 8;              // threads per token row (8 features each)
+  constexpr int TQ = kThreads / DQ;      // row groups
+  constexpr int RPT = kSub / TQ;         // rows per thread per sub-tile (D/32)
+  constexpr int NBLK = (D / 32) * (D / 32);
+  constexpr int NB = NBLK / 4;           // 32x32 output blocks per wave
+  constexpr bool kMat = MODE != MODE_KEYSUM;
+  constexpr bool kDelta = MODE == MODE_DELTA;
+
+  __shared__ __align__(16) uint16_t sk_hi[kMat ? D : 1][kRowPad];
+  __shared__ __align__(16) uint16_t sk_lo[kMat ? D : 1][kRowPad];
+  __shared__ __align__(16) uint16_t vts[kMat ? D : 1][kRowPad];
+  __shared__ __align__(16) uint16_t dk_hi[kDelta ? D : 1][kRowPad];
+  __shared__ __align__(16) uint16_t dk_lo[kDelta ? D : 1][kRowPad];
+  __shared__ float zprev[kDelta ? D : 1];
+  __shared__ float red[TQ][D];
+
+  const int u = blockIdx.x / a.chk;
+  const int c = blockIdx.x % a.chk;
+  const UnitPos p = unit_pos(a, u);
+  const int tid = threadIdx.x;
+  const int dq = tid % DQ, tq = tid / DQ;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  if constexpr (kDelta) {
+    z_before<D>(a, p, zprev);
+    __syncthreads();
+  }
+
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
+  const int64_t row_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D + dq * 8;
+
+  float zacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
+  f32x16 acc_u[kMat ? NB : 1];
+  f32x16 acc_g[kDelta ? NB : 1];
+#pragma unroll
+  for (int k = 0; k < (kMat ? NB : 1); ++k) acc_u[k] = zero16();
+#pragma unroll
+  for (int k = 0; k < (kDelta ? NB : 1); ++k) acc_g[k] = zero16();
+
+  const int t_begin = c * a.ch;
+  const int t_end = min(t_begin + a.ch, p.n);
+  for (int ts = t_begin; ts < t_end; ts += kSub) {
+    // ---- load RPT rows x 8 features of K (and V), form sigma(K) in fp32
+    float sk[RPT][8];
+    u32x4 vraw[kMat ? RPT : 1];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int t = ts + tq * RPT + r;
+      u32x4 kr = {0u, 0u, 0u, 0u};
+      if (t < p.n) kr = ld16(kg + row_base + static_cast<int64_t>(t) * D);
+      if constexpr (kMat) {
+        u32x4 vr = {0u, 0u, 0u, 0u};
+        if (t < p.n) vr = ld16(vg + row_base + static_cast<int64_t>(t) * D);
+        vraw[r] = vr;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = bf16lo_to_f32(kr[i]), x1 = bf16hi_to_f32(kr[i]);
+        sk[r][2 * i] = (t < p.n) ? elu_plus_one(x0) : 0.f;
+        sk[r][2 * i + 1] = (t < p.n) ? elu_plus_one(x1) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zacc[i] += sk[r][i];
+    }
+    if constexpr (kMat) {
+      float dsc[RPT];
+      if constexpr (kDelta) {
+        // den_t = sigma(k_t) . z_{s-1} + eps; the row is spread over DQ consecutive lanes
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          float part = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) part += sk[r][i] * zprev[dq * 8 + i];
+#pragma unroll
+          for (int off = DQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+          const int t = ts + tq * RPT + r;
+          dsc[r] = (t < p.n) ? 1.f / (part + a.eps) : 0.f;
+        }
+      }
+      // ---- write the transposed hi/lo operands into LDS: row = feature, column = token
+      const int col = tq * RPT;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = dq * 8 + i;
+        uint16_t hi[RPT], lo[RPT], vv[RPT], dh[RPT], dl[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          split_bf16(sk[r][i], hi[r], lo[r]);
+          const uint32_t w = vraw[r][i >> 1];
+          vv[r] = static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xffffu));
+          if constexpr (kDelta) split_bf16(sk[r][i] * dsc[r], dh[r], dl[r]);
+        }
+        if constexpr (RPT == 4) {
+          st8(&sk_hi[row][col], u32x2{hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16)});
+          st8(&sk_lo[row][col], u32x2{lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16)});
+          st8(&vts[row][col], u32x2{vv[0] | (uint32_t(vv[1]) << 16), vv[2] | (uint32_t(vv[3]) << 16)});
+          if constexpr (kDelta) {
+            st8(&dk_hi[row][col], u32x2{dh[0] | (uint32_t(dh[1]) << 16), dh[2] | (uint32_t(dh[3]) << 16)});
+            st8(&dk_lo[row][col], u32x2{dl[0] | (uint32_t(dl[1]) << 16), dl[2] | (uint32_t(dl[3]) << 16)});
+          }
+        } else {
+          static_assert(RPT == 2, "D must be 64 or 128");
+          *reinterpret_cast<uint32_t*>(&sk_hi[row][col]) = hi[0] | (uint32_t(hi[1]) << 16);
+          *reinterpret_cast<uint32_t*>(&sk_lo[row][col]) = lo[0] | (uint32_t(lo[1]) << 16);
+          *reinterpret_cast<uint32_t*>(&vts[row][col]) = vv[0] | (uint32_t(vv[1]) << 16);
+          if constexpr (kDelta) {
+            *reinterpret_cast<uint32_t*>(&dk_hi[row][col]) = dh[0] | (uint32_t(dh[1]) << 16);
+            *reinterpret_cast<uint32_t*>(&dk_lo[row][col]) = dl[0] | (uint32_t(dl[1]) << 16);
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- V^T to the workspace, positions permuted inside each 16-token group so that
+      // the attention kernel's A operand of P V is one 16-byte read (see attention.hip).
+      {
+        uint16_t* vt = a.ws.vt + static_cast<int64_t>(u) * D * a.NP + ts;
+        for (int id = tid; id < D * 8; id += kThreads) {
+          const int row = id >> 3, cc = id & 7;  // destination chunk cc: 8 positions
+          const int g = cc >> 1, hh = cc & 1;
+          const u32x2 lo8 = ld8(&vts[row][16 * g + 4 * hh]);
+          const u32x2 hi8 = ld8(&vts[row][16 * g + 8 + 4 * hh]);
+          st16(vt + static_cast<int64_t>(row) * a.NP + 8 * cc, u32x4{lo8[0], lo8[1], hi8[0], hi8[1]});
+        }
+      }
+
+      // ---- MFMA: each wave owns NB 32x32 blocks of the d x d outputs
+#pragma unroll
+      for (int ks = 0; ks < kSub / 16; ++ks) {
+        const int kc = 16 * ks + 8 * hl;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          const int blk = wave * NB + kb;
+          const int ib = blk / (D / 32), jb = blk % (D / 32);
+          // U^T block (rows = value features ib, columns = key features jb)
+          const bf16x8 av = as_bf16x8(ld16(&vts[32 * ib + l32][kc]));
+          const bf16x8 bkh = as_bf16x8(ld16(&sk_hi[32 * jb + l32][kc]));
+          const bf16x8 bkl = as_bf16x8(ld16(&sk_lo[32 * jb + l32][kc]));
+          acc_u[kb] = mfma32x32x16(av, bkh, acc_u[kb]);
+          acc_u[kb] = mfma32x32x16(av, bkl, acc_u[kb]);
+          if constexpr (kDelta) {
+            // G block (rows = key features ib, columns = key features jb)
+            const bf16x8 ah = as_bf16x8(ld16(&sk_hi[32 * ib + l32][kc]));
+            const bf16x8 al = as_bf16x8(ld16(&sk_lo[32 * ib + l32][kc]));
+            const bf16x8 bh = as_bf16x8(ld16(&dk_hi[32 * jb + l32][kc]));
+            const bf16x8 bl = as_bf16x8(ld16(&dk_lo[32 * jb + l32][kc]));
+            acc_g[kb] = mfma32x32x16(ah, bh, acc_g[kb]);
+            acc_g[kb] = mfma32x32x16(ah, bl, acc_g[kb]);
+            acc_g[kb] = mfma32x32x16(al, bh, acc_g[kb]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- key sums: reduce the per-thread partials over the row groups (in group order)
+  const bool want_dz = MODE != MODE_DELTA;
+  if (want_dz) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
+    __syncthreads();
+  }
+
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const bool direct = a.chk == 1;
+  float* dz_dst = direct ? a.ws.dz + static_cast<int64_t>(u) * D
+                         : a.ws.dz_part + (static_cast<int64_t>(u) * a.chk + c) * D;
+  if (want_dz) {
+    for (int d = tid; d < D; d += kThreads) {
+      float s = 0.f;
+      for (int g = 0; g < TQ; ++g) s += red[g][d];
+      dz_dst[d] = s;
+    }
+  }
+  float* u_dst = direct ? a.ws.u_red + u * DD : a.ws.u_part + (static_cast<int64_t>(u) * a.chk + c) * DD;
+  float* g_dst = direct ? a.ws.g_red + u * DD : a.ws.g_part + (static_cast<int64_t>(u) * a.chk + c) * DD;
+  if constexpr (kMat) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      const int blk = wave * NB + kb;
+      const int ib = blk / (D / 32), jb = blk % (D / 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * ib + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const int col = 32 * jb + l32;
+        u_dst[row * D + col] = acc_u[kb][r];
+        if constexpr (kDelta) g_dst[row * D + col] = acc_g[kb][r];
+      }
+    }
+  }
+  if (direct) return;
+
+  // ---- the last chunk of the unit to finish adds the partials in chunk order
+  uint32_t* cnt = a.ws.cnt + (MODE == MODE_KEYSUM ? 0 : a.units()) + u;
+  if (!arrive_last(cnt, a.chk)) return;
+  if (want_dz) {
+    for (int d = tid; d < D; d += kThreads) {
+      float s = 0.f;
+      for (int cc = 0; cc < a.chk; ++cc) s += __builtin_nontemporal_load(&a.ws.dz_part[(static_cast<int64_t>(u) * a.chk + cc) * D + d]);
+      a.ws.dz[static_cast<int64_t>(u) * D + d] = s;
+    }
+  }
+  if constexpr (kMat) {
+    for (int e = tid * 4; e < DD; e += kThreads * 4) {
+      f32x4 su = {0.f, 0.f, 0.f, 0.f}, sg = {0.f, 0.f, 0.f, 0.f};
+      for (int cc = 0; cc < a.chk; ++cc) {
+        const int64_t off = (static_cast<int64_t>(u) * a.chk + cc) * DD + e;
+        su += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ws.u_part + off));
+        if constexpr (kDelta) sg += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ws.g_part + off));
+      }
+      *reinterpret_cast<f32x4*>(a.ws.u_red + u * DD + e) = su;
+      if constexpr (kDelta) *reinterpret_cast<f32x4*>(a.ws.g_red + u * DD + e) = sg;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ float32 I/O path
+// One workgroup per unit (no chunking).  Thread (bi, bj) owns a TB x TB block of U (and
+// G); tokens are staged in LDS 32 at a time.
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kThreads) void k_state_f32(const WindowArgs a) {
+  constexpr int TB = D / 16;
+  constexpr int TT = 32;
+  __shared__ float sk[TT][D];
+  __shared__ float vv[TT][D];
+  __shared__ float dsc[TT];
+  __shared__ float zprev[D];
+
+  const int u = blockIdx.x;
+  const UnitPos p = unit_pos(a, u);
+  const int tid = threadIdx.x;
+  const int bi = tid / 16, bj = tid % 16;
+  if (DELTA) z_before<D>(a, p, zprev);
+
+  const float* kg = static_cast<const float*>(a.k);
+  const float* vg = static_cast<const float*>(a.v);
+  const int64_t base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
+
+  float accu[TB][TB], accg[TB][TB];
+  for (int i = 0; i < TB; ++i)
+    for (int j = 0; j < TB; ++j) accu[i][j] = accg[i][j] = 0.f;
+  float zsum = 0.f;
+
+  for (int t0 = 0; t0 < p.n; t0 += TT) {
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kThreads) {
+      const int t = e / D, d = e % D;
+      const bool ok = t0 + t < p.n;
+      sk[t][d] = ok ? elu_plus_one(kg[base + static_cast<int64_t>(t0 + t) * D + d]) : 0.f;
+      vv[t][d] = ok ? vg[base + static_cast<int64_t>(t0 + t) * D + d] : 0.f;
+    }
+    __syncthreads();
+    if (DELTA && tid < TT) {
+      float den = 0.f;
+      for (int d = 0; d < D; ++d) den += sk[tid][d] * zprev[d];
+      dsc[tid] = 1.f / (den + a.eps);
+    }
+    if (tid < D)
+      for (int t = 0; t < TT; ++t) zsum += sk[t][tid];
+    __syncthreads();
+    for (int t = 0; t < TT; ++t) {
+      float ks[TB], vs[TB], ds[TB];
+      for (int i = 0; i < TB; ++i) {
+        ks[i] = sk[t][bi * TB + i];
+        vs[i] = vv[t][bj * TB + i];
+        if (DELTA) ds[i] = sk[t][bj * TB + i] * dsc[t];
+      }
+      for (int i = 0; i < TB; ++i)
+        for (int j = 0; j < TB; ++j) {
+          accu[i][j] += ks[i] * vs[j];
+          if (DELTA) accg[i][j] += ks[i] * ds[j];
+        }
+    }
+  }
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  for (int i = 0; i < TB; ++i)
+    for (int j = 0; j < TB; ++j) {
+      // U^T [value feature][key feature]; G [key feature][key feature]
+      const int64_t e = static_cast<int64_t>(bi * TB + i) * D + bj * TB + j;
+      const int64_t et = static_cast<int64_t>(bj * TB + j) * D + bi * TB + i;
+      a.ws.u_red[u * DD + et] = accu[i][j];
+      if (DELTA) a.ws.g_red[u * DD + e] = accg[i][j];
+    }
+  if (!DELTA && tid < D) a.ws.dz[static_cast<int64_t>(u) * D + tid] = zsum;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_keysum_f32(const WindowArgs a) {
+  const int u = blockIdx.x;
+  const UnitPos p = unit_pos(a, u);
+  const float* kg = static_cast<const float*>(a.k);
+  const int64_t base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float s = 0.f;
+    for (int t = 0; t < p.n; ++t) s += elu_plus_one(kg[base + static_cast<int64_t>(t) * D + d]);
+    a.ws.dz[static_cast<int64_t>(u) * D + d] = s;
+  }
+}
+
+template <int D>
+hipError_t launch_state_d(const WindowArgs& a, hipStream_t st, int mode) {
+  if (a.bf16) {
+    const dim3 grid(a.units() * a.chk);
+    if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_state_bf16<D, MODE_KEYSUM>), grid, dim3(kThreads), 0, st, a);
+    else if (mode == MODE_LINEAR) hipLaunchKernelGGL((k_state_bf16<D, MODE_LINEAR>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_state_bf16<D, MODE_DELTA>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    const dim3 grid(a.units());
+    if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_keysum_f32<D>), grid, dim3(kThreads), 0, st, a);
+    else if (mode == MODE_LINEAR) hipLaunchKernelGGL((k_state_f32<D, false>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_state_f32<D, true>), grid, dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st) {
+  return a.D == 128 ? launch_state_d<128>(a, st, MODE_KEYSUM) : launch_state_d<64>(a, st, MODE_KEYSUM);
+}
+
+hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st) {
+  const int mode = a.delta ? MODE_DELTA : MODE_LINEAR;
+  return a.D == 128 ? launch_state_d<128>(a, st, mode) : launch_state_d<64>(a, st, mode);
+}
+
+}  // namespace infini

@@ -13,9 +13,10 @@ experiments).  The pages' data sets (PG19, passkey text, BookSum) and trained we
 are not available; these draws stand in for them.
 
 Recipe (fixed, so any segment of any stream can be regenerated on its own):
-* every (seed, batch index, segment index, tensor id) gets its own
-  ``numpy.random.SeedSequence``; tensor ids: 0 = Q, 1 = K, 2 = V, 3 = per-token scale;
-* Q, K, V entries are N(0, 1) / sqrt(d), drawn as float32 with shape [H, n, d];
+* every (seed, batch index, segment index, tensor id, head) gets its own
+  ``numpy.random.SeedSequence``; tensor ids: 0 = Q, 1 = K, 2 = V, 3 = per-token scale
+  (drawn once per (seed, batch, segment), head slot 0);
+* Q, K, V entries are N(0, 1) / sqrt(d), drawn as float32, [n, d] per head;
 * a per-token scale exp(U(ln 0.5, ln 2)), one per (batch, token), multiplies Q, K and V
   of every head before rounding (the 32-head, 512K-token workload);
 * bf16 workloads round the float32 draws to bf16 with round-to-nearest-even;
@@ -29,6 +30,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -129,20 +131,49 @@ def planted_pair(w: Workload):
     return k_star, v_star
 
 
-def segment_inputs(w: Workload, b: int, s: int, plant: bool | None = None):
-    """Q, K, V of batch element b, segment s: three float32 arrays [H, n, d]."""
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        _POOL = concurrent.futures.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+def segment_inputs(w: Workload, b: int, s: int, plant: bool | None = None, heads=None):
+    """Q, K, V of batch element b, segment s: three float32 arrays [len(heads), n, d].
+
+    ``heads`` selects a subset of heads (default: all); each head's draws depend only on
+    (seed, b, s, tensor, head), so a subset equals the same rows of the full draw.
+    """
     n = w.segment_len_of(s)
     if n <= 0:
         raise ValueError(f"segment {s} is past the end of a {w.n_tokens}-token stream")
+    heads = list(range(w.heads)) if heads is None else list(heads)
     inv = np.float32(1.0 / math.sqrt(w.head_dim))
-    qkv = [(_rng(w.seed, b, s, t).standard_normal((w.heads, n, w.head_dim), dtype=np.float32) * inv)
-           for t in (TENSOR_Q, TENSOR_K, TENSOR_V)]
+    scale = None
     if w.token_scale:
         lo, hi = math.log(0.5), math.log(2.0)
-        scale = np.exp(_rng(w.seed, b, s, TENSOR_SCALE).uniform(lo, hi, size=n)).astype(np.float32)
-        qkv = [x * scale[None, :, None] for x in qkv]
-    if w.io_dtype == "bf16":
-        qkv = [round_to_bf16(x) for x in qkv]
+        scale = np.exp(_rng(w.seed, b, s, TENSOR_SCALE, 0).uniform(lo, hi, size=n)).astype(np.float32)
+    qkv = [np.empty((len(heads), n, w.head_dim), dtype=np.float32) for _ in range(3)]
+
+    def draw(job):
+        t, i = job
+        x = _rng(w.seed, b, s, t, heads[i]).standard_normal((n, w.head_dim), dtype=np.float32) * inv
+        if scale is not None:
+            x = x * scale[:, None]
+        if w.io_dtype == "bf16":
+            x = round_to_bf16(x)
+        qkv[t][i] = x
+
+    jobs = [(t, i) for t in (TENSOR_Q, TENSOR_K, TENSOR_V) for i in range(len(heads))]
+    if len(heads) * n * w.head_dim >= (1 << 18):
+        list(_pool().map(draw, jobs))
+    else:
+        for job in jobs:
+            draw(job)
     if (w.plant if plant is None else plant):
         k_star, v_star = planted_pair(w)
         q, k, v = qkv

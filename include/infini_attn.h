@@ -1,0 +1,131 @@
+/*
+ * infini_attn.h -- C-ABI of the Infini-attention layer forward for AMD MI355X (gfx950).
+ *
+ * The method: "Leave No Context Behind: Efficient Infinite Context Transformers with
+ * Infini-attention" (arXiv 2404.07143), as stated in the architecture summary on
+ * paper-graph-ui.vercel.app, section 3.4 "Detailed, Sentence-Based Technical Breakdown".
+ * For each segment of N tokens, per (batch element, head):
+ *
+ *   A_dot = softmax(scale * Q K^T, causal inside the segment) V          (Eq. 6)
+ *   A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1} + eps)                  (Eq. 7)
+ *   A     = sigmoid(beta_h) A_mem + (1 - sigmoid(beta_h)) A_dot           (Eq. 10)
+ *   linear: M_s = M_{s-1} + sigma(K)^T V                                  (Eq. 8)
+ *   delta:  M_s = M_{s-1} + sigma(K)^T (V - sigma(K) M_{s-1} / (sigma(K) z_{s-1} + eps))  (Eq. 9)
+ *   z_s = z_{s-1} + sum_t sigma(K_t)                                      (Eq. 8, both rules)
+ *
+ * with sigma = ELU + 1 (alpha = 1).  The state (M, z) is carried from segment to segment
+ * and from call to call (Eq. 4, "The Recurrent Formulation of Infini-Attention").
+ *
+ * Boundary.  The library sits after the Q/K/V projections (Eq. 5) and before the output
+ * projection W_O (Eq. 11): callers pass per-head Q, K, V and receive the per-head gated
+ * context A.
+ *
+ * Layout.  Q, K, V and out are dense [B, H, T, d] arrays (d fastest), T = tokens of the
+ * call, element type io_dtype.  Segments start at the first token of every call; a last
+ * segment shorter than N is processed with its own length.  M is [B, H, d_key, d_value]
+ * float32 row-major (M[i][j] binds key feature i to value feature j), z is [B, H, d_key]
+ * float32.
+ *
+ * Ownership.  The caller owns Q, K, V and out (device pointers).  The library owns M, z,
+ * the gate values and its workspace, all on the device of the create call.  out must not
+ * overlap any input.  A handle is not thread-safe.
+ *
+ * Execution.  Compute calls are enqueued on the HIP stream passed in (NULL = the null
+ * stream) and return without waiting for the device.  Consecutive calls on one handle
+ * must be ordered on one stream (or synchronised by the caller).
+ *
+ * Errors.  Every entry point returns INFINI_OK (0) or a negative status.  Argument
+ * errors are found before anything is enqueued and leave the state untouched.  HIP
+ * errors from launches are reported as INFINI_ERR_HIP.  Numerics are not checked: NaN
+ * in the inputs propagates as the equations dictate.
+ */
+#ifndef INFINI_ATTN_H
+#define INFINI_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define INFINI_OK 0
+#define INFINI_ERR_INVALID_ARG (-1)
+#define INFINI_ERR_UNSUPPORTED (-2)
+#define INFINI_ERR_HIP (-3)
+#define INFINI_ERR_OOM (-4)
+
+typedef struct infini_attn* infini_attn_t;
+
+/* Memory update rule: Eq. 8 (linear) or Eq. 9 (delta). */
+typedef enum { INFINI_UPDATE_LINEAR = 0, INFINI_UPDATE_DELTA = 1 } infini_update_t;
+
+/* Element type of Q, K, V and out.  bf16 runs the bf16 matrix-core path; f32 runs an
+ * all-float32 path meant for small shapes and checks. */
+typedef enum { INFINI_DTYPE_BF16 = 0, INFINI_DTYPE_F32 = 1 } infini_dtype_t;
+
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t heads;          /* H >= 1; each head has its own M, z and beta ("Multi-Head Infini-Attention") */
+  int32_t head_dim;       /* d = d_key = d_value; 64 or 128 */
+  int32_t segment_len;    /* N >= 1 (a multiple of 64 for the bf16 path) */
+  int32_t update;         /* infini_update_t */
+  int32_t io_dtype;       /* infini_dtype_t */
+  float eps;              /* >= 0; added to the retrieval denominator in Eq. 7 and Eq. 9.  With
+                             eps = 0 the first segment (zero memory) yields 0/0 = NaN. */
+  float softmax_scale;    /* > 0, or <= 0 for 1/sqrt(head_dim) */
+  int32_t max_window_segments; /* segments processed per internal window of forward_stream;
+                                  bounds the workspace; <= 0 picks a default */
+} infini_attn_config_t;
+
+/* Create a layer.  beta_host: H gate logits (host memory, copied; +-inf allowed).
+ * Allocates M = 0, z = 0 and the workspace on the current device.  hip_stream orders
+ * the zero fill.  *out receives the handle. */
+int infini_attn_create(const infini_attn_config_t* cfg, const float* beta_host,
+                       void* hip_stream, infini_attn_t* out);
+
+/* One segment (Eq. 4): 1 <= n_tokens <= N tokens of Q/K/V [B,H,n_tokens,d] -> out.
+ * Reads the state, writes out, advances the state by this segment. */
+int infini_attn_forward_segment(infini_attn_t h, const void* q, const void* k, const void* v,
+                                void* out, int32_t n_tokens, void* hip_stream);
+
+/* A stream of n_tokens >= 1 tokens, cut into ceil(n_tokens / N) segments processed in
+ * order (section "Training Infrastructure for Recurrent Attention", segment chunking).
+ * Same result as calling forward_segment once per segment. */
+int infini_attn_forward_stream(infini_attn_t h, const void* q, const void* k, const void* v,
+                               void* out, int64_t n_tokens, void* hip_stream);
+
+/* forward_stream that also writes the two gated terms for checks: a_mem (Eq. 7) and
+ * a_dot (Eq. 6), float32 [B,H,n_tokens,d] each; either may be NULL. */
+int infini_attn_forward_stream_ex(infini_attn_t h, const void* q, const void* k, const void* v,
+                                  void* out, float* a_mem, float* a_dot, int64_t n_tokens,
+                                  void* hip_stream);
+
+/* M = 0, z = 0 (stream-ordered). */
+int infini_attn_reset_state(infini_attn_t h, void* hip_stream);
+
+/* Copy the state out / in.  M: [B,H,d,d] float32, z: [B,H,d] float32, device or host
+ * pointers (hipMemcpyDefault).  get_state waits for the copy to finish. */
+int infini_attn_get_state(infini_attn_t h, float* M, float* z, void* hip_stream);
+int infini_attn_set_state(infini_attn_t h, const float* M, const float* z, void* hip_stream);
+
+/* Replace the H gate logits (host memory).  Waits for the device to be idle first. */
+int infini_attn_set_beta(infini_attn_t h, const float* beta_host);
+
+/* Device bytes the handle holds: state + gate values + workspace.  Constant for the
+ * handle's life, independent of how many tokens have been processed. */
+int64_t infini_attn_device_bytes(infini_attn_t h);
+
+/* Tokens per internal window of forward_stream (window segments * N). */
+int64_t infini_attn_window_tokens(infini_attn_t h);
+
+/* Waits for pending work on the handle's device, then frees everything.  NULL is a no-op. */
+int infini_attn_destroy(infini_attn_t h);
+
+/* Static text for a status code. */
+const char* infini_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFINI_ATTN_H */
