@@ -1,0 +1,209 @@
+"""Throughput of the Infini-attention layer forward on one MI355X.
+
+A step is one ``infini_attn_forward_stream`` over the whole 32768-token stream of the
+8-head, d=128, N=2048 workload (16 segments, linear update, bf16), preceded by a state
+reset, with Q/K/V already resident in HBM.  The JSON line reports whole-step tokens/s,
+the roofline of the dominant kernel (the fused local-attention + retrieval + gate kernel,
+timed with HIP events on its own stream inside the timed region), and the CPU oracle's
+throughput on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Infini-attention fwd tokens/sec per layer (H=8,d=128,N=2048) + % bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel_hash: str):
+    """HBM bytes per attention launch from the committed counter summary, if it was taken
+    from the kernel source that is built now; else None."""
+    path = os.path.join(ROOT, "profiles", "attention_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\): ([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (numpy float64, as written) on whole heads of the same stream until about
+    budget_s seconds of CPU work; reported as layer tokens/s (all heads)."""
+    import numpy as np
+    from compressive_memory_transformer_segment_amd import workloads as wl
+    from oracle import infini_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    beta = wl.beta_for(w)
+    done_heads, elapsed = 0, 0.0
+    for h in range(w.heads):
+        qkv = [np.empty((1, 1, w.n_tokens, w.head_dim), dtype=np.float32) for _ in range(3)]
+        for s in range(w.n_segments):
+            lo = s * w.segment_len
+            parts = wl.segment_inputs(w, 0, s, heads=[h])
+            for x, p in zip(qkv, parts):
+                x[0, 0, lo:lo + p.shape[1]] = p[0]
+        t0 = time.perf_counter()
+        orc.forward(*qkv, beta[h:h + 1], w.segment_len, w.update, eps=w.eps)
+        elapsed += time.perf_counter() - t0
+        done_heads += 1
+        if elapsed >= budget_s:
+            break
+    per_head_s = elapsed / done_heads
+    value = w.batch * w.n_tokens / (per_head_s * w.heads)
+    return {"value": value, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "sample": (f"oracle.forward over the full {w.n_tokens}-token stream of {done_heads} of "
+                       f"{w.heads} heads ({elapsed:.1f} s), scaled to all heads")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from compressive_memory_transformer_segment_amd import binding, profiling
+    from compressive_memory_transformer_segment_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload or wl.THROUGHPUT_WORKLOAD]
+    if w.io_dtype != "bf16":
+        raise SystemExit("bench.py times the bf16 path")
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    # inputs resident in HBM before the timed region
+    shape = (w.batch, w.heads, w.n_tokens, w.head_dim)
+    Q, K, V = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    for b in range(w.batch):
+        for s in range(w.n_segments):
+            lo = s * w.segment_len
+            for x, p in zip((Q, K, V), wl.segment_inputs(w, b, s)):
+                x[b, :, lo:lo + p.shape[1]] = torch.from_numpy(p).to(dev, torch.bfloat16)
+    out = torch.empty_like(Q)
+    layer = binding.InfiniAttention(w.batch, w.heads, w.head_dim, w.segment_len, update=w.update,
+                                    io_dtype="bf16", eps=w.eps, beta=wl.beta_for(w))
+    stream = torch.cuda.current_stream()
+
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        layer.reset_state(stream)
+        layer.forward_stream(Q, K, V, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup {args.warmup} done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    # timed region: K steps between two synchronisations
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # the same K steps with every kernel bracketed by HIP events on the launch stream
+    layer.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    torch.cuda.synchronize()
+
+    tokens = w.batch * w.n_tokens
+    value = tokens / (ms / 1e3)
+    flops_step = profiling.layer_flops(w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens, w.update)
+    attn_ms, attn_launches = prof["attention"]
+    attn_avg_s = attn_ms / attn_launches / 1e3
+    attn_flops = profiling.attention_kernel_flops(w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens)
+    attn_flops_launch = attn_flops * args.steps / attn_launches
+    achieved = attn_flops_launch / attn_avg_s / 1e12
+    traffic = traffic_from_profiles(profiling.kernel_source_hash())
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "segment_len": w.segment_len, "n_tokens": w.n_tokens, "update": w.update,
+                   "parallelism": "none"},
+        "pct_bf16_peak": 100.0 * flops_step / (ms / 1e3) / profiling.PEAK_BF16_FLOPS,
+        "roofline": {
+            "kernel": "k_attn_bf16 (local attention + retrieval + gate)",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": profiling.PEAK_BF16_FLOPS / 1e12,
+            "unit": "TFLOP/s",
+            "frac": achieved / (profiling.PEAK_BF16_FLOPS / 1e12),
+            "traffic": traffic,
+            "algorithmic_bytes": profiling.attention_kernel_bytes(
+                w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens),
+            "avg_launch_us": attn_avg_s * 1e6,
+        },
+        "kernels_avg_us": {k: (t / n * 1e3 if n else None) for k, (t, n) in prof.items()},
+        "wall_ms_per_step": wall_ms / args.steps,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    else:
+        rec["cpu_baseline"] = None
+    layer.close()
+    del np
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

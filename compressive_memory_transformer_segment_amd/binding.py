@@ -39,6 +39,13 @@ class Config(ctypes.Structure):
     ]
 
 
+KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention")
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("total_ms", ctypes.c_double * 4), ("launches", ctypes.c_int64 * 4)]
+
+
 class InfiniAttnError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn} failed: {text} ({status})")
@@ -80,6 +87,8 @@ def load() -> ctypes.CDLL:
         "infini_attn_window_tokens": (i64, [vp]),
         "infini_attn_destroy": (ctypes.c_int, [vp]),
         "infini_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "infini_attn_profile_enable": (ctypes.c_int, [vp, ctypes.c_int]),
+        "infini_attn_profile_read": (ctypes.c_int, [vp, ctypes.POINTER(Profile)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -220,3 +229,13 @@ class InfiniAttention:
 
     def window_tokens(self) -> int:
         return int(self._lib.infini_attn_window_tokens(self._h))
+
+    # ------------------------------------------------------------------ measurement
+    def profile_enable(self, enable: bool = True) -> None:
+        _check("infini_attn_profile_enable", self._lib.infini_attn_profile_enable(self._h, int(enable)))
+
+    def profile_read(self) -> dict:
+        """{kernel kind: (total milliseconds, launches)} since the last enable/read."""
+        p = Profile()
+        _check("infini_attn_profile_read", self._lib.infini_attn_profile_read(self._h, ctypes.byref(p)))
+        return {k: (p.total_ms[i], int(p.launches[i])) for i, k in enumerate(KERNEL_KINDS)}

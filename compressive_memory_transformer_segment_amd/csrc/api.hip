@@ -11,6 +11,8 @@
 #include <mutex>
 #include <new>
 #include <unordered_set>
+#include <utility>
+#include <vector>
 
 #include "../../include/infini_attn.h"
 #include "kernels.hpp"
@@ -31,6 +33,11 @@ struct infini_attn {
   void* ws_base;
   size_t ws_bytes;
   infini::Workspace ws;
+  // per-kernel event timing (measurement only)
+  bool profiling = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<std::pair<int, size_t>> ev_marks;   // (kernel kind, index of the start event)
 };
 
 namespace {
@@ -175,6 +182,27 @@ int check_io(const infini_attn* h, const void* q, const void* k, const void* v, 
   return INFINI_OK;
 }
 
+// Launch one kernel, bracketed by events when profiling is on.
+template <typename F>
+hipError_t timed(infini_attn* h, int kind, hipStream_t st, F&& launch) {
+  if (!h->profiling) return launch();
+  while (h->ev_pool.size() < h->ev_used + 2) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return err;
+    h->ev_pool.push_back(e);
+  }
+  const size_t i = h->ev_used;
+  hipError_t e = hipEventRecord(h->ev_pool[i], st);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(h->ev_pool[i + 1], st);
+  if (e == hipSuccess) {
+    h->ev_marks.emplace_back(kind, i);
+    h->ev_used += 2;
+  }
+  return e;
+}
+
 int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void* out, float* a_mem,
                float* a_dot, int64_t n_tokens, void* hip_stream) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
@@ -225,10 +253,10 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
     a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
     a.chk = (h->N + a.ch - 1) / a.ch;
     hipError_t e = hipSuccess;
-    if (h->delta) e = infini::launch_key_sums(a, st);
-    if (e == hipSuccess) e = infini::launch_state_pass(a, st);
-    if (e == hipSuccess) e = infini::launch_chain(a, st);
-    if (e == hipSuccess) e = infini::launch_attention(a, st);
+    if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
+    if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
+    if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+    if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(a, st); });
     if (e != hipSuccess) return INFINI_ERR_HIP;
   }
   return INFINI_OK;
@@ -335,6 +363,7 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   }
   DeviceGuard dg(h->device);
   const hipError_t e = hipDeviceSynchronize();
+  for (hipEvent_t ev : h->ev_pool) (void)hipEventDestroy(ev);
   (void)hipFree(h->M);
   (void)hipFree(h->z);
   (void)hipFree(h->gate);
@@ -418,4 +447,30 @@ INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
 INFINI_EXPORT int64_t infini_attn_window_tokens(infini_attn_t h) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   return int64_t(h->window) * h->N;
+}
+
+INFINI_EXPORT int infini_attn_profile_enable(infini_attn_t h, int enable) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  h->profiling = enable != 0;
+  h->ev_used = 0;
+  h->ev_marks.clear();
+  return INFINI_OK;
+}
+
+INFINI_EXPORT int infini_attn_profile_read(infini_attn_t h, infini_attn_profile_t* out) {
+  if (!live(h) || !out) return INFINI_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  DeviceGuard dg(h->device);
+  hipError_t e = hipSuccess;
+  if (h->ev_used > 0) e = hipEventSynchronize(h->ev_pool[h->ev_used - 1]);
+  for (const auto& m : h->ev_marks) {
+    if (e != hipSuccess) break;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, h->ev_pool[m.second], h->ev_pool[m.second + 1]);
+    out->total_ms[m.first] += ms;
+    out->launches[m.first] += 1;
+  }
+  h->ev_used = 0;
+  h->ev_marks.clear();
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }

@@ -67,7 +67,7 @@ typedef struct {
   int32_t batch;          /* B >= 1 */
   int32_t heads;          /* H >= 1; each head has its own M, z and beta ("Multi-Head Infini-Attention") */
   int32_t head_dim;       /* d = d_key = d_value; 64 or 128 */
-  int32_t segment_len;    /* N >= 1 (a multiple of 64 for the bf16 path) */
+  int32_t segment_len;    /* N >= 1 */
   int32_t update;         /* infini_update_t */
   int32_t io_dtype;       /* infini_dtype_t */
   float eps;              /* >= 0; added to the retrieval denominator in Eq. 7 and Eq. 9.  With
@@ -117,6 +117,20 @@ int64_t infini_attn_device_bytes(infini_attn_t h);
 
 /* Tokens per internal window of forward_stream (window segments * N). */
 int64_t infini_attn_window_tokens(infini_attn_t h);
+
+/* Per-kernel timing with HIP events, for measurement.  While enabled, every kernel the
+ * handle launches is bracketed by two events on the call's stream.  profile_read waits
+ * for the recorded events, reports the summed durations per kernel kind, and clears the
+ * record.  Kernel kinds: 0 = key sums (delta rule only), 1 = state pass (per-segment
+ * sigma(K)^T V, key sums, delta Gram term, V transpose), 2 = memory chain (Eq. 8/9
+ * recurrence), 3 = fused local attention + retrieval + gate (Eq. 6, 7, 10). */
+#define INFINI_KERNEL_KINDS 4
+typedef struct {
+  double total_ms[INFINI_KERNEL_KINDS];
+  int64_t launches[INFINI_KERNEL_KINDS];
+} infini_attn_profile_t;
+int infini_attn_profile_enable(infini_attn_t h, int enable);
+int infini_attn_profile_read(infini_attn_t h, infini_attn_profile_t* out);
 
 /* Waits for pending work on the handle's device, then frees everything.  NULL is a no-op. */
 int infini_attn_destroy(infini_attn_t h);

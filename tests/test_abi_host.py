@@ -14,6 +14,7 @@ EXPECTED = {
     "infini_attn_forward_stream_ex", "infini_attn_reset_state", "infini_attn_get_state",
     "infini_attn_set_state", "infini_attn_set_beta", "infini_attn_device_bytes",
     "infini_attn_window_tokens", "infini_attn_destroy", "infini_attn_status_string",
+    "infini_attn_profile_enable", "infini_attn_profile_read",
 }
 
 
@@ -84,3 +85,5 @@ def test_calls_on_a_missing_handle_fail_cleanly(lib):
         assert lib.infini_attn_set_beta(h, (ctypes.c_float * 1)(0.0)) == -1
         assert lib.infini_attn_device_bytes(h) == -1
         assert lib.infini_attn_window_tokens(h) == -1
+        assert lib.infini_attn_profile_enable(h, 1) == -1
+        assert lib.infini_attn_profile_read(h, ctypes.byref(binding.Profile())) == -1
