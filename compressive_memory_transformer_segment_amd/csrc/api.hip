@@ -69,24 +69,20 @@ struct DeviceGuard {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Bytes of workspace one window needs, per (b,h) pair, excluding the chunk partials.
-size_t unit_bytes(const infini_attn& h) {
-  const size_t D = h.D, DD = D * D;
-  size_t b = 0;
-  b += D * 4;                        // dz
-  b += DD * 4;                       // u_red
-  if (h.delta) b += DD * 4;          // g_red
-  b += 2 * 4;                        // counters
-  if (h.bf16) b += D * h.NP * 2;     // vt
-  b += DD * (h.bf16 ? 2 : 4);        // mt
-  b += D * 4;                        // zb
-  return b;
-}
-size_t part_bytes(const infini_attn& h) {   // one chunk-partial slot
+// One chunk-partial slot: key sums, (sigma(K)^T V)^T and, for the delta rule, the Gram term.
+size_t part_bytes(const infini_attn& h) {
   const size_t D = h.D, DD = D * D;
   return D * 4 + DD * 4 + (h.delta ? DD * 4 : 0);
 }
 
+// Bytes of workspace one window needs, per (b,h) pair, excluding the chunk partials.
+size_t unit_bytes(const infini_attn& h) {
+  const size_t D = h.D, DD = D * D;
+  size_t b = 0;
+  b += DD * (h.bf16 ? 2 : 4);        // mt
+  b += D * 4;                        // zb
+  return b + part_bytes(h);          // at least one chunk slot per unit
+}
 int chunks_for(const infini_attn& h, int w_call) {
   if (!h.bf16) return 1;
   const int units = w_call * h.BH;
@@ -97,48 +93,38 @@ int chunks_for(const infini_attn& h, int w_call) {
   return std::max(chk, 1);
 }
 
-void carve(infini_attn& h) {
+// Workspace layout: one window of units plus the chunk-partial slots.
+template <typename F>
+void layout(const infini_attn& h, F&& take) {
   const size_t U = size_t(h.window) * h.BH;
   const size_t P = size_t(h.part_cap) * h.BH;
   const size_t D = h.D, DD = D * D;
-  char* p = static_cast<char*>(h.ws_base);
-  auto take = [&](size_t bytes) { char* r = p; p += align_up(bytes, 256); return r; };
-  h.ws.dz = reinterpret_cast<float*>(take(U * D * 4));
-  h.ws.u_red = reinterpret_cast<float*>(take(U * DD * 4));
-  h.ws.g_red = h.delta ? reinterpret_cast<float*>(take(U * DD * 4)) : nullptr;
-  h.ws.cnt = reinterpret_cast<uint32_t*>(take(2 * U * 4));
-  h.ws.vt = h.bf16 ? reinterpret_cast<uint16_t*>(take(U * D * h.NP * 2)) : nullptr;
-  h.ws.mt = take(U * DD * (h.bf16 ? 2 : 4));
-  h.ws.zb = reinterpret_cast<float*>(take(U * D * 4));
-  if (h.part_cap > 0) {
-    h.ws.dz_part = reinterpret_cast<float*>(take(P * D * 4));
-    h.ws.u_part = reinterpret_cast<float*>(take(P * DD * 4));
-    h.ws.g_part = h.delta ? reinterpret_cast<float*>(take(P * DD * 4)) : nullptr;
-  } else {
-    h.ws.dz_part = h.ws.u_part = h.ws.g_part = nullptr;
-  }
-  h.ws_bytes = static_cast<size_t>(p - static_cast<char*>(h.ws_base));
+  take(0, P * D * 4);                                // dz
+  take(1, P * DD * 4);                               // u
+  take(2, h.delta ? P * DD * 4 : 0);                 // g
+  take(4, U * DD * (h.bf16 ? 2 : 4));                // mt
+  take(5, U * D * 4);                                // zb
 }
 
 size_t layout_bytes(const infini_attn& h) {
-  const size_t U = size_t(h.window) * h.BH;
-  const size_t P = size_t(h.part_cap) * h.BH;
-  const size_t D = h.D, DD = D * D;
   size_t b = 0;
-  auto add = [&](size_t x) { b += align_up(x, 256); };
-  add(U * D * 4);
-  add(U * DD * 4);
-  if (h.delta) add(U * DD * 4);
-  add(2 * U * 4);
-  if (h.bf16) add(U * D * h.NP * 2);
-  add(U * DD * (h.bf16 ? 2 : 4));
-  add(U * D * 4);
-  if (h.part_cap > 0) {
-    add(P * D * 4);
-    add(P * DD * 4);
-    if (h.delta) add(P * DD * 4);
-  }
+  layout(h, [&](int, size_t bytes) { b += align_up(bytes, 256); });
   return b;
+}
+
+void carve(infini_attn& h) {
+  char* p = static_cast<char*>(h.ws_base);
+  void* ptrs[6] = {};
+  layout(h, [&](int i, size_t bytes) {
+    ptrs[i] = bytes ? p : nullptr;
+    p += align_up(bytes, 256);
+  });
+  h.ws.dz = static_cast<float*>(ptrs[0]);
+  h.ws.u = static_cast<float*>(ptrs[1]);
+  h.ws.g = static_cast<float*>(ptrs[2]);
+  h.ws.mt = ptrs[4];
+  h.ws.zb = static_cast<float*>(ptrs[5]);
+  h.ws_bytes = static_cast<size_t>(p - static_cast<char*>(h.ws_base));
 }
 
 void gate_values(const float* beta, int H, float* out) {
@@ -233,7 +219,6 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   a.D = h->D;
   a.T = n_tokens;
   a.N = h->N;
-  a.NP = h->NP;
   a.S = static_cast<int>(S64);
   a.n_last = static_cast<int>(n_tokens - (S64 - 1) * h->N);
   a.delta = h->delta;
@@ -312,13 +297,10 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   if (c.max_window_segments > 0) w = std::min(w, c.max_window_segments);
   h->window = w;
   // chunk partials: enough slots for the chunking chosen at any window size
-  int cap = 0;
+  int cap = w;
   if (h->bf16) {
     h->part_cap = 1 << 30;
-    for (int wc = 1; wc <= w; ++wc) {
-      const int chk = chunks_for(*h, wc);
-      if (chk > 1) cap = std::max(cap, wc * chk);
-    }
+    for (int wc = 1; wc <= w; ++wc) cap = std::max(cap, wc * chunks_for(*h, wc));
   }
   h->part_cap = cap;
 
@@ -348,7 +330,6 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   delete[] gv;
   if (e == hipSuccess) e = hipMemsetAsync(h->M, 0, m_bytes, st);
   if (e == hipSuccess) e = hipMemsetAsync(h->z, 0, z_bytes, st);
-  if (e == hipSuccess) e = hipMemsetAsync(h->ws.cnt, 0, size_t(2) * h->window * h->BH * 4, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) { infini_attn_destroy(h); return INFINI_ERR_HIP; }
   *out = h;

@@ -12,8 +12,9 @@
 // directly the B operand of O^T += V^T P^T, and the retrieval sigma(Q) reuses the Q
 // registers (Q is the B operand of S^T) as the B operand of A_mem^T = M^T sigma(Q)^T.
 //
-// K tiles (64 keys x d) and V^T tiles (d x 64 keys, from the state pass) are staged in
-// LDS, double buffered, prefetched into registers one tile ahead.  The online softmax is
+// K and V tiles (64 keys x d, row-major as in memory) are staged in LDS, double buffered,
+// prefetched into registers one tile ahead.  The V^T operand of O^T += V^T P^T is read
+// with LDS transpose reads, in the key order the S^T result registers hold.  The online softmax is
 // in the exp2 domain with the scale folded in, and rescales the accumulator lazily: only
 // when a row maximum grows by more than 2^8 (exact: the final division uses the same
 // stale maximum).  The gated result is staged through LDS and written once with
@@ -33,15 +34,14 @@ constexpr float kTau = 8.f;
 template <int D, bool PARTS>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
   constexpr int KP = D + 8;          // K tile row pitch (bf16 elements)
-  constexpr int VP = kBN + 8;        // V^T tile row pitch
+  constexpr int VP = D + 32;         // V tile row pitch: conflict-free transpose reads
   constexpr int KS = D / 16;         // k-steps over the head dimension
   constexpr int DB = D / 32;         // 32-row blocks of the head dimension
-  constexpr int KCH = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread per tile
-  constexpr int VCH = D * kBN / 8 / kThreads;  // 16-byte V^T chunks per thread per tile
+  constexpr int KCH = kBN * D / 8 / kThreads;  // 16-byte K (and V) chunks per thread per tile
   constexpr int OP = D + 8;          // output staging row pitch
 
   __shared__ __align__(16) uint16_t k_lds[2][kBN][KP];
-  __shared__ __align__(16) uint16_t v_lds[2][D][VP];
+  __shared__ __align__(16) uint16_t v_lds[2][kBN][VP];
   static_assert(sizeof(uint16_t) * 4 * 32 * OP <= sizeof(uint16_t) * 2 * kBN * KP, "staging fits");
 
   const int units = a.units();
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
 
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
   const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vt = a.ws.vt + static_cast<int64_t>(u) * D * a.NP;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
 
   // Q as the B operand of S^T: lane holds Q[q][16 ks + 8 hl .. +7]
   u32x4 qreg[KS];
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
   }
 
   const int nkv = (min(q0 + kBM, n) + kBN - 1) / kBN;
-  u32x4 kpre[KCH], vpre[VCH];
+  u32x4 kpre[KCH], vpre[KCH];
   auto prefetch = [&](int j) {
     const int kv0 = j * kBN;
 #pragma unroll
@@ -82,13 +82,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
       const int id = tid + kThreads * i;
       const int row = id / (D / 8), c = id % (D / 8);
       kpre[i] = u32x4{0u, 0u, 0u, 0u};
-      if (kv0 + row < n) kpre[i] = ld16(kg + (row0 + kv0 + row) * D + 8 * c);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id / (kBN / 8), c = id % (kBN / 8);
-      vpre[i] = ld16(vt + static_cast<int64_t>(row) * a.NP + kv0 + 8 * c);
+      vpre[i] = u32x4{0u, 0u, 0u, 0u};
+      if (kv0 + row < n) {
+        kpre[i] = ld16(kg + (row0 + kv0 + row) * D + 8 * c);
+        vpre[i] = ld16(vg + (row0 + kv0 + row) * D + 8 * c);
+      }
     }
   };
   auto commit = [&](int buf) {
@@ -96,13 +94,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
     for (int i = 0; i < KCH; ++i) {
       const int id = tid + kThreads * i;
       st16(&k_lds[buf][id / (D / 8)][8 * (id % (D / 8))], kpre[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int id = tid + kThreads * i;
-      st16(&v_lds[buf][id / (kBN / 8)][8 * (id % (kBN / 8))], vpre[i]);
+      st16(&v_lds[buf][id / (D / 8)][8 * (id % (D / 8))], vpre[i]);
     }
   };
+  // transpose-read addressing of the V^T operand: k-slot (hl, i) of k-step j4 is key
+  // 16 j4 + 8 (i / 4) + 4 hl + i % 4, the key the S^T register feeding that slot holds
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int tr_row = 4 * hl + (tr_j >> 2);
+  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_j & 3);
 
   prefetch(0);
   commit(0);
@@ -122,16 +121,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
     const int kv0 = j * kBN;
     if (kv0 <= qw0 + 31) {
       // ---- S^T = K Q^T for 64 keys x 32 queries
-      f32x16 acc_s[2];
+      f32x16 acc_s[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc_s[kb] = zero16();
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int kb = 0; kb < 2; ++kb) {   // two independent accumulation chains
           const bf16x8 ak = as_bf16x8(ld16(&k_lds[buf][32 * kb + l32][16 * ks + 8 * hl]));
           acc_s[kb] = mfma32x32x16(ak, as_bf16x8(qreg[ks]), acc_s[kb]);
         }
-      }
       // ---- causal mask on tiles that reach past this wave's first query
       if (kv0 + kBN - 1 > qw0) {
 #pragma unroll
@@ -184,7 +181,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
-          const bf16x8 av = as_bf16x8(ld16(&v_lds[buf][32 * db + l32][16 * j4 + 8 * hl]));
+          const uint16_t* vp = &v_lds[buf][16 * j4 + tr_row][32 * db + tr_col];
+          const u32x2 v0 = lds_read_tr16(vp);
+          const u32x2 v1 = lds_read_tr16(vp + 8 * VP);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
           acc_o[db] = mfma32x32x16(av, pb[j4], acc_o[db]);
         }
     }

@@ -5,7 +5,8 @@
 //   linear (Eq. 8):  M^T_s = M^T_{s-1} + U^T_s
 //   delta  (Eq. 9):  M^T_s = M^T_{s-1} - M^T_{s-1} G_s^T + U^T_s   (from M_s = M - G M + U)
 //   z_s = z_{s-1} + dz_s
-// with U_s, G_s, dz_s from the state pass.  Rows of M^T (value features) evolve
+// with U_s, G_s, dz_s from the state pass, which leaves them as per-chunk partials; the
+// chain adds the chunks in chunk order.  Rows of M^T (value features) evolve
 // independently under both rules, so each workgroup owns a block of rows and never
 // waits on another.  For every segment of the window the chain first records the state
 // the segment reads (M^T_{s-1} in the attention kernel's operand type, and z_{s-1}), then
@@ -18,9 +19,6 @@ namespace infini {
 namespace {
 
 constexpr int kThreads = 256;
-
-template <bool BF16>
-__device__ __forceinline__ void store_state_row(void* mt, int64_t off, const float* m, int ept);
 
 template <int D, int EPT, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
@@ -50,8 +48,16 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
       const int s = s0 + sb;
       const int64_t u = static_cast<int64_t>(s) * BH + bh;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) ut[sb][e] = (s < a.W) ? a.ws.u_red[u * DD + static_cast<int64_t>(dv) * D + i0 + e] : 0.f;
-      dzv[sb] = (s < a.W && zown) ? a.ws.dz[u * D + tid] : 0.f;
+      for (int e = 0; e < EPT; ++e) ut[sb][e] = 0.f;
+      dzv[sb] = 0.f;
+      if (s < a.W) {
+        for (int c = 0; c < a.chk; ++c) {
+          const int64_t slot = u * a.chk + c;
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) ut[sb][e] += a.ws.u[slot * DD + static_cast<int64_t>(dv) * D + i0 + e];
+          if (zown) dzv[sb] += a.ws.dz[slot * D + tid];
+        }
+      }
     }
 #pragma unroll
     for (int sb = 0; sb < kBatch; ++sb) {
@@ -126,13 +132,17 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
     }
     if (zown) {
       a.ws.zb[u * D + tid] = z;
-      z += a.ws.dz[u * D + tid];
+      float dz = 0.f;
+      for (int c = 0; c < a.chk; ++c) dz += a.ws.dz[(u * a.chk + c) * D + tid];
+      z += dz;
     }
-    // stage G_s and the rows of M^T
-    const float* g = a.ws.g_red + u * DD;
+    // stage G_s (sum of the chunk partials) and the rows of M^T
     for (int e4 = tid; e4 < D * D / 4; e4 += kThreads) {
       const int row = (e4 * 4) / D, col = (e4 * 4) % D;
-      *reinterpret_cast<f32x4*>(&g_lds[row][col]) = *reinterpret_cast<const f32x4*>(g + row * D + col);
+      f32x4 gs = *reinterpret_cast<const f32x4*>(a.ws.g + u * a.chk * DD + row * D + col);
+      for (int c = 1; c < a.chk; ++c)
+        gs += *reinterpret_cast<const f32x4*>(a.ws.g + (u * a.chk + c) * DD + row * D + col);
+      *reinterpret_cast<f32x4*>(&g_lds[row][col]) = gs;
     }
 #pragma unroll
     for (int e = 0; e < EPT; ++e) m_lds[r][cg + CG * e] = m[e];
@@ -149,9 +159,12 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
         acc[e] += mk[0] * gk[0] + mk[1] * gk[1] + mk[2] * gk[2] + mk[3] * gk[3];
       }
     }
-    const float* ut = a.ws.u_red + off;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) m[e] = (m[e] - acc[e]) + ut[cg + CG * e];
+    for (int e = 0; e < EPT; ++e) {
+      float ut = 0.f;
+      for (int c = 0; c < a.chk; ++c) ut += a.ws.u[(u * a.chk + c) * DD + static_cast<int64_t>(dv) * D + cg + CG * e];
+      m[e] = (m[e] - acc[e]) + ut;
+    }
     __syncthreads();
   }
 #pragma unroll

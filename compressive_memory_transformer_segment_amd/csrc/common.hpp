@@ -38,9 +38,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 b = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, b);
 }
-// Two floats -> one dword holding bf16(a) in the low half and bf16(b) in the high half.
+// Two floats -> one dword holding bf16(a) in the low half and bf16(b) in the high half
+// (one v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // sigma(x) = ELU(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise.
@@ -65,6 +69,29 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16(x);
   lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// supplies the address of 4 consecutive 16-bit elements; lane i of the group receives
+// element i % 4 of the loads of lanes 4r + i / 4, r = 0..3.  With a row-major [k][n] tile
+// and lane j addressing &X[k0 + j/4][n0 + 4*(j%4)], lane i receives X[k0 + r][n0 + i] for
+// r = 0..3: four consecutive k of column n0 + i, i.e. half of an MFMA operand slice.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// The 8 consecutive-k values of a 32x32x16 MFMA operand (A or B) for this lane, from a
+// row-major [k][n] bf16 tile in LDS with row pitch `pitch` elements: lane l gets
+// X[k0 + 8*(l/32) + 0..7][n0 + l%32].  Two transpose reads.
+__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* tile, int pitch, int k0, int n0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = tile + (k0 + 8 * (g >> 1) + (j >> 2)) * pitch + n0 + 16 * (g & 1) + 4 * (j & 3);
+  const u32x2 lo = lds_read_tr16(p);
+  const u32x2 hi = lds_read_tr16(p + 4 * pitch);
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -9,16 +9,11 @@ namespace infini {
 // Device workspace for one window of W segments.  A "unit" is one (batch, head) pair on
 // one segment: u = s_local * (B*H) + b*H + h.
 struct Workspace {
-  float* dz;        // [U][D]        sum_t sigma(k_t) of the unit's segment
-  float* dz_part;   // [U][CHK][D]   per-chunk partial sums (CHK > 1)
-  float* u_part;    // [U][CHK][D][D] per-chunk (sigma(K)^T V)^T (CHK > 1)
-  float* u_red;     // [U][D][D]     (sigma(K)^T V)^T of the segment: [d_value][d_key]
-  float* g_part;    // [U][CHK][D][D] per-chunk sigma(K)^T diag(1/den) sigma(K) (delta, CHK > 1)
-  float* g_red;     // [U][D][D]     the same for the segment (delta): [d_key][d_key]
-  uint32_t* cnt;    // [2][U]        arrival counters of the chunked reductions (kept at 0)
-  uint16_t* vt;     // [U][D][NP]    V of the segment, transposed, bf16 (bf16 path)
-  void* mt;         // [U][D][D]     M_{s-1} transposed ([d_value][d_key]); bf16 or f32
-  float* zb;        // [U][D]        z_{s-1}
+  float* dz;        // [U][CHK][D]    per-chunk key sums  sum_t sigma(k_t)
+  float* u;         // [U][CHK][D][D] per-chunk (sigma(K)^T V)^T: [d_value][d_key]
+  float* g;         // [U][CHK][D][D] per-chunk sigma(K)^T diag(1/den) sigma(K) (delta): [d_key][d_key]
+  void* mt;         // [U][D][D]      M_{s-1} transposed ([d_value][d_key]); bf16 or f32
+  float* zb;        // [U][D]         z_{s-1}
 };
 
 struct WindowArgs {
@@ -31,12 +26,11 @@ struct WindowArgs {
   int B, H, D;
   int64_t T;         // tokens in the call
   int N;             // segment length
-  int NP;            // N rounded up to 64 (row stride of the transposed V)
   int S;             // segments in the call
   int n_last;        // tokens of the call's last segment
   int s0;            // first segment of this window (call-relative)
   int W;             // segments in this window
-  int chk;           // chunks per segment in the state pass
+  int chk;           // chunks per segment in the state pass (partials summed by the chain)
   int ch;            // tokens per chunk (multiple of 64)
   bool delta;
   bool bf16;

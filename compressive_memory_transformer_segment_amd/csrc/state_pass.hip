@@ -14,9 +14,10 @@
 //
 // bf16 path: sigma(K) is formed in fp32 and split into bf16 hi + lo, so the bf16 matrix
 // cores give fp32-accurate sums (V is exact in bf16); G uses hi*hi + hi*lo + lo*hi.
-// The pass also writes V transposed ([d][t], bf16) for the attention kernel's P V product.
-// A segment is cut into `chk` chunks, one workgroup each; the last workgroup to finish a
-// unit adds the chunk partials in chunk order (deterministic) and writes the unit's sums.
+// A segment is cut into `chk` chunks, one workgroup each, and every chunk writes its own
+// partial sums with plain stores; the chain kernel (the next launch on the stream, so the
+// partials are visible to it) adds them in chunk order, which keeps results deterministic
+// without any cross-workgroup synchronisation here.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,7 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSub = 64;                  // tokens per sub-tile
-constexpr int kRowPad = kSub + 8;         // LDS row stride in bf16 elements (144 bytes)
 
 enum Mode { MODE_KEYSUM = 0, MODE_LINEAR = 1, MODE_DELTA = 2 };
 
@@ -48,31 +48,20 @@ __device__ __forceinline__ UnitPos unit_pos(const WindowArgs& a, int u) {
 }
 
 // z_{s-1} for unit (s_local, bh): the state's z plus the key sums of the window's earlier
-// segments, added in segment order (the chain adds them in the same order).
+// segments, added segment by segment and chunk by chunk (the chain adds them in the same
+// order, so both see the same z).
 template <int D>
 __device__ void z_before(const WindowArgs& a, const UnitPos& p, float* zs) {
+  const int BH = a.B * a.H;
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float z = a.z[static_cast<int64_t>(p.bh) * D + d];
-    for (int s = 0; s < p.s_local; ++s) z += a.ws.dz[(static_cast<int64_t>(s) * a.B * a.H + p.bh) * D + d];
+    for (int s = 0; s < p.s_local; ++s) {
+      float dz = 0.f;
+      for (int c = 0; c < a.chk; ++c) dz += a.ws.dz[((static_cast<int64_t>(s) * BH + p.bh) * a.chk + c) * D + d];
+      z += dz;
+    }
     zs[d] = z;
   }
-}
-
-// Last-arriver bookkeeping.  Every thread's partial stores are made visible device-wide
-// before thread 0 counts the chunk in; the workgroup that brings the count to chk resets
-// the counter and returns true.
-__device__ bool arrive_last(uint32_t* cnt, int chk) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(cnt, 1u);
-    s_last = (prev == static_cast<uint32_t>(chk - 1));
-    if (s_last) atomicExch(cnt, 0u);
-  }
-  __syncthreads();
-  if (s_last) __threadfence();
-  return s_last != 0;
 }
 
 template <int D, int MODE>
@@ -82,14 +71,16 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
   constexpr int RPT = kSub / TQ;         // rows per thread per sub-tile (D/32)
   constexpr int NBLK = (D / 32) * (D / 32);
   constexpr int NB = NBLK / 4;           // 32x32 output blocks per wave
+  constexpr int P = D + 32;              // LDS row pitch (elements): conflict-free transpose reads
   constexpr bool kMat = MODE != MODE_KEYSUM;
   constexpr bool kDelta = MODE == MODE_DELTA;
 
-  __shared__ __align__(16) uint16_t sk_hi[kMat ? D : 1][kRowPad];
-  __shared__ __align__(16) uint16_t sk_lo[kMat ? D : 1][kRowPad];
-  __shared__ __align__(16) uint16_t vts[kMat ? D : 1][kRowPad];
-  __shared__ __align__(16) uint16_t dk_hi[kDelta ? D : 1][kRowPad];
-  __shared__ __align__(16) uint16_t dk_lo[kDelta ? D : 1][kRowPad];
+  // Row-major [token][feature] tiles; MFMA operands are read with LDS transpose reads.
+  __shared__ __align__(16) uint16_t sk_hi[kMat ? kSub : 1][P];
+  __shared__ __align__(16) uint16_t sk_lo[kMat ? kSub : 1][P];
+  __shared__ __align__(16) uint16_t v_s[kMat ? kSub : 1][P];
+  __shared__ __align__(16) uint16_t dk_hi[kDelta ? kSub : 1][P];
+  __shared__ __align__(16) uint16_t dk_lo[kDelta ? kSub : 1][P];
   __shared__ float zprev[kDelta ? D : 1];
   __shared__ float red[TQ][D];
 
@@ -99,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
   const int tid = threadIdx.x;
   const int dq = tid % DQ, tq = tid / DQ;
   const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hl = lane >> 5;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
 
   if constexpr (kDelta) {
     z_before<D>(a, p, zprev);
@@ -125,16 +117,16 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
   for (int ts = t_begin; ts < t_end; ts += kSub) {
     // ---- load RPT rows x 8 features of K (and V), form sigma(K) in fp32
     float sk[RPT][8];
-    u32x4 vraw[kMat ? RPT : 1];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const int t = ts + tq * RPT + r;
+      const int tl = tq * RPT + r;
+      const int t = ts + tl;
       u32x4 kr = {0u, 0u, 0u, 0u};
       if (t < p.n) kr = ld16(kg + row_base + static_cast<int64_t>(t) * D);
       if constexpr (kMat) {
         u32x4 vr = {0u, 0u, 0u, 0u};
         if (t < p.n) vr = ld16(vg + row_base + static_cast<int64_t>(t) * D);
-        vraw[r] = vr;
+        st16(&v_s[tl][dq * 8], vr);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -146,87 +138,61 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
       for (int i = 0; i < 8; ++i) zacc[i] += sk[r][i];
     }
     if constexpr (kMat) {
-      float dsc[RPT];
-      if constexpr (kDelta) {
-        // den_t = sigma(k_t) . z_{s-1} + eps; the row is spread over DQ consecutive lanes
+      // ---- hi/lo bf16 split of sigma(K) (and of diag(1/den) sigma(K) for the delta rule)
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) {
+      for (int r = 0; r < RPT; ++r) {
+        const int tl = tq * RPT + r;
+        float dsc = 0.f;
+        if constexpr (kDelta) {
+          // den_t = sigma(k_t) . z_{s-1} + eps; the row is spread over DQ consecutive lanes
           float part = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) part += sk[r][i] * zprev[dq * 8 + i];
 #pragma unroll
           for (int off = DQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-          const int t = ts + tq * RPT + r;
-          dsc[r] = (t < p.n) ? 1.f / (part + a.eps) : 0.f;
+          dsc = (ts + tl < p.n) ? 1.f / (part + a.eps) : 0.f;
         }
-      }
-      // ---- write the transposed hi/lo operands into LDS: row = feature, column = token
-      const int col = tq * RPT;
+        u32x4 hi, lo, dh, dl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = dq * 8 + i;
-        uint16_t hi[RPT], lo[RPT], vv[RPT], dh[RPT], dl[RPT];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-          split_bf16(sk[r][i], hi[r], lo[r]);
-          const uint32_t w = vraw[r][i >> 1];
-          vv[r] = static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xffffu));
-          if constexpr (kDelta) split_bf16(sk[r][i] * dsc[r], dh[r], dl[r]);
+        for (int i = 0; i < 4; ++i) {
+          const float s0 = sk[r][2 * i], s1 = sk[r][2 * i + 1];
+          hi[i] = pack_bf16x2(s0, s1);
+          lo[i] = pack_bf16x2(s0 - bf16lo_to_f32(hi[i]), s1 - bf16hi_to_f32(hi[i]));
+          if constexpr (kDelta) {
+            const float d0 = s0 * dsc, d1 = s1 * dsc;
+            dh[i] = pack_bf16x2(d0, d1);
+            dl[i] = pack_bf16x2(d0 - bf16lo_to_f32(dh[i]), d1 - bf16hi_to_f32(dh[i]));
+          }
         }
-        if constexpr (RPT == 4) {
-          st8(&sk_hi[row][col], u32x2{hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16)});
-          st8(&sk_lo[row][col], u32x2{lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16)});
-          st8(&vts[row][col], u32x2{vv[0] | (uint32_t(vv[1]) << 16), vv[2] | (uint32_t(vv[3]) << 16)});
-          if constexpr (kDelta) {
-            st8(&dk_hi[row][col], u32x2{dh[0] | (uint32_t(dh[1]) << 16), dh[2] | (uint32_t(dh[3]) << 16)});
-            st8(&dk_lo[row][col], u32x2{dl[0] | (uint32_t(dl[1]) << 16), dl[2] | (uint32_t(dl[3]) << 16)});
-          }
-        } else {
-          static_assert(RPT == 2, "D must be 64 or 128");
-          *reinterpret_cast<uint32_t*>(&sk_hi[row][col]) = hi[0] | (uint32_t(hi[1]) << 16);
-          *reinterpret_cast<uint32_t*>(&sk_lo[row][col]) = lo[0] | (uint32_t(lo[1]) << 16);
-          *reinterpret_cast<uint32_t*>(&vts[row][col]) = vv[0] | (uint32_t(vv[1]) << 16);
-          if constexpr (kDelta) {
-            *reinterpret_cast<uint32_t*>(&dk_hi[row][col]) = dh[0] | (uint32_t(dh[1]) << 16);
-            *reinterpret_cast<uint32_t*>(&dk_lo[row][col]) = dl[0] | (uint32_t(dl[1]) << 16);
-          }
+        st16(&sk_hi[tl][dq * 8], hi);
+        st16(&sk_lo[tl][dq * 8], lo);
+        if constexpr (kDelta) {
+          st16(&dk_hi[tl][dq * 8], dh);
+          st16(&dk_lo[tl][dq * 8], dl);
         }
       }
       __syncthreads();
 
-      // ---- V^T to the workspace, positions permuted inside each 16-token group so that
-      // the attention kernel's A operand of P V is one 16-byte read (see attention.hip).
-      {
-        uint16_t* vt = a.ws.vt + static_cast<int64_t>(u) * D * a.NP + ts;
-        for (int id = tid; id < D * 8; id += kThreads) {
-          const int row = id >> 3, cc = id & 7;  // destination chunk cc: 8 positions
-          const int g = cc >> 1, hh = cc & 1;
-          const u32x2 lo8 = ld8(&vts[row][16 * g + 4 * hh]);
-          const u32x2 hi8 = ld8(&vts[row][16 * g + 8 + 4 * hh]);
-          st16(vt + static_cast<int64_t>(row) * a.NP + 8 * cc, u32x4{lo8[0], lo8[1], hi8[0], hi8[1]});
-        }
-      }
-
-      // ---- MFMA: each wave owns NB 32x32 blocks of the d x d outputs
+      // ---- MFMA: each wave owns NB 32x32 blocks of the d x d outputs; operands come
+      // from the row-major tiles through transpose reads (k = token).
 #pragma unroll
       for (int ks = 0; ks < kSub / 16; ++ks) {
-        const int kc = 16 * ks + 8 * hl;
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
           const int blk = wave * NB + kb;
           const int ib = blk / (D / 32), jb = blk % (D / 32);
           // U^T block (rows = value features ib, columns = key features jb)
-          const bf16x8 av = as_bf16x8(ld16(&vts[32 * ib + l32][kc]));
-          const bf16x8 bkh = as_bf16x8(ld16(&sk_hi[32 * jb + l32][kc]));
-          const bf16x8 bkl = as_bf16x8(ld16(&sk_lo[32 * jb + l32][kc]));
+          const bf16x8 av = lds_operand_tr(&v_s[0][0], P, 16 * ks, 32 * ib, lane);
+          const bf16x8 bkh = lds_operand_tr(&sk_hi[0][0], P, 16 * ks, 32 * jb, lane);
+          const bf16x8 bkl = lds_operand_tr(&sk_lo[0][0], P, 16 * ks, 32 * jb, lane);
           acc_u[kb] = mfma32x32x16(av, bkh, acc_u[kb]);
           acc_u[kb] = mfma32x32x16(av, bkl, acc_u[kb]);
           if constexpr (kDelta) {
             // G block (rows = key features ib, columns = key features jb)
-            const bf16x8 ah = as_bf16x8(ld16(&sk_hi[32 * ib + l32][kc]));
-            const bf16x8 al = as_bf16x8(ld16(&sk_lo[32 * ib + l32][kc]));
-            const bf16x8 bh = as_bf16x8(ld16(&dk_hi[32 * jb + l32][kc]));
-            const bf16x8 bl = as_bf16x8(ld16(&dk_lo[32 * jb + l32][kc]));
+            const bf16x8 ah = lds_operand_tr(&sk_hi[0][0], P, 16 * ks, 32 * ib, lane);
+            const bf16x8 al = lds_operand_tr(&sk_lo[0][0], P, 16 * ks, 32 * ib, lane);
+            const bf16x8 bh = lds_operand_tr(&dk_hi[0][0], P, 16 * ks, 32 * jb, lane);
+            const bf16x8 bl = lds_operand_tr(&dk_lo[0][0], P, 16 * ks, 32 * jb, lane);
             acc_g[kb] = mfma32x32x16(ah, bh, acc_g[kb]);
             acc_g[kb] = mfma32x32x16(ah, bl, acc_g[kb]);
             acc_g[kb] = mfma32x32x16(al, bh, acc_g[kb]);
@@ -238,27 +204,21 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
   }
 
   // ---- key sums: reduce the per-thread partials over the row groups (in group order)
-  const bool want_dz = MODE != MODE_DELTA;
-  if (want_dz) {
+  const int64_t slot = static_cast<int64_t>(u) * a.chk + c;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  if constexpr (MODE != MODE_DELTA) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
     __syncthreads();
-  }
-
-  const int64_t DD = static_cast<int64_t>(D) * D;
-  const bool direct = a.chk == 1;
-  float* dz_dst = direct ? a.ws.dz + static_cast<int64_t>(u) * D
-                         : a.ws.dz_part + (static_cast<int64_t>(u) * a.chk + c) * D;
-  if (want_dz) {
     for (int d = tid; d < D; d += kThreads) {
-      float s = 0.f;
-      for (int g = 0; g < TQ; ++g) s += red[g][d];
-      dz_dst[d] = s;
+      float sum = 0.f;
+      for (int g = 0; g < TQ; ++g) sum += red[g][d];
+      a.ws.dz[slot * D + d] = sum;
     }
   }
-  float* u_dst = direct ? a.ws.u_red + u * DD : a.ws.u_part + (static_cast<int64_t>(u) * a.chk + c) * DD;
-  float* g_dst = direct ? a.ws.g_red + u * DD : a.ws.g_part + (static_cast<int64_t>(u) * a.chk + c) * DD;
   if constexpr (kMat) {
+    float* u_dst = a.ws.u + slot * DD;
+    float* g_dst = kDelta ? a.ws.g + slot * DD : nullptr;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
       const int blk = wave * NB + kb;
@@ -270,30 +230,6 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
         u_dst[row * D + col] = acc_u[kb][r];
         if constexpr (kDelta) g_dst[row * D + col] = acc_g[kb][r];
       }
-    }
-  }
-  if (direct) return;
-
-  // ---- the last chunk of the unit to finish adds the partials in chunk order
-  uint32_t* cnt = a.ws.cnt + (MODE == MODE_KEYSUM ? 0 : a.units()) + u;
-  if (!arrive_last(cnt, a.chk)) return;
-  if (want_dz) {
-    for (int d = tid; d < D; d += kThreads) {
-      float s = 0.f;
-      for (int cc = 0; cc < a.chk; ++cc) s += __builtin_nontemporal_load(&a.ws.dz_part[(static_cast<int64_t>(u) * a.chk + cc) * D + d]);
-      a.ws.dz[static_cast<int64_t>(u) * D + d] = s;
-    }
-  }
-  if constexpr (kMat) {
-    for (int e = tid * 4; e < DD; e += kThreads * 4) {
-      f32x4 su = {0.f, 0.f, 0.f, 0.f}, sg = {0.f, 0.f, 0.f, 0.f};
-      for (int cc = 0; cc < a.chk; ++cc) {
-        const int64_t off = (static_cast<int64_t>(u) * a.chk + cc) * DD + e;
-        su += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ws.u_part + off));
-        if constexpr (kDelta) sg += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.ws.g_part + off));
-      }
-      *reinterpret_cast<f32x4*>(a.ws.u_red + u * DD + e) = su;
-      if constexpr (kDelta) *reinterpret_cast<f32x4*>(a.ws.g_red + u * DD + e) = sg;
     }
   }
 }
@@ -362,10 +298,10 @@ __global__ __launch_bounds__(kThreads) void k_state_f32(const WindowArgs a) {
       // U^T [value feature][key feature]; G [key feature][key feature]
       const int64_t e = static_cast<int64_t>(bi * TB + i) * D + bj * TB + j;
       const int64_t et = static_cast<int64_t>(bj * TB + j) * D + bi * TB + i;
-      a.ws.u_red[u * DD + et] = accu[i][j];
-      if (DELTA) a.ws.g_red[u * DD + e] = accg[i][j];
+      a.ws.u[u * DD + et] = accu[i][j];
+      if (DELTA) a.ws.g[u * DD + e] = accg[i][j];
     }
-  if (!DELTA && tid < D) a.ws.dz[static_cast<int64_t>(u) * D + tid] = zsum;
+  if (!DELTA && tid < D) a.ws.dz[static_cast<int64_t>(u) * D + tid] = zsum;   // chk == 1
 }
 
 template <int D>
