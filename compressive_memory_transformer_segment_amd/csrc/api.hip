@@ -86,11 +86,13 @@ size_t unit_bytes(const infini_attn& h) {
 int chunks_for(const infini_attn& h, int w_call) {
   if (!h.bf16) return 1;
   const int units = w_call * h.BH;
-  int chk = (kStateTargetWorkgroups + units - 1) / units;
-  chk = std::min(chk, 8);
-  chk = std::min(chk, std::max(1, h.NP / 64));
-  while (chk > 1 && w_call * chk > h.part_cap) --chk;
-  return std::max(chk, 1);
+  // a power of two (the chain kernel is specialised on it), at most 8, and no more chunks
+  // than 64-token sub-tiles
+  const int want = (kStateTargetWorkgroups + units - 1) / units;
+  int chk = 1;
+  while (chk * 2 <= want && chk * 2 <= 8 && chk * 2 <= std::max(1, h.NP / 64) && w_call * chk * 2 <= h.part_cap)
+    chk *= 2;
+  return chk;
 }
 
 // Workspace layout: one window of units plus the chunk-partial slots.
@@ -235,8 +237,7 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
     a.s0 = s0;
     a.W = std::min(h->window, a.S - s0);
     a.chk = chunks_for(*h, a.W);
-    a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
-    a.chk = (h->N + a.ch - 1) / a.ch;
+    a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));   // trailing chunks may be empty
     hipError_t e = hipSuccess;
     if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
     if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });

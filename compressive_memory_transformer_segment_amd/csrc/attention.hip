@@ -19,6 +19,8 @@
 // when a row maximum grows by more than 2^8 (exact: the final division uses the same
 // stale maximum).  The gated result is staged through LDS and written once with
 // coalesced 16-byte stores.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,6 +32,18 @@ constexpr int kThreads = 256;
 constexpr int kBM = 128;   // queries per workgroup
 constexpr int kBN = 64;    // keys per tile
 constexpr float kTau = 8.f;
+
+template <int N_>
+using IC = std::integral_constant<int, N_>;
+
+// Workgroup -> (unit, query tile): query tiles longest first across all units, so the
+// many short diagonal-heavy tiles fill the tail of the launch.
+template <int BM>
+__device__ __forceinline__ void tile_of_block(int units, int nq, int& u, int& qt) {
+  const int b = static_cast<int>(blockIdx.x);
+  qt = nq - 1 - b / units;
+  u = b % units;
+}
 
 template <int D, bool PARTS>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
@@ -46,8 +60,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
 
   const int units = a.units();
   const int nq = (a.N + kBM - 1) / kBM;
-  const int qt = nq - 1 - static_cast<int>(blockIdx.x) / units;   // longest rows first
-  const int u = static_cast<int>(blockIdx.x) % units;
+  int u, qt;
+  tile_of_block<kBM>(units, nq, u, qt);
   const int BH = a.B * a.H;
   const int s_local = u / BH, bh = u % BH, h = bh % a.H;
   const int n = a.seg_tokens(s_local);
@@ -61,50 +75,58 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
   const int qw0 = q0 + 32 * wave;
   const int q = qw0 + l32;
 
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + row0 * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + row0 * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + row0 * D;
 
-  // Q as the B operand of S^T: lane holds Q[q][16 ks + 8 hl .. +7]
+  // Q as the B operand of S^T: lane holds Q[q][16 ks + 8 hl .. +7]; rows >= n read as 0
   u32x4 qreg[KS];
+  {
+    const auto qr = buffer_rsrc(qg, static_cast<uint32_t>(n) * D * 2);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qreg[ks] = u32x4{0u, 0u, 0u, 0u};
-    if (q < n) qreg[ks] = ld16(qg + (row0 + q) * D + 16 * ks + 8 * hl);
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = buffer_ld16(qr, (static_cast<uint32_t>(q) * D + 16 * ks + 8 * hl) * 2);
   }
 
+  // per-thread byte offsets of the K/V chunks inside a tile, and their LDS slots
+  uint32_t g_off[KCH];
+  int lk_off[KCH], lv_off[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int id = tid + kThreads * i;
+    const int row = id / (D / 8), c = id % (D / 8);
+    g_off[i] = static_cast<uint32_t>(row * D + 8 * c) * 2;
+    lk_off[i] = row * KP + 8 * c;
+    lv_off[i] = row * VP + 8 * c;
+  }
   const int nkv = (min(q0 + kBM, n) + kBN - 1) / kBN;
   u32x4 kpre[KCH], vpre[KCH];
   auto prefetch = [&](int j) {
+    // the resource ends at the segment end: keys past it load as zeros
     const int kv0 = j * kBN;
+    const uint32_t bytes = static_cast<uint32_t>(n - kv0) * D * 2;
+    const auto kr = buffer_rsrc(kg + static_cast<int64_t>(kv0) * D, bytes);
+    const auto vr = buffer_rsrc(vg + static_cast<int64_t>(kv0) * D, bytes);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int id = tid + kThreads * i;
-      const int row = id / (D / 8), c = id % (D / 8);
-      kpre[i] = u32x4{0u, 0u, 0u, 0u};
-      vpre[i] = u32x4{0u, 0u, 0u, 0u};
-      if (kv0 + row < n) {
-        kpre[i] = ld16(kg + (row0 + kv0 + row) * D + 8 * c);
-        vpre[i] = ld16(vg + (row0 + kv0 + row) * D + 8 * c);
-      }
+      kpre[i] = buffer_ld16(kr, g_off[i]);
+      vpre[i] = buffer_ld16(vr, g_off[i]);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](uint16_t* kb, uint16_t* vb) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int id = tid + kThreads * i;
-      st16(&k_lds[buf][id / (D / 8)][8 * (id % (D / 8))], kpre[i]);
-      st16(&v_lds[buf][id / (D / 8)][8 * (id % (D / 8))], vpre[i]);
+      st16(kb + lk_off[i], kpre[i]);
+      st16(vb + lv_off[i], vpre[i]);
     }
   };
-  // transpose-read addressing of the V^T operand: k-slot (hl, i) of k-step j4 is key
-  // 16 j4 + 8 (i / 4) + 4 hl + i % 4, the key the S^T register feeding that slot holds
-  const int tr_g = lane >> 4, tr_j = lane & 15;
-  const int tr_row = 4 * hl + (tr_j >> 2);
-  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_j & 3);
+  // lane offsets of the K operand reads, and of the V^T transpose reads: k-slot (hl, i) of
+  // k-step j4 is key 16 j4 + 8 (i / 4) + 4 hl + i % 4, the key the S^T register feeding
+  // that slot holds
+  const int k_rd = l32 * KP + 8 * hl;
+  const int v_rd = (4 * hl + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   prefetch(0);
-  commit(0);
+  commit(&k_lds[0][0][0], &v_lds[0][0][0]);
   __syncthreads();
 
   const float c2 = a.scale_log2;
@@ -114,8 +136,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc_o[db] = zero16();
 
-  for (int j = 0; j < nkv; ++j) {
-    const int buf = j & 1;
+  auto step = [&](int j, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const uint16_t* kt = &k_lds[buf][0][0];
+    const uint16_t* vt = &v_lds[buf][0][0];
     const bool more = j + 1 < nkv;
     if (more) prefetch(j + 1);
     const int kv0 = j * kBN;
@@ -126,18 +150,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {   // two independent accumulation chains
-          const bf16x8 ak = as_bf16x8(ld16(&k_lds[buf][32 * kb + l32][16 * ks + 8 * hl]));
+          const bf16x8 ak = as_bf16x8(ld16(kt + k_rd + 32 * kb * KP + 16 * ks));
           acc_s[kb] = mfma32x32x16(ak, as_bf16x8(qreg[ks]), acc_s[kb]);
         }
-      // ---- causal mask on tiles that reach past this wave's first query
+      // ---- causal mask on tiles that reach past this wave's first query:
+      // register r of block kb holds key kv0 + 32 kb + 8 (r / 4) + 4 hl + r % 4
       if (kv0 + kBN - 1 > qw0) {
+        const int lim = q - kv0 - 4 * hl;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kv = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (kv > q) acc_s[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) acc_s[kb][r] = -INFINITY;
       }
       // ---- row maximum (this lane's 32 keys, then the other half of the row)
       float mx = acc_s[0][0];
@@ -171,25 +195,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
       bf16x8 pb[4];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x16& s = acc_s[j4 >> 1];
+        const f32x16& sv = acc_s[j4 >> 1];
         const int r0 = 8 * (j4 & 1);
-        pb[j4] = as_bf16x8(u32x4{pack_bf16x2(s[r0 + 0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
-                                 pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
+        pb[j4] = as_bf16x8(u32x4{pack_bf16x2(sv[r0 + 0], sv[r0 + 1]), pack_bf16x2(sv[r0 + 2], sv[r0 + 3]),
+                                 pack_bf16x2(sv[r0 + 4], sv[r0 + 5]), pack_bf16x2(sv[r0 + 6], sv[r0 + 7])});
       }
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) {
-          const uint16_t* vp = &v_lds[buf][16 * j4 + tr_row][32 * db + tr_col];
+          const uint16_t* vp = vt + v_rd + 16 * j4 * VP + 32 * db;
           const u32x2 v0 = lds_read_tr16(vp);
           const u32x2 v1 = lds_read_tr16(vp + 8 * VP);
           const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
           acc_o[db] = mfma32x32x16(av, pb[j4], acc_o[db]);
         }
     }
-    if (more) commit(buf ^ 1);
+    if (more) commit(&k_lds[buf ^ 1][0][0], &v_lds[buf ^ 1][0][0]);
     __syncthreads();
+  };
+  for (int j = 0; j < nkv; j += 2) {
+    step(j, IC<0>{});
+    if (j + 1 < nkv) step(j + 1, IC<1>{});
   }
 
   // ---------------------------------------------------------------- epilogue

@@ -20,11 +20,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D, int EPT, bool BF16>
+template <int D, int EPT, int CHK, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
   constexpr int CG = D / EPT;             // thread columns per row
   constexpr int RB = kThreads / CG;       // rows of M^T per workgroup
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 8;               // segments whose partials are loaded together
   const int BH = a.B * a.H;
   const int bh = blockIdx.x / (D / RB);
   const int rb = (blockIdx.x % (D / RB)) * RB;
@@ -41,22 +41,26 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
   float z = zown ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
 
   for (int s0 = 0; s0 < a.W; s0 += kBatch) {
-    float ut[kBatch][EPT];
-    float dzv[kBatch];
+    // all chunk partials of the batch are independent of the chain: issue them together
+    float ut[kBatch][CHK][EPT];
+    float dzv[kBatch][CHK];
 #pragma unroll
     for (int sb = 0; sb < kBatch; ++sb) {
-      const int s = s0 + sb;
+      const int s = min(s0 + sb, a.W - 1);
       const int64_t u = static_cast<int64_t>(s) * BH + bh;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) ut[sb][e] = 0.f;
-      dzv[sb] = 0.f;
-      if (s < a.W) {
-        for (int c = 0; c < a.chk; ++c) {
-          const int64_t slot = u * a.chk + c;
+      for (int c = 0; c < CHK; ++c) {
+        const int64_t slot = u * CHK + c;
+        const float* src = a.ws.u + slot * DD + static_cast<int64_t>(dv) * D + i0;
+        if constexpr (EPT == 2) {
+          const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+          ut[sb][c][0] = v[0];
+          ut[sb][c][1] = v[1];
+        } else {
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) ut[sb][e] += a.ws.u[slot * DD + static_cast<int64_t>(dv) * D + i0 + e];
-          if (zown) dzv[sb] += a.ws.dz[slot * D + tid];
+          for (int e = 0; e < EPT; ++e) ut[sb][c][e] = src[e];
         }
+        dzv[sb][c] = zown ? a.ws.dz[slot * D + tid] : 0.f;
       }
     }
 #pragma unroll
@@ -80,10 +84,18 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
       }
       if (zown) {
         a.ws.zb[u * D + tid] = z;
-        z += dzv[sb];
+        float dz = 0.f;
+#pragma unroll
+        for (int c = 0; c < CHK; ++c) dz += dzv[sb][c];
+        z += dz;
       }
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) m[e] += ut[sb][e];
+      for (int e = 0; e < EPT; ++e) {
+        float add = 0.f;
+#pragma unroll
+        for (int c = 0; c < CHK; ++c) add += ut[sb][c][e];
+        m[e] += add;
+      }
     }
   }
 #pragma unroll
@@ -184,8 +196,11 @@ hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
     constexpr int EPT = 2;
     constexpr int RB = kThreads / (D / EPT);
     const dim3 grid(BH * (D / RB));
-    if (a.bf16) hipLaunchKernelGGL((k_chain_linear<D, EPT, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_chain_linear<D, EPT, false>), grid, dim3(kThreads), 0, st, a);
+    if (!a.bf16) hipLaunchKernelGGL((k_chain_linear<D, EPT, 1, false>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_linear<D, EPT, 1, true>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_linear<D, EPT, 2, true>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_linear<D, EPT, 4, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_chain_linear<D, EPT, 8, true>), grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }
