@@ -28,7 +28,7 @@ struct infini_attn {
   int window;          // segments per window
   int part_cap;        // chunk-partial slots per (b,h): >= W_call * chk_call
   float* M;            // [B,H,D,D]
-  float* z;            // [B,H,D]
+  float* z;            // [B,H,D], stored right after M
   float* gate;         // [2H]: sigmoid(beta), 1 - sigmoid(beta)
   void* ws_base;
   size_t ws_bytes;
@@ -41,6 +41,25 @@ struct infini_attn {
 };
 
 namespace {
+
+// Zero fill by a kernel rather than hipMemsetAsync, so that a caller may capture the
+// reset in a HIP graph.
+__global__ void k_zero_f32(float* p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * 4;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<float4*>(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      for (int64_t k = i; k < n; ++k) p[k] = 0.f;
+    }
+  }
+}
+
+hipError_t zero_f32(float* p, int64_t n, hipStream_t st) {
+  const int64_t blocks = std::min<int64_t>((n + 1023) / 1024, 1024);
+  hipLaunchKernelGGL(k_zero_f32, dim3(static_cast<unsigned>(std::max<int64_t>(blocks, 1))), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
 
 std::mutex g_live_mu;
 std::unordered_set<const infini_attn*> g_live;
@@ -309,11 +328,12 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   const size_t DD = size_t(h->D) * h->D;
   const size_t m_bytes = size_t(h->BH) * DD * 4, z_bytes = size_t(h->BH) * h->D * 4;
   const size_t ws_bytes = layout_bytes(*h);
-  if (hipMalloc(&h->M, m_bytes) != hipSuccess) { delete h; return INFINI_ERR_OOM; }
-  if (hipMalloc(&h->z, z_bytes) != hipSuccess) { (void)hipFree(h->M); delete h; return INFINI_ERR_OOM; }
+  // M and z in one allocation (z follows M), so one fill resets both
+  if (hipMalloc(&h->M, m_bytes + z_bytes) != hipSuccess) { (void)hipGetLastError(); delete h; return INFINI_ERR_OOM; }
+  h->z = h->M + size_t(h->BH) * DD;
   if (hipMalloc(&h->gate, size_t(2) * c.heads * 4) != hipSuccess ||
       hipMalloc(&h->ws_base, ws_bytes) != hipSuccess) {
-    (void)hipFree(h->M); (void)hipFree(h->z); (void)hipFree(h->gate);
+    (void)hipFree(h->M); (void)hipFree(h->gate);
     delete h;
     (void)hipGetLastError();
     return INFINI_ERR_OOM;
@@ -329,8 +349,7 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   hipError_t e = hipMemcpy(h->gate, gv, size_t(2) * c.heads * 4, hipMemcpyHostToDevice);
   delete[] gv;
-  if (e == hipSuccess) e = hipMemsetAsync(h->M, 0, m_bytes, st);
-  if (e == hipSuccess) e = hipMemsetAsync(h->z, 0, z_bytes, st);
+  if (e == hipSuccess) e = hipMemsetAsync(h->M, 0, m_bytes + z_bytes, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) { infini_attn_destroy(h); return INFINI_ERR_HIP; }
   *out = h;
@@ -346,8 +365,7 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   DeviceGuard dg(h->device);
   const hipError_t e = hipDeviceSynchronize();
   for (hipEvent_t ev : h->ev_pool) (void)hipEventDestroy(ev);
-  (void)hipFree(h->M);
-  (void)hipFree(h->z);
+  (void)hipFree(h->M);   // also holds z
   (void)hipFree(h->gate);
   (void)hipFree(h->ws_base);
   delete h;
@@ -376,9 +394,8 @@ INFINI_EXPORT int infini_attn_reset_state(infini_attn_t h, void* hip_stream) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const size_t DD = size_t(h->D) * h->D;
-  hipError_t e = hipMemsetAsync(h->M, 0, size_t(h->BH) * DD * 4, st);
-  if (e == hipSuccess) e = hipMemsetAsync(h->z, 0, size_t(h->BH) * h->D * 4, st);
+  const int64_t DD = int64_t(h->D) * h->D;
+  const hipError_t e = zero_f32(h->M, int64_t(h->BH) * (DD + h->D), st);   // M and z
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
 

@@ -98,9 +98,10 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
     __syncthreads();
   }
 
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
-  const int64_t row_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D + dq * 8;
+  // the segment's K and V rows as buffer resources: rows at or past n read as zeros
+  const int64_t seg_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
+  const auto krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + seg_base, static_cast<uint32_t>(p.n) * D * 2);
+  const auto vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + seg_base, static_cast<uint32_t>(p.n) * D * 2);
 
   float zacc[8];
 #pragma unroll
@@ -112,25 +113,32 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
 #pragma unroll
   for (int k = 0; k < (kDelta ? NB : 1); ++k) acc_g[k] = zero16();
 
+  // sub-tile loads, one sub-tile ahead of the one being processed
+  u32x4 kcur[RPT], vcur[RPT];
+  auto load = [&](int ts, u32x4 (&kd)[RPT], u32x4 (&vd)[RPT]) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const uint32_t off = (static_cast<uint32_t>(ts + tq * RPT + r) * D + dq * 8) * 2;
+      kd[r] = buffer_ld16(krs, off);
+      if constexpr (kMat) vd[r] = buffer_ld16(vrs, off);
+    }
+  };
   const int t_begin = c * a.ch;
   const int t_end = min(t_begin + a.ch, p.n);
+  if (t_begin < t_end) load(t_begin, kcur, vcur);
   for (int ts = t_begin; ts < t_end; ts += kSub) {
-    // ---- load RPT rows x 8 features of K (and V), form sigma(K) in fp32
+    u32x4 knext[RPT], vnext[RPT];
+    if (ts + kSub < t_end) load(ts + kSub, knext, vnext);
+    // ---- sigma(K) in fp32 for this thread's RPT rows x 8 features
     float sk[RPT][8];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const int tl = tq * RPT + r;
       const int t = ts + tl;
-      u32x4 kr = {0u, 0u, 0u, 0u};
-      if (t < p.n) kr = ld16(kg + row_base + static_cast<int64_t>(t) * D);
-      if constexpr (kMat) {
-        u32x4 vr = {0u, 0u, 0u, 0u};
-        if (t < p.n) vr = ld16(vg + row_base + static_cast<int64_t>(t) * D);
-        st16(&v_s[tl][dq * 8], vr);
-      }
+      if constexpr (kMat) st16(&v_s[tl][dq * 8], vcur[r]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x0 = bf16lo_to_f32(kr[i]), x1 = bf16hi_to_f32(kr[i]);
+        const float x0 = bf16lo_to_f32(kcur[r][i]), x1 = bf16hi_to_f32(kcur[r][i]);
         sk[r][2 * i] = (t < p.n) ? elu_plus_one(x0) : 0.f;
         sk[r][2 * i + 1] = (t < p.n) ? elu_plus_one(x1) : 0.f;
       }
@@ -200,6 +208,11 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
         }
       }
       __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      kcur[r] = knext[r];
+      if constexpr (kMat) vcur[r] = vnext[r];
     }
   }
 
