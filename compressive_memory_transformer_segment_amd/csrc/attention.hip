@@ -48,7 +48,7 @@ __device__ __forceinline__ void tile_of_block(int units, int nq, int& u, int& qt
 }
 
 template <int D, bool PARTS>
-__global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
+__global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(const WindowArgs a) {
   constexpr int KS = D / 16;                  // k-steps over the head dimension
   constexpr int DB = D / 32;                  // 32-row blocks of the head dimension
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -187,24 +187,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
     float mx = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_across_halves(mx);
     const float mxs = mx * c2;
     const bool need = __any(mxs > m_run + kTau);
     const float m_use = need ? fmaxf(m_run, mxs) : m_run;
     alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_use;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -m_run));
+    // P in bf16 (the MFMA operand); the row sum adds the same rounded values, so the
+    // weights the output is normalised with are exactly the ones it was accumulated with
+    u32x4 pw[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pw[i >> 2][i & 3] = pack_bf16x2(sc[2 * i], sc[2 * i + 1]);
     float ls = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -m_run));
-      sc[r] = pv;
-      ls += pv;
-    }
+    for (int i = 0; i < 8; ++i) ls = add_bf16x2(pw[i >> 2][i & 3], ls);
     l_part = fmaf(l_part, alpha, ls);
-    p_lo = as_bf16x8(u32x4{pack_bf16x2(sc[0], sc[1]), pack_bf16x2(sc[2], sc[3]),
-                           pack_bf16x2(sc[4], sc[5]), pack_bf16x2(sc[6], sc[7])});
-    p_hi = as_bf16x8(u32x4{pack_bf16x2(sc[8], sc[9]), pack_bf16x2(sc[10], sc[11]),
-                           pack_bf16x2(sc[12], sc[13]), pack_bf16x2(sc[14], sc[15])});
+    p_lo = as_bf16x8(pw[0]);
+    p_hi = as_bf16x8(pw[1]);
     return need;
   };
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
@@ -235,8 +236,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
         acc_o[db] = mfma32x32x16(av, jj ? p_hi : p_lo, acc_o[db]);
       }
   };
-  auto tile_body = [&](const uint16_t* kt, int kv0, auto maskc) __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(maskc)::value != 0;
+  // The mask test is a wave-uniform branch around the masking only: one copy of the tile
+  // body, so the accumulators keep their registers on every path.
+  auto tile_body = [&](const uint16_t* kt, int kv0, bool kMask) __attribute__((always_inline)) {
     f32x16 s0, s1;
     bf16x8 p0, p1, p2, p3;
     float a0, a1;
@@ -259,8 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
     else load_mt(other);
     const int kv0 = j * kBN;
     if (kv0 <= qw0 + 31) {
-      if (kv0 + kBN - 1 > qw0) tile_body(kt, kv0, IC<1>{});   // some keys past this wave's queries
-      else tile_body(kt, kv0, IC<0>{});
+      tile_body(kt, kv0, kv0 + kBN - 1 > qw0);   // mask when some keys lie past this wave's queries
     }
     __syncthreads();   // waits for this wave's copies, then for every wave's
   };
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
   // M^T_{s-1} is in buffer nkv % 2 (z_{s-1} in zsh); the output is staged in the other one
   const uint16_t* mts = (nkv & 1) ? buf1 : buf0;
   uint16_t* ost = ((nkv & 1) ? buf0 : buf1) + wave * 32 * D;
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = sum_across_halves(l_part);
   const float inv_l = 1.f / l_tot;
 
   // sigma(Q) as the B operand of the retrieval, and the denominator sigma(q) . z_{s-1}
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(const WindowArgs a) {
     sq[ks] = as_bf16x8(u32x4{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
                              pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7])});
   }
-  den += __shfl_xor(den, 32);
+  den = sum_across_halves(den);
   const float inv_den = 1.f / (den + a.eps);
   const float g = a.gate_g[h], omg = a.gate_omg[h];
 

@@ -47,6 +47,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Lane l and lane l ^ 32 combined without LDS (v_permlane32_swap): the swap leaves the
+// low half's values in both halves of one register and the high half's in the other.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc + lo + hi of a packed bf16 pair (v_dot2 against (1, 1); the products are exact).
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
 // sigma(x) = ELU(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise.
 __device__ __forceinline__ float elu_plus_one(float x) {
   return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e);

@@ -61,7 +61,7 @@ def attention_kernel_flops(batch, heads, head_dim, segment_len, n_tokens) -> flo
 
 
 def attention_kernel_bytes(batch, heads, head_dim, segment_len, n_tokens) -> float:
-    """Algorithmic HBM bytes of the fused attention kernel: Q, K, V^T read once (bf16),
+    """Algorithmic HBM bytes of the fused attention kernel: Q, K, V read once (bf16),
     out written once (bf16), M^T (bf16) and z (fp32) read once per segment."""
     d = head_dim
     segs = len(segment_lengths(n_tokens, segment_len))
@@ -79,12 +79,19 @@ def kernel_source_hash() -> str:
 # ---------------------------------------------------------------------- rocprofv3 summaries
 
 def _short(name: str) -> str:
-    base = name.split("(")[0]
+    """Kernel name without namespaces and argument list, template arguments kept."""
     for key in ("k_attn_bf16", "k_attn_f32", "k_state_bf16", "k_state_f32", "k_keysum_f32",
-                "k_chain_linear", "k_chain_delta"):
-        if key in base:
-            return key + name[len(base.split(key)[0]) + len(key):].split("(")[0].replace("infini::", "")
-    return base[:80]
+                "k_chain_linear", "k_chain_delta", "k_zero_f32"):
+        i = name.find(key)
+        if i >= 0:
+            rest = name[i:]
+            j = rest.find("(")
+            return rest[:j] if j >= 0 else rest
+    if "copyBuffer" in name:
+        return "__amd_rocclr_copyBuffer"
+    if "direct_copy_kernel" in name:
+        return "torch direct_copy_kernel (input staging)"
+    return (name.split("(")[0] or "(unnamed)")[:80]
 
 
 def stats_table(path: str) -> str:

@@ -20,7 +20,7 @@ Breakdown".  Equation numbers are the ones that page uses in its prose:
 * Eq. 9  -- delta-rule update  M_s = M_{s-1} + sigma(K)^T (V - sigma(K)M_{s-1}/(sigma(K)z_{s-1}))
 * Eq. 10 -- per-head gate  A = sigmoid(beta) A_mem + (1 - sigmoid(beta)) A_dot
 
-Readings taken where the page is silent or loose (each is also listed in the design doc):
+Readings taken where the page is silent or loose:
 
 1. Softmax scale: the page prints 1/sqrt(d_model) but also says the local attention is
    vanilla per-head attention.  The scale is an explicit argument; ``None`` means
