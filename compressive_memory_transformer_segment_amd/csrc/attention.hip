@@ -30,62 +30,104 @@ namespace infini {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBM = 128;   // queries per workgroup (4 waves x 32)
-constexpr int kBN = 64;    // keys per tile
+constexpr int kThreads = 256;    // float32 path
+constexpr int kThreadsA = 512;   // bf16 path: 8 waves
+constexpr int kBMA = 256;        // bf16 path: queries per workgroup (8 waves x 32)
+constexpr int kBN = 64;          // keys per tile
 constexpr float kTau = 8.f;
 
 template <int N_>
 using IC = std::integral_constant<int, N_>;
 
-// Workgroup -> (unit, query tile): query tiles longest first across all units, so the
-// many short diagonal-heavy tiles fill the tail of the launch.
+// Workgroup -> (unit, query tile).  Workgroups are dispatched to the 8 XCDs round-robin
+// (block b to XCD b % 8), and each XCD has its own L2.  When the unit count is a multiple
+// of 8, XCD x takes the units u = x + 8 k in groups of kGroup units; inside a group the
+// query tiles run longest first.  About kGroup units' K and V are then live in one L2 at
+// a time, and the short diagonal tiles of each group fill in behind the long ones.
+// Otherwise: longest tiles first across all units.
+constexpr int kGroup = 4;
 template <int BM>
 __device__ __forceinline__ void tile_of_block(int units, int nq, int& u, int& qt) {
   const int b = static_cast<int>(blockIdx.x);
-  qt = nq - 1 - b / units;
-  u = b % units;
+  if (units % 8 != 0) {
+    qt = nq - 1 - b / units;
+    u = b % units;
+    return;
+  }
+  const int x = b % 8, i = b / 8;            // XCD and position in its sequence
+  const int per_x = units / 8;               // units of this XCD
+  const int gi = i / (kGroup * nq);          // group index
+  const int g_units = min(kGroup, per_x - gi * kGroup);
+  const int r = i - gi * kGroup * nq;        // position inside the group
+  qt = nq - 1 - r / g_units;
+  u = x + 8 * (gi * kGroup + r % g_units);
+}
+
+// s_waitcnt with vmcnt <= vm and lgkmcnt = 0 (expcnt not waited on); gfx9 encoding.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm_le(int vm) {   // vm wave-uniform, 0 .. 15
+  switch (vm) {
+    case 0: wait_vm_lgkm0<0>(); break;
+    case 1: wait_vm_lgkm0<1>(); break;
+    case 2: wait_vm_lgkm0<2>(); break;
+    case 3: wait_vm_lgkm0<3>(); break;
+    case 4: wait_vm_lgkm0<4>(); break;
+    case 5: wait_vm_lgkm0<5>(); break;
+    case 6: wait_vm_lgkm0<6>(); break;
+    case 7: wait_vm_lgkm0<7>(); break;
+    case 8: wait_vm_lgkm0<8>(); break;
+    case 9: wait_vm_lgkm0<9>(); break;
+    case 10: wait_vm_lgkm0<10>(); break;
+    default: wait_vm_lgkm0<0>(); break;
+  }
 }
 
 template <int D, bool PARTS>
-__global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(const WindowArgs a) {
+__global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(const WindowArgs a) {
   constexpr int KS = D / 16;                  // k-steps over the head dimension
   constexpr int DB = D / 32;                  // 32-row blocks of the head dimension
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = kBN * D;               // elements of one K or V tile
   constexpr int BUF = 2 * TILE;               // one buffer: [K tile | V tile]
-  constexpr int NV = D / 32;                  // 1 KB copies per wave for a V tile
-  static_assert(kBM * D <= BUF && D * D <= BUF, "Q, M^T and the output fit in one buffer");
+  constexpr int CW = CPR / 8;                 // 1 KB copies per wave for a K (or V) tile
+  constexpr int MW = D * D / 4096;            // ... for M^T_{s-1}
+  static_assert(D * D <= BUF && 4 * 32 * D <= BUF, "M^T and four waves' output fit in one buffer");
 
   // LDS layouts (bf16, 16-byte chunks; chunk c of a row holds columns 8c .. 8c + 7):
-  //  "row groups" for K, Q and M^T: chunk c of row r sits in slot
-  //      (r / 16) * 16 CPR + 16 c + r % 16,
+  //  "row groups" for K and M^T: chunk c of row r sits in slot (r / 16) * 16 CPR + 16 c + r % 16,
   //  so the 16 rows an MFMA operand read touches at one chunk are 16 consecutive slots
   //  (one 256-byte bank line), and every k-step / row block is an immediate offset;
   //  "quads" for V: chunk c of row r sits in slot (r / 4) * 4 CPR + 4 c + r % 4, so the
   //  4 rows x 64 bytes a transpose read takes per half-wave are 16 consecutive slots.
-  // Each layout is filled by 1 KB buffer -> LDS copies (64 lanes x 16 bytes, lane i to
-  // slot 64 k + i of copy k); everything that differs between a wave's copies is in the
-  // scalar resource base and the LDS base, so one offset register per layout suffices.
-  // The output is staged row-major with chunk c of row r at physical chunk c ^ swz(r).
+  // Both are filled by 1 KB buffer -> LDS copies (64 lanes x 16 bytes, lane i to slot
+  // 64 c + i of copy c); what differs between a wave's copies sits in the scalar resource
+  // base and the LDS base, so one offset register per layout suffices.
+  // Four buffers: the copy of tile j + 3 (then M^T_{s-1}) is in flight while tile j is
+  // consumed.  After the loop the output is staged row-major, chunk c of row r at
+  // physical chunk c ^ swz(r), in two of the free buffers.
   __shared__ __align__(16) uint16_t buf0[BUF];
   __shared__ __align__(16) uint16_t buf1[BUF];
+  __shared__ __align__(16) uint16_t buf2[BUF];
+  __shared__ __align__(16) uint16_t buf3[BUF];
   __shared__ __align__(16) float zsh[256];
 
   const int units = a.units();
-  const int nq = (a.N + kBM - 1) / kBM;
+  const int nq = (a.N + kBMA - 1) / kBMA;
   int u, qt;
-  tile_of_block<kBM>(units, nq, u, qt);
+  tile_of_block<kBMA>(units, nq, u, qt);
   const int BH = a.B * a.H;
   const int s_local = u / BH, bh = u % BH, h = bh % a.H;
   const int n = a.seg_tokens(s_local);
-  const int q0 = qt * kBM;
+  const int q0 = qt * kBMA;
   if (q0 >= n) return;
   const int64_t tok0 = static_cast<int64_t>(a.s0 + s_local) * a.N;
   const int64_t row0 = static_cast<int64_t>(bh) * a.T + tok0;   // token row of the segment start
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, 0 .. 7
   const int l32 = lane & 31, hl = lane >> 5;
   const int qw0 = q0 + 32 * wave;
   const int q = qw0 + l32;
@@ -94,9 +136,19 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + row0 * D;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + row0 * D;
 
+  // Q as the B operand of S^T, straight from HBM: lane holds Q[q][16 ks + 8 hl .. +7];
+  // rows >= n read as zeros.  Issued first, so the tile waits below also cover it.
+  u32x4 qreg[KS];
+  {
+    const auto qr = buffer_rsrc(qg + static_cast<int64_t>(qw0) * D,
+                                static_cast<uint32_t>(max(n - qw0, 0)) * D * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = buffer_ld16(qr, static_cast<uint32_t>(l32 * D + 16 * ks + 8 * hl) * 2);
+  }
+
   // source byte offsets of this lane's 16 bytes within a copy:
-  //   row groups, copy (g, j): rows 16 g + lane % 16, chunk 4 j + lane / 16
-  //   quads, copy k: rows 4 (CPR k / 16 + lane / (4 CPR)) + lane % 4, chunk (lane / 4) % CPR
+  //   row groups, copy c = (CPR / 4) g + j: row 16 g + lane % 16, chunk 4 j + lane / 16
+  //   quads, copy c: row 4 (CPR c / 16 + lane / (4 CPR)) + lane % 4, chunk (lane / 4) % CPR
   const uint32_t lp_g = (lane & 15) * (2 * D) + 16 * (lane >> 4);
   const uint32_t lp_v = (((lane >> 2) / CPR) * 4 + (lane & 3)) * (2 * D) + 16 * ((lane >> 2) % CPR);
   // one copy: the resource starts `shift` bytes into the source (bytes past `bytes` of the
@@ -106,43 +158,54 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
     const int left = __builtin_amdgcn_readfirstlane(max(static_cast<int>(bytes) - static_cast<int>(shift), 0));
     buffer_to_lds16(buffer_rsrc(static_cast<const char*>(src) + shift, static_cast<uint32_t>(left)), lds, voff);
   };
-  // row-group copies of this wave's GW groups (of 16 rows) of a tile
-  auto copy_groups = [&](auto gwc, const void* src, uint32_t bytes, uint16_t* dst) __attribute__((always_inline)) {
-    constexpr int GW = decltype(gwc)::value;
-#pragma unroll
-    for (int gg = 0; gg < GW; ++gg)
-#pragma unroll
-      for (int j = 0; j < CPR / 4; ++j) {
-        const int g = wave * GW + gg;
-        copy1k(src, bytes, g * 32 * D + 64 * j, reinterpret_cast<char*>(dst) + (g * (CPR / 4) + j) * 1024, lp_g);
-      }
+  auto copy_group = [&](int c, const void* src, uint32_t bytes, uint16_t* dst) __attribute__((always_inline)) {
+    const int g = c / (CPR / 4), j = c % (CPR / 4);
+    copy1k(src, bytes, g * 32 * D + 64 * j, reinterpret_cast<char*>(dst) + c * 1024, lp_g);
   };
   auto bufp = [&](auto bc) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (decltype(bc)::value == 0) return buf0;
-    else return buf1;
+    constexpr int b = decltype(bc)::value & 3;
+    if constexpr (b == 0) return buf0;
+    else if constexpr (b == 1) return buf1;
+    else if constexpr (b == 2) return buf2;
+    else return buf3;
   };
-  const int nkv = (min(q0 + kBM, n) + kBN - 1) / kBN;
-  // K and V of tile j; rows at or past the segment end arrive as zeros
-  auto load_tile = [&](int j, uint16_t* dst) __attribute__((always_inline)) {
-    const int kv0 = j * kBN;
-    const uint32_t bytes = static_cast<uint32_t>(n - kv0) * D * 2;
-    copy_groups(IC<1>{}, kg + static_cast<int64_t>(kv0) * D, bytes, dst);
-    const uint16_t* vsrc = vg + static_cast<int64_t>(kv0) * D;
+  const int nkv = (min(q0 + kBMA, n) + kBN - 1) / kBN;
+  // Copy number i of the sequence: K and V of tile i for i < nkv (rows at or past the
+  // segment end arrive as zeros), M^T_{s-1} and z_{s-1} for i == nkv, nothing after.
+  // Returns how many copy instructions this wave issued.
+  auto issue = [&](int i, uint16_t* dst) __attribute__((always_inline)) -> int {
+    if (i < nkv) {
+      const int kv0 = i * kBN;
+      const uint32_t bytes = static_cast<uint32_t>(n - kv0) * D * 2;
+      const uint16_t* ksrc = kg + static_cast<int64_t>(kv0) * D;
+      const uint16_t* vsrc = vg + static_cast<int64_t>(kv0) * D;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int k = wave * NV + i;
-      copy1k(vsrc, bytes, 1024 * k, reinterpret_cast<char*>(dst + TILE) + 1024 * k, lp_v);
+      for (int t = 0; t < CW; ++t) copy_group(wave * CW + t, ksrc, bytes, dst);
+#pragma unroll
+      for (int t = 0; t < CW; ++t) {
+        const int c = wave * CW + t;
+        copy1k(vsrc, bytes, 1024 * c, reinterpret_cast<char*>(dst + TILE) + 1024 * c, lp_v);
+      }
+      return 2 * CW;
     }
+    if (i == nkv) {
+      const uint16_t* msrc = static_cast<const uint16_t*>(a.ws.mt) + static_cast<int64_t>(u) * D * D;
+#pragma unroll
+      for (int t = 0; t < MW; ++t) copy_group(wave * MW + t, msrc, D * D * 2, dst);
+      if (wave == 0) {   // lanes past D / 4 read zeros
+        copy1k(a.ws.zb + static_cast<int64_t>(u) * D, D * 4, 0, zsh, static_cast<uint32_t>(lane) * 16);
+        return MW + 1;
+      }
+      return MW;
+    }
+    return 0;
   };
-  // M^T_{s-1} ([d_value][d_key]) and z_{s-1} for the epilogue
-  auto load_mt = [&](uint16_t* dst) __attribute__((always_inline)) {
-    copy_groups(IC<D / 64>{}, static_cast<const uint16_t*>(a.ws.mt) + static_cast<int64_t>(u) * D * D, D * D * 2, dst);
-    if (wave == 0)   // lanes past D / 4 read zeros
-      copy1k(a.ws.zb + static_cast<int64_t>(u) * D, D * 4, 0, zsh, static_cast<uint32_t>(lane) * 16);
+  auto count = [&](int i) __attribute__((always_inline)) -> int {
+    return i < nkv ? 2 * CW : (i == nkv ? MW + (wave == 0 ? 1 : 0) : 0);
   };
+
   // element offsets of this lane's operand reads
-  //  K / Q / M^T (row groups): row 32 blk + l32, chunk 2 ks + hl
-  //    -> g_rd + blk * 256 CPR + ks * 256
+  //  K / M^T (row groups): row 32 blk + l32, chunk 2 ks + hl -> g_rd + blk * 256 CPR + ks * 256
   //  V^T (quads, transpose reads): k-slot (hl, i) of k-step j4 is key
   //    16 j4 + 8 (i / 4) + 4 hl + i % 4, the key the S^T register feeding that slot holds;
   //    the lane addresses row 16 j4 + 8 s + 4 hl + (lane % 16) / 4 and columns
@@ -153,16 +216,13 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
                    4 * (lane & 1);
   auto swz = [](int row) __attribute__((always_inline)) -> int { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
 
-  // ---- prologue: the Q tile into buffer 1, tile 0 into buffer 0
-  u32x4 qreg[KS];
+  // ---- prologue: copies 0, 1, 2 of the sequence; wait for tile 0
   {
-    copy_groups(IC<2>{}, qg + static_cast<int64_t>(q0) * D, static_cast<uint32_t>(n - q0) * D * 2, buf1);
-    load_tile(0, buf0);
-    __syncthreads();
-    // Q as the B operand of S^T: lane holds Q[q][16 ks + 8 hl .. +7]; rows >= n are 0
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = ld16(buf1 + g_rd + wave * 256 * CPR + 256 * ks);
-    __syncthreads();   // buffer 1 is free again before tile 1 is copied there
+    issue(0, buf0);
+    const int c1 = issue(1, buf1);
+    const int c2 = issue(2, buf2);
+    wait_vm_le(c1 + c2);
+    __builtin_amdgcn_s_barrier();
   }
 
   const float c2 = a.scale_log2;
@@ -172,41 +232,36 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc_o[db] = zero16();
 
-  // One 64-key tile is processed as two 32-key halves, each a full online-softmax step
-  // (S_h = K_h Q^T, masked, exponentiated, O += V_h P_h); the running maximum moves only
-  // when some row's grows by more than 2^kTau (decided per wave), and the accumulator is
-  // then rescaled before the half's product is added.
-  auto half_softmax = [&](f32x16& sc, int kvh, bool mask, bf16x8& p_lo, bf16x8& p_hi, float& alpha)
-      __attribute__((always_inline)) -> bool {
-    if (mask) {
-      // register r holds key kvh + 8 (r / 4) + 4 hl + r % 4
-      const int lim = q - kvh - 4 * hl;
+  // Online softmax, one decision per 64-key tile: the running maximum m_run (log2 domain,
+  // scale folded in) moves only when some row's maximum over the tile exceeds it by more
+  // than kTau (decided per wave); O and the row sum are then rescaled once, before any of
+  // the tile's products.  Otherwise the tile is straight-line code.
+  auto mask_half = [&](f32x16& sc, int kvh) __attribute__((always_inline)) {
+    // register r holds key kvh + 8 (r / 4) + 4 hl + r % 4
+    const int lim = q - kvh - 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : sc[r];
-    }
+    for (int r = 0; r < 16; ++r) sc[r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : sc[r];
+  };
+  auto half_max = [&](const f32x16& sc) __attribute__((always_inline)) -> float {
     float mx = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = max_across_halves(mx);
-    const float mxs = mx * c2;
-    const bool need = __any(mxs > m_run + kTau);
-    const float m_use = need ? fmaxf(m_run, mxs) : m_run;
-    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_use;
+    return mx;
+  };
+  // P = exp2(scale log2e S - m_run) in bf16 (the MFMA operand); the row sum adds the same
+  // rounded values, so the output is normalised with exactly the weights it accumulated
+  auto half_exp = [&](f32x16& sc, bf16x8& p_lo, bf16x8& p_hi) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -m_run));
-    // P in bf16 (the MFMA operand); the row sum adds the same rounded values, so the
-    // weights the output is normalised with are exactly the ones it was accumulated with
     u32x4 pw[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) pw[i >> 2][i & 3] = pack_bf16x2(sc[2 * i], sc[2 * i + 1]);
-    float ls = 0.f;
+    float ls = l_part;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ls = add_bf16x2(pw[i >> 2][i & 3], ls);
-    l_part = fmaf(l_part, alpha, ls);
+    l_part = ls;
     p_lo = as_bf16x8(pw[0]);
     p_hi = as_bf16x8(pw[1]);
-    return need;
   };
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
 #pragma unroll
@@ -214,17 +269,26 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
   };
-  auto qk_half = [&](const uint16_t* kt, int half, f32x16& sc) __attribute__((always_inline)) {
-    sc = zero16();
+  // S^T of both halves: all 2 KS K-operand reads are issued first (their LDS latency then
+  // overlaps), and the two accumulation chains alternate so that consecutive MFMAs are
+  // independent.
+  auto qk_tile = [&](const uint16_t* kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+    bf16x8 ak[2][KS];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ak[hh][ks] = as_bf16x8(ld16(kt + g_rd + hh * 256 * CPR + 256 * ks));
+    __builtin_amdgcn_sched_barrier(0);
+    s0 = zero16();
+    s1 = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ak = as_bf16x8(ld16(kt + g_rd + half * 256 * CPR + 256 * ks));
-      sc = mfma32x32x16(ak, as_bf16x8(qreg[ks]), sc);
+      s0 = mfma32x32x16(ak[0][ks], as_bf16x8(qreg[ks]), s0);
+      s1 = mfma32x32x16(ak[1][ks], as_bf16x8(qreg[ks]), s1);
     }
   };
-  // k-steps j4 = 2 half + {0, 1} of the P V product take their keys from this half
-  auto pv_half = [&](const uint16_t* kt, int half, const bf16x8& p_lo, const bf16x8& p_hi)
-      __attribute__((always_inline)) {
+  // V^T operands of one half (k-steps j4 = 2 half + {0, 1} take their keys from it)
+  auto v_operands = [&](const uint16_t* kt, int half, bf16x8 (&av)[DB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -232,48 +296,91 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
         const uint16_t* vp = kt + v_rd + 4 * (2 * half + jj) * 32 * CPR + 128 * db;
         const u32x2 v0 = lds_read_tr16(vp);
         const u32x2 v1 = lds_read_tr16(vp + 2 * 32 * CPR);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
-        acc_o[db] = mfma32x32x16(av, jj ? p_hi : p_lo, acc_o[db]);
+        av[db][jj] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
       }
   };
-  // The mask test is a wave-uniform branch around the masking only: one copy of the tile
-  // body, so the accumulators keep their registers on every path.
-  auto tile_body = [&](const uint16_t* kt, int kv0, bool kMask) __attribute__((always_inline)) {
+  auto pv = [&](const bf16x8 (&av)[DB][2], const bf16x8& p_lo, const bf16x8& p_hi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[db] = mfma32x32x16(av[db][jj], jj ? p_hi : p_lo, acc_o[db]);
+  };
+  // One tile: S_A = K_A Q^T and S_B = K_B Q^T (keys kv0 .. and kv0 + 32 ..), the tile
+  // maximum, a rare rescale, then P_A, O += V_A P_A, P_B, O += V_B P_B.  The V^T reads of a
+  // half are issued before its exponentials, which cover their latency; the exponentials
+  // of B run under the MFMAs of A.
+  auto tile_body = [&](const uint16_t* kt, int kv0, auto maskc) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(maskc)::value != 0;
     f32x16 s0, s1;
     bf16x8 p0, p1, p2, p3;
-    float a0, a1;
-    qk_half(kt, 0, s0);
-    const bool n0 = half_softmax(s0, kv0, kMask, p0, p1, a0);
-    if (n0) rescale(a0);
-    pv_half(kt, 0, p0, p1);
-    qk_half(kt, 1, s1);
-    const bool n1 = half_softmax(s1, kv0 + 32, kMask, p2, p3, a1);
-    if (n1) rescale(a1);
-    pv_half(kt, 1, p2, p3);
+    qk_tile(kt, s0, s1);
+    if constexpr (kMask) {
+      mask_half(s0, kv0);
+      mask_half(s1, kv0 + 32);
+    }
+    const float mxs = max_across_halves(fmaxf(half_max(s0), half_max(s1))) * c2;
+    if (__any(mxs > m_run + kTau)) {
+      const float m_use = fmaxf(m_run, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      rescale(alpha);
+      l_part *= alpha;
+      m_run = m_use;
+    }
+    bf16x8 va[DB][2], vb[DB][2];
+    v_operands(kt, 0, va);
+    half_exp(s0, p0, p1);
+    v_operands(kt, 1, vb);
+    pv(va, p0, p1);
+    half_exp(s1, p2, p3);
+    pv(vb, p2, p3);
   };
 
-  // iteration j: buffer j%2 holds tile j; tile j+1 (or M^T) is copied into the other one
-  auto step = [&](int j, auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
+  // iteration j: buffer j % 4 holds tile j; copy j + 3 of the sequence goes into buffer
+  // (j + 3) % 4, consumed in iteration j - 1.  The closing wait lets this wave's copies
+  // j + 2 and j + 3 stay in flight; after the barrier tile j + 1 is complete for every wave.
+  auto step = [&](int j, auto bufc, auto maskc) __attribute__((always_inline)) {
+    constexpr int b = decltype(bufc)::value;
+    constexpr bool kMask = decltype(maskc)::value != 0;
     const uint16_t* kt = bufp(bufc);
-    uint16_t* other = bufp(IC<buf ^ 1>{});
-    if (j + 1 < nkv) load_tile(j + 1, other);
-    else load_mt(other);
+    issue(j + 3, bufp(IC<b + 3>{}));
     const int kv0 = j * kBN;
-    if (kv0 <= qw0 + 31) {
-      tile_body(kt, kv0, kv0 + kBN - 1 > qw0);   // mask when some keys lie past this wave's queries
+    if constexpr (kMask) {
+      if (kv0 <= qw0 + 31) tile_body(kt, kv0, IC<1>{});   // else: every key lies past the wave's queries
+    } else {
+      tile_body(kt, kv0, IC<0>{});
     }
-    __syncthreads();   // waits for this wave's copies, then for every wave's
+    wait_vm_le(count(j + 2) + count(j + 3));
+    __builtin_amdgcn_s_barrier();
   };
-  for (int j = 0; j < nkv; j += 2) {
-    step(j, IC<0>{});
-    if (j + 1 < nkv) step(j + 1, IC<1>{});
+  // Tiles below the query tile (j < q0 / 64, a multiple of 4) need no mask; the (up to)
+  // four tiles from q0 on hold the diagonal of every wave and run the masked body.
+  const int jm = q0 / kBN;
+  for (int j = 0; j < jm; j += 4) {
+    step(j, IC<0>{}, IC<0>{});
+    step(j + 1, IC<1>{}, IC<0>{});
+    step(j + 2, IC<2>{}, IC<0>{});
+    step(j + 3, IC<3>{}, IC<0>{});
   }
+  step(jm, IC<0>{}, IC<1>{});
+  if (jm + 1 < nkv) step(jm + 1, IC<1>{}, IC<1>{});
+  if (jm + 2 < nkv) step(jm + 2, IC<2>{}, IC<1>{});
+  if (jm + 3 < nkv) step(jm + 3, IC<3>{}, IC<1>{});
+  wait_vm_le(0);   // M^T_{s-1} and z_{s-1}
+  __builtin_amdgcn_s_barrier();
 
   // ---------------------------------------------------------------- epilogue
-  // M^T_{s-1} is in buffer nkv % 2 (z_{s-1} in zsh); the output is staged in the other one
-  const uint16_t* mts = (nkv & 1) ? buf1 : buf0;
-  uint16_t* ost = ((nkv & 1) ? buf0 : buf1) + wave * 32 * D;
+  // M^T_{s-1} is in buffer nkv % 4 (z_{s-1} in zsh); the output is staged in buffers
+  // (nkv + 1) % 4 (waves 0-3) and (nkv + 2) % 4 (waves 4-7)
+  auto buf_at = [&](int i) __attribute__((always_inline)) -> uint16_t* {
+    switch (i & 3) {
+      case 0: return buf0;
+      case 1: return buf1;
+      case 2: return buf2;
+      default: return buf3;
+    }
+  };
+  const uint16_t* mts = buf_at(nkv);
+  uint16_t* ost = buf_at(nkv + 1 + (wave >> 2)) + (wave & 3) * 32 * D;
   const float l_tot = sum_across_halves(l_part);
   const float inv_l = 1.f / l_tot;
 
@@ -327,7 +434,10 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
       st8(ost + l32 * D + 8 * ((4 * db + r4) ^ swz(l32)) + 4 * hl,
           u32x2{pack_bf16x2(o[4 * r4], o[4 * r4 + 1]), pack_bf16x2(o[4 * r4 + 2], o[4 * r4 + 3])});
   }
-  __syncthreads();
+  // each wave reads back only the rows it staged
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint16_t* og = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int i = 0; i < 32 * D / 8 / 64; ++i) {
@@ -435,9 +545,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_attn_f32(const WindowArgs a) 
 template <int D>
 hipError_t launch_attention_d(const WindowArgs& a, hipStream_t st) {
   if (a.bf16) {
-    const dim3 grid(a.units() * ((a.N + kBM - 1) / kBM));
-    if (a.a_mem || a.a_dot) hipLaunchKernelGGL((k_attn_bf16<D, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_bf16<D, false>), grid, dim3(kThreads), 0, st, a);
+    const dim3 grid(a.units() * ((a.N + kBMA - 1) / kBMA));
+    if (a.a_mem || a.a_dot) hipLaunchKernelGGL((k_attn_bf16<D, true>), grid, dim3(kThreadsA), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_bf16<D, false>), grid, dim3(kThreadsA), 0, st, a);
   } else {
     const dim3 grid(a.units() * ((a.N + 63) / 64));
     hipLaunchKernelGGL((k_attn_f32<D>), grid, dim3(64 * (D / 32)), 0, st, a);
