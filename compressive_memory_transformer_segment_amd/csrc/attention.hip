@@ -216,12 +216,12 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
                    4 * (lane & 1);
   auto swz = [](int row) __attribute__((always_inline)) -> int { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
 
-  // ---- prologue: copies 0, 1, 2 of the sequence; wait for tile 0
+  // ---- prologue: copies 0, 1, 2 of the sequence; wait for tiles 0 and 1
   {
     issue(0, buf0);
-    const int c1 = issue(1, buf1);
+    issue(1, buf1);
     const int c2 = issue(2, buf2);
-    wait_vm_le(c1 + c2);
+    wait_vm_le(c2);   // tiles 0 and 1
     __builtin_amdgcn_s_barrier();
   }
 
@@ -305,20 +305,10 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc_o[db] = mfma32x32x16(av[db][jj], jj ? p_hi : p_lo, acc_o[db]);
   };
-  // One tile: S_A = K_A Q^T and S_B = K_B Q^T (keys kv0 .. and kv0 + 32 ..), the tile
-  // maximum, a rare rescale, then P_A, O += V_A P_A, P_B, O += V_B P_B.  The V^T reads of a
-  // half are issued before its exponentials, which cover their latency; the exponentials
-  // of B run under the MFMAs of A.
-  auto tile_body = [&](const uint16_t* kt, int kv0, auto maskc) __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(maskc)::value != 0;
-    f32x16 s0, s1;
-    bf16x8 p0, p1, p2, p3;
-    qk_tile(kt, s0, s1);
-    if constexpr (kMask) {
-      mask_half(s0, kv0);
-      mask_half(s1, kv0 + 32);
-    }
-    const float mxs = max_across_halves(fmaxf(half_max(s0), half_max(s1))) * c2;
+  auto tile_max = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) -> float {
+    return max_across_halves(fmaxf(half_max(s0), half_max(s1))) * c2;
+  };
+  auto maybe_rescale = [&](float mxs) __attribute__((always_inline)) {
     if (__any(mxs > m_run + kTau)) {
       const float m_use = fmaxf(m_run, mxs);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -326,6 +316,12 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       l_part *= alpha;
       m_run = m_use;
     }
+  };
+  // P_A, O += V_A P_A, P_B, O += V_B P_B for a tile whose scores are in s0 / s1.  The V^T
+  // reads of a half are issued before its exponentials, which cover their latency; the
+  // exponentials of B run under the MFMAs of A.
+  auto finish_tile = [&](const uint16_t* kt, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+    bf16x8 p0, p1, p2, p3;
     bf16x8 va[DB][2], vb[DB][2];
     v_operands(kt, 0, va);
     half_exp(s0, p0, p1);
@@ -335,36 +331,57 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     pv(vb, p2, p3);
   };
 
-  // iteration j: buffer j % 4 holds tile j; copy j + 3 of the sequence goes into buffer
-  // (j + 3) % 4, consumed in iteration j - 1.  The closing wait lets this wave's copies
-  // j + 2 and j + 3 stay in flight; after the barrier tile j + 1 is complete for every wave.
-  auto step = [&](int j, auto bufc, auto maskc) __attribute__((always_inline)) {
+  // Unmasked tiles j < jm = q0 / 64 (a multiple of 4) run software-pipelined: iteration j
+  // holds the scores of tile j (sc0 / sc1, maximum mxc) and computes those of tile j + 1
+  // while it exponentiates and multiplies tile j, so a wave's own MFMAs run under its
+  // softmax arithmetic.  Buffer j % 4 holds tile j; copy j + 3 of the sequence goes into
+  // buffer (j + 3) % 4, consumed in iteration j - 1.  The closing wait leaves only this
+  // wave's copy j + 3 in flight: after the barrier tiles j + 1 and j + 2 are complete.
+  const int jm = q0 / kBN;
+  f32x16 sc0, sc1;
+  qk_tile(buf0, sc0, sc1);   // tile 0
+  float mxc = tile_max(sc0, sc1);
+  auto pstep = [&](int j, auto bufc) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
-    constexpr bool kMask = decltype(maskc)::value != 0;
+    maybe_rescale(mxc);
+    issue(j + 3, bufp(IC<b + 3>{}));
+    f32x16 n0, n1;
+    qk_tile(bufp(IC<b + 1>{}), n0, n1);   // tile j + 1 (tile jm, masked later, at the end)
+    finish_tile(bufp(bufc), sc0, sc1);
+    mxc = tile_max(n0, n1);
+    sc0 = n0;
+    sc1 = n1;
+    wait_vm_le(count(j + 3));
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int j = 0; j < jm; j += 4) {
+    pstep(j, IC<0>{});
+    pstep(j + 1, IC<1>{});
+    pstep(j + 2, IC<2>{});
+    pstep(j + 3, IC<3>{});
+  }
+  // The (up to) four tiles from q0 on hold the diagonal of every wave: masked, one at a
+  // time; tile jm's scores are already in sc0 / sc1.  A wave skips a tile whose keys all
+  // lie past its queries.
+  auto mstep = [&](int j, auto bufc, bool have_scores) __attribute__((always_inline)) {
+    constexpr int b = decltype(bufc)::value;
     const uint16_t* kt = bufp(bufc);
     issue(j + 3, bufp(IC<b + 3>{}));
     const int kv0 = j * kBN;
-    if constexpr (kMask) {
-      if (kv0 <= qw0 + 31) tile_body(kt, kv0, IC<1>{});   // else: every key lies past the wave's queries
-    } else {
-      tile_body(kt, kv0, IC<0>{});
+    if (kv0 <= qw0 + 31) {
+      if (!have_scores) qk_tile(kt, sc0, sc1);
+      mask_half(sc0, kv0);
+      mask_half(sc1, kv0 + 32);
+      maybe_rescale(tile_max(sc0, sc1));
+      finish_tile(kt, sc0, sc1);
     }
     wait_vm_le(count(j + 2) + count(j + 3));
     __builtin_amdgcn_s_barrier();
   };
-  // Tiles below the query tile (j < q0 / 64, a multiple of 4) need no mask; the (up to)
-  // four tiles from q0 on hold the diagonal of every wave and run the masked body.
-  const int jm = q0 / kBN;
-  for (int j = 0; j < jm; j += 4) {
-    step(j, IC<0>{}, IC<0>{});
-    step(j + 1, IC<1>{}, IC<0>{});
-    step(j + 2, IC<2>{}, IC<0>{});
-    step(j + 3, IC<3>{}, IC<0>{});
-  }
-  step(jm, IC<0>{}, IC<1>{});
-  if (jm + 1 < nkv) step(jm + 1, IC<1>{}, IC<1>{});
-  if (jm + 2 < nkv) step(jm + 2, IC<2>{}, IC<1>{});
-  if (jm + 3 < nkv) step(jm + 3, IC<3>{}, IC<1>{});
+  mstep(jm, IC<0>{}, true);
+  if (jm + 1 < nkv) mstep(jm + 1, IC<1>{}, false);
+  if (jm + 2 < nkv) mstep(jm + 2, IC<2>{}, false);
+  if (jm + 3 < nkv) mstep(jm + 3, IC<3>{}, false);
   wait_vm_le(0);   // M^T_{s-1} and z_{s-1}
   __builtin_amdgcn_s_barrier();
 
