@@ -121,12 +121,60 @@ def pmc_table(path: str, counter: str) -> str:
     return "\n".join(out)
 
 
+def _per_kernel(path: str, counter: str, grid: int | None = None):
+    """Counter values (KiB) per dispatch of each kernel; optionally only dispatches whose
+    grid size (work items) is ``grid``."""
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        if grid is not None and int(r.get("Grid_Size", -1)) != grid:
+            continue
+        vals[_short(r.get("Kernel_Name", ""))].append(float(r["Counter_Value"]))
+    return vals
+
+
+def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int, algorithmic_bytes: float) -> str:
+    """Markdown summary of the attention kernel's HBM traffic from two counter passes.
+
+    Each counter is calibrated on the device copy of ``copy_mib`` MiB that bench.py runs
+    before timing (``--copy-probe-mib``): factor = known bytes / counter reading, taken
+    from the largest copy dispatch.  The attention kernel's readings are scaled by the
+    same factors."""
+    known = copy_mib * 1024.0   # KiB read and written by the copy
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    f_copy = max(fetch["__amd_rocclr_copyBuffer"])
+    w_copy = max(write["__amd_rocclr_copyBuffer"])
+    kf, kw = known / f_copy, known / w_copy
+    key = next(k for k in fetch if k.startswith("k_attn_bf16"))
+    fa = sum(fetch[key]) / len(fetch[key])
+    wa = sum(write[key]) / len(write[key])
+    total = (fa * kf + wa * kw) * 1024.0
+    lines = [
+        f"kernel: `{key}`; kernel source hash: `{kernel_source_hash()}`",
+        "",
+        "| counter | copy probe reading (KiB) | known (KiB) | factor | attention avg per dispatch (KiB) | scaled (MB) |",
+        "|---|---|---|---|---|---|",
+        f"| FETCH_SIZE | {f_copy:.1f} | {known:.0f} | {kf:.4f} | {fa:.1f} ({len(fetch[key])} dispatches) | {fa * kf * 1024 / 1e6:.1f} |",
+        f"| WRITE_SIZE | {w_copy:.1f} | {known:.0f} | {kw:.4f} | {wa:.1f} ({len(write[key])} dispatches) | {wa * kw * 1024 / 1e6:.1f} |",
+        "",
+        f"HBM bytes per launch (scaled): {total:.6e}",
+        f"Algorithmic bytes per launch: {algorithmic_bytes:.6e} (ratio {total / algorithmic_bytes:.2f})",
+    ]
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
     what = sys.argv[1]
     if what == "stats":
         print(stats_table(sys.argv[2]))
     elif what == "pmc":
         print(pmc_table(sys.argv[2], sys.argv[3]))
+    elif what == "hbm":
+        # hbm <fetch csv> <write csv> <copy MiB> : the C1-shaped attention launch
+        alg = attention_kernel_bytes(1, 8, 128, 2048, 32768)
+        print(hbm_summary(sys.argv[2], sys.argv[3], int(sys.argv[4]), alg))
     elif what == "hash":
         print(kernel_source_hash())
     else:
