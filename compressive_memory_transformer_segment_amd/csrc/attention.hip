@@ -136,15 +136,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + row0 * D;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + row0 * D;
 
-  // Q as the B operand of S^T, straight from HBM: lane holds Q[q][16 ks + 8 hl .. +7];
-  // rows >= n read as zeros.  Issued first, so the tile waits below also cover it.
-  u32x4 qreg[KS];
-  {
-    const auto qr = buffer_rsrc(qg + static_cast<int64_t>(qw0) * D,
-                                static_cast<uint32_t>(max(n - qw0, 0)) * D * 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = buffer_ld16(qr, static_cast<uint32_t>(l32 * D + 16 * ks + 8 * hl) * 2);
-  }
+  u32x4 qreg[KS];   // Q as the B operand of S^T: lane holds Q[q][16 ks + 8 hl .. +7]
 
   // source byte offsets of this lane's 16 bytes within a copy:
   //   row groups, copy c = (CPR / 4) g + j: row 16 g + lane % 16, chunk 4 j + lane / 16
@@ -216,13 +208,24 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
                    4 * (lane & 1);
   auto swz = [](int row) __attribute__((always_inline)) -> int { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
 
-  // ---- prologue: copies 0, 1, 2 of the sequence; wait for tiles 0 and 1
+  // ---- prologue.  Every wave copies its own 32 rows of Q (row-group layout, rows >= n
+  // as zeros) into buffer 2 (waves 0-3) or 3 (waves 4-7) and reads them into registers
+  // itself; tiles 0 and 1 go into buffers 0 and 1.  Copy 2 of the sequence is issued once
+  // every wave is done with its Q rows.
   {
-    issue(0, buf0);
-    issue(1, buf1);
-    const int c2 = issue(2, buf2);
-    wait_vm_le(c2);   // tiles 0 and 1
+    uint16_t* qs = (wave < 4 ? buf2 : buf3) + (wave & 3) * 32 * D;
+    const uint16_t* qsrc = qg + static_cast<int64_t>(qw0) * D;
+    const uint32_t qbytes = static_cast<uint32_t>(max(n - qw0, 0)) * D * 2;
+#pragma unroll
+    for (int c = 0; c < CPR / 2; ++c) copy_group(c, qsrc, qbytes, qs);
+    const int c0 = issue(0, buf0);
+    const int c1 = issue(1, buf1);
+    wait_vm_le(c0 + c1);   // this wave's Q rows
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = ld16(qs + g_rd + 256 * ks);
+    wait_vm_le(0);   // tiles 0 and 1; Q read
     __builtin_amdgcn_s_barrier();
+    issue(2, buf2);
   }
 
   const float c2 = a.scale_log2;
