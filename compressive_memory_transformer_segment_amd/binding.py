@@ -216,10 +216,12 @@ class InfiniAttention:
         return M, z
 
     def set_state(self, M, z, stream=None) -> None:
-        M = M.to(device="cuda", dtype=torch.float32).contiguous()
-        z = z.to(device="cuda", dtype=torch.float32).contiguous()
+        """Either part may be None (that part keeps its value)."""
+        M = None if M is None else M.to(device="cuda", dtype=torch.float32).contiguous()
+        z = None if z is None else z.to(device="cuda", dtype=torch.float32).contiguous()
         _check("infini_attn_set_state",
-               self._lib.infini_attn_set_state(self._h, _ptr(M), _ptr(z), _stream_ptr(stream)))
+               self._lib.infini_attn_set_state(self._h, _ptr(M) if M is not None else None,
+                                               _ptr(z) if z is not None else None, _stream_ptr(stream)))
 
     def set_beta(self, beta) -> None:
         _check("infini_attn_set_beta", self._lib.infini_attn_set_beta(self._h, _float_array(beta)))

@@ -30,6 +30,7 @@ struct infini_attn {
   float* M;            // [B,H,D,D]
   float* z;            // [B,H,D], stored right after M
   float* gate;         // [2H]: sigmoid(beta), 1 - sigmoid(beta)
+  bool state_zero = false;   // M, z are logically zero: reset_state ran, memory not yet written
   void* ws_base;
   size_t ws_bytes;
   infini::Workspace ws;
@@ -252,6 +253,7 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   a.M = h->M;
   a.z = h->z;
   a.ws = h->ws;
+  a.zero_state = h->state_zero;
   for (int s0 = 0; s0 < a.S; s0 += h->window) {
     a.s0 = s0;
     a.W = std::min(h->window, a.S - s0);
@@ -261,6 +263,10 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
     if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
     if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
     if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+    if (e == hipSuccess) {   // the chain has written the carried state
+      h->state_zero = false;
+      a.zero_state = false;
+    }
     if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(a, st); });
     if (e != hipSuccess) return INFINI_ERR_HIP;
   }
@@ -392,11 +398,21 @@ INFINI_EXPORT int infini_attn_forward_segment(infini_attn_t h, const void* q, co
 
 INFINI_EXPORT int infini_attn_reset_state(infini_attn_t h, void* hip_stream) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
-  DeviceGuard dg(h->device);
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  (void)hip_stream;
+  // No device work: the next call that reads the state treats it as zero (the chain and
+  // the state pass of its first window read 0 instead of M and z); get_state and
+  // set_state write the zeros out first.
+  h->state_zero = true;
+  return INFINI_OK;
+}
+
+// Writes the zeros of a reset into M and z (stream-ordered), if still pending.
+static hipError_t materialize_zero_state(infini_attn* h, hipStream_t st) {
+  if (!h->state_zero) return hipSuccess;
   const int64_t DD = int64_t(h->D) * h->D;
   const hipError_t e = zero_f32(h->M, int64_t(h->BH) * (DD + h->D), st);   // M and z
-  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+  if (e == hipSuccess) h->state_zero = false;
+  return e;
 }
 
 INFINI_EXPORT int infini_attn_get_state(infini_attn_t h, float* M, float* z, void* hip_stream) {
@@ -404,8 +420,8 @@ INFINI_EXPORT int infini_attn_get_state(infini_attn_t h, float* M, float* z, voi
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const size_t DD = size_t(h->D) * h->D;
-  hipError_t e = hipSuccess;
-  if (M) e = hipMemcpyAsync(M, h->M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
+  hipError_t e = materialize_zero_state(h, st);
+  if (e == hipSuccess && M) e = hipMemcpyAsync(M, h->M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
   if (e == hipSuccess && z) e = hipMemcpyAsync(z, h->z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
@@ -416,8 +432,8 @@ INFINI_EXPORT int infini_attn_set_state(infini_attn_t h, const float* M, const f
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const size_t DD = size_t(h->D) * h->D;
-  hipError_t e = hipSuccess;
-  if (M) e = hipMemcpyAsync(h->M, M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
+  hipError_t e = materialize_zero_state(h, st);   // a part not given keeps its (zero) value
+  if (e == hipSuccess && M) e = hipMemcpyAsync(h->M, M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
   if (e == hipSuccess && z) e = hipMemcpyAsync(h->z, z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;

@@ -36,9 +36,9 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
 
   float m[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) m[e] = a.M[bh * DD + static_cast<int64_t>(i0 + e) * D + dv];
+  for (int e = 0; e < EPT; ++e) m[e] = a.zero_state ? 0.f : a.M[bh * DD + static_cast<int64_t>(i0 + e) * D + dv];
   const bool zown = rb == 0 && tid < D;
-  float z = zown ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
+  float z = zown && !a.zero_state ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
 
   for (int s0 = 0; s0 < a.W; s0 += kBatch) {
     // all chunk partials of the batch are independent of the chain: issue them together
@@ -125,9 +125,9 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
 
   float m[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) m[e] = a.M[bh * DD + static_cast<int64_t>(cg + CG * e) * D + dv];
+  for (int e = 0; e < EPT; ++e) m[e] = a.zero_state ? 0.f : a.M[bh * DD + static_cast<int64_t>(cg + CG * e) * D + dv];
   const bool zown = rb == 0 && tid < D;
-  float z = zown ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
+  float z = zown && !a.zero_state ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
 
   for (int s = 0; s < a.W; ++s) {
     const int64_t u = static_cast<int64_t>(s) * BH + bh;

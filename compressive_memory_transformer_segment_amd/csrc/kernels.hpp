@@ -34,6 +34,7 @@ struct WindowArgs {
   int ch;            // tokens per chunk (multiple of 64)
   bool delta;
   bool bf16;
+  bool zero_state;   // the carried M, z are zero (after a reset): read as 0, not from memory
   float eps;
   float scale_log2;  // softmax scale * log2(e)
   float scale;       // softmax scale

@@ -54,7 +54,7 @@ template <int D>
 __device__ void z_before(const WindowArgs& a, const UnitPos& p, float* zs) {
   const int BH = a.B * a.H;
   for (int d = threadIdx.x; d < D; d += kThreads) {
-    float z = a.z[static_cast<int64_t>(p.bh) * D + d];
+    float z = a.zero_state ? 0.f : a.z[static_cast<int64_t>(p.bh) * D + d];
     for (int s = 0; s < p.s_local; ++s) {
       float dz = 0.f;
       for (int c = 0; c < a.chk; ++c) dz += a.ws.dz[((static_cast<int64_t>(s) * BH + p.bh) * a.chk + c) * D + d];

@@ -100,7 +100,10 @@ int infini_attn_forward_stream_ex(infini_attn_t h, const void* q, const void* k,
                                   void* out, float* a_mem, float* a_dot, int64_t n_tokens,
                                   void* hip_stream);
 
-/* M = 0, z = 0 (stream-ordered). */
+/* M = 0, z = 0: the memory before the first segment of a new stream (Eq. 4 with an
+ * empty history).  Takes effect for every later call on the handle; enqueues no device
+ * work (the next forward reads the state as zero; get_state / set_state write the zeros
+ * out first on their stream).  hip_stream is accepted for symmetry and not used. */
 int infini_attn_reset_state(infini_attn_t h, void* hip_stream);
 
 /* Copy the state out / in.  M: [B,H,d,d] float32, z: [B,H,d] float32, device or host

@@ -167,6 +167,34 @@ def test_state_save_restore_is_bit_identical(update):
     assert torch.equal(Ma, Mb) and torch.equal(za, zb)
 
 
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_reset_between_streams(update):
+    """reset_state enqueues nothing: the next forward must read the state as zero (it
+    equals a fresh handle), and a partial set_state after a reset keeps the other part 0."""
+    gu.require_gpu()
+    w = wl.Workload(f"reset-{update}", 1, 2, 128, 256, 3 * 256 + 40, "bf16", update, seed=13)
+    gu.note(f"[parity] reset between streams {update}")
+    Q, K, V = wl.stream_inputs(w)
+    beta = wl.beta_for(w)
+    dev = [gu.to_dev(x, "bf16") for x in (Q, K, V)]
+    with binding.InfiniAttention(1, 2, 128, 256, update=update, beta=beta) as fresh:
+        out_f = fresh.forward_stream(*dev)
+        Mf, zf = fresh.get_state()
+    with binding.InfiniAttention(1, 2, 128, 256, update=update, beta=beta) as layer:
+        layer.forward_stream(*dev)
+        layer.forward_stream(*dev)
+        layer.reset_state()
+        out_r = layer.forward_stream(*dev)
+        Mr, zr = layer.get_state()
+        layer.reset_state()
+        layer.set_state(torch.ones_like(Mr), None)
+        M1, z1 = layer.get_state()
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_r)
+    assert torch.equal(Mf, Mr) and torch.equal(zf, zr)
+    assert torch.all(M1 == 1) and torch.count_nonzero(z1) == 0
+
+
 def test_nonzero_initial_state_and_literal_scale():
     """set_state with an arbitrary start, and the page's literal 1/sqrt(d_model) scale."""
     gu.require_gpu()
