@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
     float acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+#pragma unroll 2
     for (int k = 0; k < D; k += 4) {
       const f32x4 mk = *reinterpret_cast<const f32x4*>(&m_lds[r][k]);
 #pragma unroll
