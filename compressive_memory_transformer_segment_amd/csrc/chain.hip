@@ -105,13 +105,17 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
 
 // Delta rule: each step needs the workgroup's rows of M^T in full and all of G_s.
 // Thread (r, cg) owns row rb + r and columns cg + CG*e (strided, so that lanes read
-// consecutive rows of G in LDS).
-template <int D, int EPT, bool BF16>
+// consecutive rows of G in LDS).  All loads of a step that do not depend on the chain (the
+// U^T, dz and G partials) are issued in batches before they are used.
+template <int D, int EPT, int CHK, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
   constexpr int CG = D / EPT;
   constexpr int RB = kThreads / CG;
   constexpr int GP = D + 4;               // LDS row pitch of G (floats)
   constexpr int MP = D + 4;               // LDS row pitch of the M^T rows
+  constexpr int IT = D * D / 4 / kThreads;   // float4 elements of G per thread
+  constexpr int NB4 = CHK >= 8 ? 2 : 4;      // float4 elements per load batch
+  static_assert(IT % NB4 == 0, "whole batches");
   __shared__ __align__(16) float g_lds[D][GP];
   __shared__ __align__(16) float m_lds[RB][MP];
 
@@ -132,6 +136,15 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
   for (int s = 0; s < a.W; ++s) {
     const int64_t u = static_cast<int64_t>(s) * BH + bh;
     const int64_t off = u * DD + static_cast<int64_t>(dv) * D;
+    // this step's U^T and dz partials
+    float up[EPT][CHK];
+#pragma unroll
+    for (int c = 0; c < CHK; ++c)
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) up[e][c] = a.ws.u[(u * CHK + c) * DD + static_cast<int64_t>(dv) * D + cg + CG * e];
+    float dzp[CHK];
+#pragma unroll
+    for (int c = 0; c < CHK; ++c) dzp[c] = zown ? a.ws.dz[(u * CHK + c) * D + tid] : 0.f;
     // record the state this segment reads
     if constexpr (BF16) {
       uint16_t* mt = static_cast<uint16_t*>(a.ws.mt) + off;
@@ -145,16 +158,31 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
     if (zown) {
       a.ws.zb[u * D + tid] = z;
       float dz = 0.f;
-      for (int c = 0; c < a.chk; ++c) dz += a.ws.dz[(u * a.chk + c) * D + tid];
+#pragma unroll
+      for (int c = 0; c < CHK; ++c) dz += dzp[c];
       z += dz;
     }
-    // stage G_s (sum of the chunk partials) and the rows of M^T
-    for (int e4 = tid; e4 < D * D / 4; e4 += kThreads) {
-      const int row = (e4 * 4) / D, col = (e4 * 4) % D;
-      f32x4 gs = *reinterpret_cast<const f32x4*>(a.ws.g + u * a.chk * DD + row * D + col);
-      for (int c = 1; c < a.chk; ++c)
-        gs += *reinterpret_cast<const f32x4*>(a.ws.g + (u * a.chk + c) * DD + row * D + col);
-      *reinterpret_cast<f32x4*>(&g_lds[row][col]) = gs;
+    // stage G_s (sum of the chunk partials, in chunk order) and the rows of M^T
+#pragma unroll
+    for (int b = 0; b < IT; b += NB4) {
+      f32x4 gp[NB4][CHK];
+#pragma unroll
+      for (int i = 0; i < NB4; ++i) {
+        const int e4 = tid + (b + i) * kThreads;
+        const int row = (e4 * 4) / D, col = (e4 * 4) % D;
+#pragma unroll
+        for (int c = 0; c < CHK; ++c)
+          gp[i][c] = *reinterpret_cast<const f32x4*>(a.ws.g + (u * CHK + c) * DD + row * D + col);
+      }
+#pragma unroll
+      for (int i = 0; i < NB4; ++i) {
+        const int e4 = tid + (b + i) * kThreads;
+        const int row = (e4 * 4) / D, col = (e4 * 4) % D;
+        f32x4 gs = gp[i][0];
+#pragma unroll
+        for (int c = 1; c < CHK; ++c) gs += gp[i][c];
+        *reinterpret_cast<f32x4*>(&g_lds[row][col]) = gs;
+      }
     }
 #pragma unroll
     for (int e = 0; e < EPT; ++e) m_lds[r][cg + CG * e] = m[e];
@@ -175,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       float ut = 0.f;
-      for (int c = 0; c < a.chk; ++c) ut += a.ws.u[(u * a.chk + c) * DD + static_cast<int64_t>(dv) * D + cg + CG * e];
+#pragma unroll
+      for (int c = 0; c < CHK; ++c) ut += up[e][c];
       m[e] = (m[e] - acc[e]) + ut;
     }
     __syncthreads();
@@ -191,8 +220,11 @@ hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
   if (a.delta) {
     constexpr int EPT = 16 * D / kThreads;        // 16 rows of M^T per workgroup
     const dim3 grid(BH * (D / 16));
-    if (a.bf16) hipLaunchKernelGGL((k_chain_delta<D, EPT, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_chain_delta<D, EPT, false>), grid, dim3(kThreads), 0, st, a);
+    if (!a.bf16) hipLaunchKernelGGL((k_chain_delta<D, EPT, 1, false>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_delta<D, EPT, 1, true>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_delta<D, EPT, 2, true>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_delta<D, EPT, 4, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_chain_delta<D, EPT, 8, true>), grid, dim3(kThreads), 0, st, a);
   } else {
     constexpr int EPT = 2;
     constexpr int RB = kThreads / (D / EPT);
