@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--local-qk", action="store_true",
+                    help="separate (position-embedded) Q/K for the local attention: forward_stream_local")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -124,9 +126,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.local_qk:   # distinct buffers; the values do not change the kernels' work
+        Ql, Kl = Q.clone(), K.clone()
+
     def step():
         layer.reset_state(stream)
-        layer.forward_stream(Q, K, V, out=out, stream=stream)
+        if args.local_qk:
+            layer.forward_stream_local(Q, K, V, Ql, Kl, out=out, stream=stream)
+        else:
+            layer.forward_stream(Q, K, V, out=out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -178,7 +186,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "segment_len": w.segment_len, "n_tokens": w.n_tokens, "update": w.update,
-                   "parallelism": "none"},
+                   "local_qk": bool(args.local_qk), "parallelism": "none"},
         "pct_bf16_peak": 100.0 * flops_step / (ms / 1e3) / profiling.PEAK_BF16_FLOPS,
         "roofline": {
             "kernel": "k_attn_bf16 (local attention + retrieval + gate)",

@@ -79,6 +79,7 @@ def load() -> ctypes.CDLL:
         "infini_attn_forward_segment": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, vp]),
         "infini_attn_forward_stream": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_forward_stream_ex": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "infini_attn_forward_stream_local": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_reset_state": (ctypes.c_int, [vp, vp]),
         "infini_attn_get_state": (ctypes.c_int, [vp, vp, vp, vp]),
         "infini_attn_set_state": (ctypes.c_int, [vp, vp, vp, vp]),
@@ -193,6 +194,17 @@ class InfiniAttention:
             st = self._lib.infini_attn_forward_stream_ex(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                                          _ptr(a_mem), _ptr(a_dot), n, _stream_ptr(stream))
             _check("infini_attn_forward_stream_ex", st)
+        return out
+
+    def forward_stream_local(self, q, k, v, q_local=None, k_local=None, out=None, stream=None):
+        """Local attention on q_local / k_local (e.g. position-embedded), retrieval and
+        memory update on the PE-free q / k.  None means "same as q / k"."""
+        self._check_io(q, k, v, q_local, k_local, out)
+        out = self._out_like(q, out)
+        st = self._lib.infini_attn_forward_stream_local(
+            self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_local) if q_local is not None else None,
+            _ptr(k_local) if k_local is not None else None, _ptr(out), q.shape[2], _stream_ptr(stream))
+        _check("infini_attn_forward_stream_local", st)
         return out
 
     def forward_segment(self, q, k, v, out=None, stream=None):

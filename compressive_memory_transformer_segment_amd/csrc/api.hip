@@ -212,9 +212,14 @@ hipError_t timed(infini_attn* h, int kind, hipStream_t st, F&& launch) {
 }
 
 int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void* out, float* a_mem,
-               float* a_dot, int64_t n_tokens, void* hip_stream) {
+               float* a_dot, int64_t n_tokens, void* hip_stream, const void* q_loc = nullptr,
+               const void* k_loc = nullptr) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   int rc = check_io(h, q, k, v, out, n_tokens);
+  if (rc) return rc;
+  if (!q_loc) q_loc = q;
+  if (!k_loc) k_loc = k;
+  rc = check_io(h, q_loc, k_loc, v, out, n_tokens);
   if (rc) return rc;
   const size_t part_bytes_out = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * 4;
   for (const float* p : {a_mem, a_dot}) {
@@ -233,6 +238,8 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   a.q = q;
   a.k = k;
   a.v = v;
+  a.q_loc = q_loc;
+  a.k_loc = k_loc;
   a.out = out;
   a.a_mem = a_mem;
   a.a_dot = a_dot;
@@ -387,6 +394,12 @@ INFINI_EXPORT int infini_attn_forward_stream_ex(infini_attn_t h, const void* q, 
                                                 void* out, float* a_mem, float* a_dot, int64_t n_tokens,
                                                 void* hip_stream) {
   return run_stream(h, q, k, v, out, a_mem, a_dot, n_tokens, hip_stream);
+}
+
+INFINI_EXPORT int infini_attn_forward_stream_local(infini_attn_t h, const void* q, const void* k,
+                                                   const void* v, const void* q_local, const void* k_local,
+                                                   void* out, int64_t n_tokens, void* hip_stream) {
+  return run_stream(h, q, k, v, out, nullptr, nullptr, n_tokens, hip_stream, q_local, k_local);
 }
 
 INFINI_EXPORT int infini_attn_forward_segment(infini_attn_t h, const void* q, const void* k, const void* v,

@@ -132,8 +132,9 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   const int qw0 = q0 + 32 * wave;
   const int q = qw0 + l32;
 
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + row0 * D;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + row0 * D;
+  // Q and K of the local attention (position-embedded when the caller supplies them)
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q_loc) + row0 * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k_loc) + row0 * D;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + row0 * D;
 
   u32x4 qreg[KS];   // Q as the B operand of S^T: lane holds Q[q][16 ks + 8 hl .. +7]
@@ -404,6 +405,20 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   const float l_tot = sum_across_halves(l_part);
   const float inv_l = 1.f / l_tot;
 
+  // With a separate local Q the retrieval needs the PE-free Q rows: each wave copies its
+  // own 32 rows into its (not yet used) staging region and reads them back, as in the
+  // prologue.
+  if (a.q_loc != a.q) {
+    const uint16_t* qm = static_cast<const uint16_t*>(a.q) + (row0 + qw0) * D;
+    const uint32_t qbytes = static_cast<uint32_t>(max(n - qw0, 0)) * D * 2;
+#pragma unroll
+    for (int c = 0; c < CPR / 2; ++c) copy_group(c, qm, qbytes, ost);
+    wait_vm_le(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = ld16(ost + g_rd + 256 * ks);
+    wait_vm_le(0);   // the reads are done before the region is reused for the output
+  }
+
   // sigma(Q) as the B operand of the retrieval, and the denominator sigma(q) . z_{s-1}
   float den = 0.f;
   bf16x8 sq[KS];
@@ -492,8 +507,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_attn_f32(const WindowArgs a) 
   const int qi = tid / TPR, part = tid % TPR;
   const int q = q0 + qi;
   const int d0 = part * 32;
-  const float* qg = static_cast<const float*>(a.q);
-  const float* kg = static_cast<const float*>(a.k);
+  const float* qg = static_cast<const float*>(a.q_loc);   // local attention's Q and K
+  const float* kg = static_cast<const float*>(a.k_loc);
   const float* vg = static_cast<const float*>(a.v);
 
   float qv[32], o[32];
@@ -534,6 +549,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_attn_f32(const WindowArgs a) 
   // retrieval: sigma(q) M_{s-1} / (sigma(q) z_{s-1} + eps), M^T stored [d_value][d_key]
   const float* mt = static_cast<const float*>(a.ws.mt) + static_cast<int64_t>(u) * D * D;
   const float* zb = a.ws.zb + static_cast<int64_t>(u) * D;
+  if (a.q_loc != a.q) {   // the retrieval reads the PE-free Q
+    const float* qm = static_cast<const float*>(a.q);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qv[i] = (q < n) ? qm[(row0 + q) * D + d0 + i] : 0.f;
+  }
   float den = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {

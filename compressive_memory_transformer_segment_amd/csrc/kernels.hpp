@@ -17,9 +17,11 @@ struct Workspace {
 };
 
 struct WindowArgs {
-  const void* q;
-  const void* k;
+  const void* q;      // PE-free Q: retrieval (sigma(Q))
+  const void* k;      // PE-free K: memory update
   const void* v;
+  const void* q_loc;  // Q and K of the local softmax attention (position-embedded, or q / k)
+  const void* k_loc;
   void* out;
   float* a_mem;      // optional fp32 [B,H,T,D]
   float* a_dot;      // optional fp32 [B,H,T,D]

@@ -100,6 +100,17 @@ int infini_attn_forward_stream_ex(infini_attn_t h, const void* q, const void* k,
                                   void* out, float* a_mem, float* a_dot, int64_t n_tokens,
                                   void* hip_stream);
 
+/* forward_stream with separate Q and K for the local softmax attention (Eq. 6), e.g.
+ * position-embedded ones: the summary page's training notes apply position embeddings to
+ * the local arm's Q and K only, after the memory has been read and updated ("Compressive
+ * Memory" and "Training Infrastructure for Recurrent Attention" subsections).  q and k
+ * (PE-free) feed the retrieval (Eq. 7) and the memory update (Eq. 8-9); q_local and k_local
+ * feed Eq. 6.  Same layout, element type and alignment as q; NULL means "same as q / k".
+ * They must not overlap out.  Everything else as forward_stream. */
+int infini_attn_forward_stream_local(infini_attn_t h, const void* q, const void* k, const void* v,
+                                     const void* q_local, const void* k_local, void* out,
+                                     int64_t n_tokens, void* hip_stream);
+
 /* M = 0, z = 0: the memory before the first segment of a new stream (Eq. 4 with an
  * empty history).  Takes effect for every later call on the handle; enqueues no device
  * work (the next forward reads the state as zero; get_state / set_state write the zeros

@@ -147,14 +147,18 @@ def gate(a_mem, a_dot, beta):
     return g * np.asarray(a_mem, dtype=np.float64) + (1.0 - g) * np.asarray(a_dot, dtype=np.float64)
 
 
-def segment_forward(q, k, v, M, z, beta, update, eps, scale):
+def segment_forward(q, k, v, M, z, beta, update, eps, scale, q_local=None, k_local=None):
     """Eq. 4 for one head and one segment: returns (A, M_s, z_s, A_mem, A_dot).
 
     Order as the page states it: read the memory with the previous state, compute the
-    local attention, gate the two, then write the memory.
+    local attention, gate the two, then write the memory.  ``q_local`` / ``k_local``
+    (default: q / k) are the query and key of the local attention only, e.g. with
+    position embeddings, which the page's training notes apply to the local arm after
+    the memory read and update; the memory always uses the PE-free q / k.
     """
     a_mem = memory_retrieval(q, M, z, eps)
-    a_dot = local_causal_attention(q, k, v, scale)
+    a_dot = local_causal_attention(q if q_local is None else q_local,
+                                   k if k_local is None else k_local, v, scale)
     a = gate(a_mem, a_dot, beta)
     if update == LINEAR:
         M_new, z_new = memory_update_linear(k, v, M, z)
@@ -182,10 +186,12 @@ def state_numbers_per_layer(heads, d_key, d_value):
 
 
 def forward(Q, K, V, beta, segment_len, update=LINEAR, eps=1e-6, scale=None,
-            M0=None, z0=None, return_parts=False):
+            M0=None, z0=None, return_parts=False, Q_local=None, K_local=None):
     """The layer over a whole stream.
 
     Q, K, V: [B, H, L, d] (any real dtype; upcast to float64).  beta: [H].
+    Q_local, K_local: optional [B, H, L, d] query / key of the local attention (see
+    ``segment_forward``); the memory path uses Q and K.
     M0: [B, H, d, d] and z0: [B, H, d] initial state (zeros when None).
     Returns (O [B,H,L,d], M [B,H,d,d], z [B,H,d]) and, with ``return_parts``, also
     A_mem and A_dot [B,H,L,d].  Each (b, h) is an independent chain (section
@@ -194,6 +200,8 @@ def forward(Q, K, V, beta, segment_len, update=LINEAR, eps=1e-6, scale=None,
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
+    Ql = None if Q_local is None else np.asarray(Q_local, dtype=np.float64)
+    Kl = None if K_local is None else np.asarray(K_local, dtype=np.float64)
     B, H, L, d = Q.shape
     dv = V.shape[-1]
     if scale is None:
@@ -211,7 +219,8 @@ def forward(Q, K, V, beta, segment_len, update=LINEAR, eps=1e-6, scale=None,
             for lo, hi in bounds:
                 a, Mbh, zbh, am, ad = segment_forward(
                     Q[b, h, lo:hi], K[b, h, lo:hi], V[b, h, lo:hi], Mbh, zbh,
-                    beta[h], update, eps, scale)
+                    beta[h], update, eps, scale,
+                    None if Ql is None else Ql[b, h, lo:hi], None if Kl is None else Kl[b, h, lo:hi])
                 O[b, h, lo:hi] = a
                 if return_parts:
                     A_mem[b, h, lo:hi] = am

@@ -11,7 +11,8 @@ from compressive_memory_transformer_segment_amd import binding
 
 EXPECTED = {
     "infini_attn_create", "infini_attn_forward_segment", "infini_attn_forward_stream",
-    "infini_attn_forward_stream_ex", "infini_attn_reset_state", "infini_attn_get_state",
+    "infini_attn_forward_stream_ex", "infini_attn_forward_stream_local", "infini_attn_reset_state",
+    "infini_attn_get_state",
     "infini_attn_set_state", "infini_attn_set_beta", "infini_attn_device_bytes",
     "infini_attn_window_tokens", "infini_attn_destroy", "infini_attn_status_string",
     "infini_attn_profile_enable", "infini_attn_profile_read",
@@ -79,6 +80,7 @@ def test_calls_on_a_missing_handle_fail_cleanly(lib):
         assert lib.infini_attn_forward_stream(h, p, p, p, p, 16, None) == -1
         assert lib.infini_attn_forward_segment(h, p, p, p, p, 16, None) == -1
         assert lib.infini_attn_forward_stream_ex(h, p, p, p, p, None, None, 16, None) == -1
+        assert lib.infini_attn_forward_stream_local(h, p, p, p, None, None, p, 16, None) == -1
         assert lib.infini_attn_reset_state(h, None) == -1
         assert lib.infini_attn_get_state(h, p, p, None) == -1
         assert lib.infini_attn_set_state(h, p, p, None) == -1

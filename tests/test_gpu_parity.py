@@ -10,6 +10,7 @@ from compressive_memory_transformer_segment_amd import binding
 from compressive_memory_transformer_segment_amd import workloads as wl
 from oracle import infini_oracle as orc
 from tests import gpu_util as gu
+from tests.rope import rope
 
 pytestmark = pytest.mark.gpu
 
@@ -214,3 +215,32 @@ def test_nonzero_initial_state_and_literal_scale():
     O_ref, M_ref, z_ref = orc.forward(Q, K, V, beta, N, "delta", eps=w.eps, scale=scale, M0=M0, z0=z0)
     gu.check_output(out.float().cpu().numpy(), O_ref, gu.BF16_TOL)
     gu.check_state(M.cpu().numpy(), z.cpu().numpy(), M_ref, z_ref, gu.BF16_TOL)
+
+
+@pytest.mark.parametrize("B,H,d,N,L,io,update", [
+    (1, 3, 128, 256, 3 * 256 + 77, "bf16", "linear"),
+    (2, 2, 128, 512, 2 * 512 + 300, "bf16", "delta"),
+    (1, 2, 64, 192, 2 * 192 + 1, "bf16", "linear"),
+    (1, 2, 128, 96, 3 * 96 + 5, "f32", "delta"),
+])
+def test_separate_local_qk_matches_oracle(B, H, d, N, L, io, update):
+    """Position-embedded Q/K for the local attention only (RoPE applied by the caller),
+    PE-free Q/K for the memory: forward_stream_local against the oracle."""
+    gu.require_gpu()
+    w = wl.Workload(f"local-qk-{io}-{update}-d{d}", B, H, d, N, L, io, update, seed=14)
+    gu.note(f"[parity] local Q/K {w.name}")
+    Q, K, V = wl.stream_inputs(w)
+    beta = wl.beta_for(w)
+    Ql, Kl = rope(Q), rope(K)
+    if io == "bf16":
+        Ql, Kl = wl.round_to_bf16(Ql), wl.round_to_bf16(Kl)
+    else:
+        Ql, Kl = Ql.astype(np.float32), Kl.astype(np.float32)
+    dev = [gu.to_dev(x, io) for x in (Q, K, V, Ql, Kl)]
+    with binding.InfiniAttention(B, H, d, N, update=update, io_dtype=io, eps=w.eps, beta=beta) as layer:
+        out = layer.forward_stream_local(*dev)
+        M, z = layer.get_state()
+    O_ref, M_ref, z_ref = orc.forward(Q, K, V, beta, N, update, eps=w.eps, Q_local=Ql, K_local=Kl)
+    tol = gu.tol_for(io)
+    gu.check_output(out.float().cpu().numpy(), O_ref, tol)
+    gu.check_state(M.cpu().numpy(), z.cpu().numpy(), M_ref, z_ref, tol)

@@ -68,6 +68,16 @@ def _gate_swapped(a_mem, a_dot, beta):
     return g * np.asarray(a_dot) + (1.0 - g) * np.asarray(a_mem)
 
 
+def _segment_ignores_local_qk(q, k, v, M, z, beta, update, eps, scale, q_local=None, k_local=None):
+    return orc.__dict__["_orig_segment_forward"](q, k, v, M, z, beta, update, eps, scale)
+
+
+def _segment_local_qk_in_memory(q, k, v, M, z, beta, update, eps, scale, q_local=None, k_local=None):
+    ql = q if q_local is None else q_local
+    kl = k if k_local is None else k_local
+    return orc.__dict__["_orig_segment_forward"](ql, kl, v, M, z, beta, update, eps, scale)
+
+
 def _elu_without_one(x):
     x = np.asarray(x, dtype=np.float64)
     return np.where(x > 0, x, np.expm1(np.minimum(x, 0.0)))
@@ -85,6 +95,8 @@ MUTANTS = {
     "attention-unscaled": ("local_causal_attention", _attention_unscaled),
     "gate-swapped": ("gate", _gate_swapped),
     "elu-without-plus-one": ("elu_plus_one", _elu_without_one),
+    "local-qk-ignored": ("segment_forward", _segment_ignores_local_qk),
+    "local-qk-fed-to-memory": ("segment_forward", _segment_local_qk_in_memory),
 }
 
 
@@ -103,12 +115,16 @@ def _all_pins(rng):
     yield lambda: pins.test_delta_equals_linear_on_first_segment_and_z_is_shared(rng)
     yield lambda: pins.test_delta_step_affine_form(rng)
     yield lambda: pins.test_delta_step_brute_force(rng)
+    yield lambda: pins.test_local_qk_with_gate_off_is_causal_sdpa_of_the_local_inputs(rng)
+    for u in ("linear", "delta"):
+        yield lambda u=u: pins.test_local_qk_leave_the_memory_path_unchanged(rng, u)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_a_planted_mistake_fails_a_pin(monkeypatch, name):
     attr, fn = MUTANTS[name]
     monkeypatch.setitem(orc.__dict__, "_orig_attention", orc.local_causal_attention)
+    monkeypatch.setitem(orc.__dict__, "_orig_segment_forward", orc.segment_forward)
     monkeypatch.setattr(orc, attr, fn)
     rng = np.random.default_rng(99)
     caught = []

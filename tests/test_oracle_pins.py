@@ -298,3 +298,53 @@ def test_page_figures():
     full = [b for b in bounds if b[1] - b[0] == bk["segment_len"]]
     assert len(full) == bk["full_segments"]
     assert (bounds[-1][1] - bounds[-1][0] < bk["segment_len"]) == bk["final_segment_shorter"]
+
+
+# ---------------------------------------------------------------- separate local Q/K
+# The summary page's training notes apply position embeddings to the local arm's Q and K
+# only, after the memory read and update ("Compressive Memory" / "Training Infrastructure"
+# subsections); the oracle takes those as optional inputs.
+
+def _pe_inputs(rng, B=1, H=2, L=70, d=16):
+    from tests.rope import rope
+    Q, K, V = (rng.standard_normal((B, H, L, d)) / math.sqrt(d) for _ in range(3))
+    return Q, K, V, rope(Q), rope(K)
+
+
+def test_local_qk_with_gate_off_is_causal_sdpa_of_the_local_inputs(rng):
+    Q, K, V, Ql, Kl = _pe_inputs(rng)
+    N = 32
+    O, _, _ = orc.forward(Q, K, V, np.full(2, -np.inf), N, "linear", Q_local=Ql, K_local=Kl)
+    for lo in range(0, Q.shape[2], N):
+        hi = min(lo + N, Q.shape[2])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Ql[..., lo:hi, :]), torch.from_numpy(Kl[..., lo:hi, :]),
+            torch.from_numpy(V[..., lo:hi, :]), is_causal=True, scale=1.0 / math.sqrt(Q.shape[-1])).numpy()
+        np.testing.assert_allclose(O[..., lo:hi, :], ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_local_qk_leave_the_memory_path_unchanged(rng, update):
+    Q, K, V, Ql, Kl = _pe_inputs(rng)
+    beta = rng.standard_normal(2)
+    base = orc.forward(Q, K, V, beta, 24, update, return_parts=True)
+    pe = orc.forward(Q, K, V, beta, 24, update, return_parts=True, Q_local=Ql, K_local=Kl)
+    for i in (1, 2, 3):   # M, z and A_mem do not see the local inputs
+        assert np.array_equal(base[i], pe[i])
+    assert not np.allclose(base[4], pe[4])   # A_dot does
+    same = orc.forward(Q, K, V, beta, 24, update, return_parts=True, Q_local=Q, K_local=K)
+    for x, y in zip(base, same):
+        assert np.array_equal(x, y)
+
+
+def test_rope_is_a_rotation_and_shifts_scores_by_relative_position(rng):
+    """Pins the test helper itself: norms are kept, and q.k after RoPE depends only on the
+    position difference."""
+    from tests.rope import rope
+    d = 8
+    q, k = rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    for p in (0, 3, 11):
+        np.testing.assert_allclose(np.linalg.norm(rope(q, pos0=p)), np.linalg.norm(q), rtol=1e-14)
+    s1 = rope(q, pos0=7) @ rope(k, pos0=4).T
+    s2 = rope(q, pos0=13) @ rope(k, pos0=10).T
+    np.testing.assert_allclose(s1, s2, rtol=1e-12)
