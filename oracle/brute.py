@@ -127,3 +127,43 @@ def layer_one_head(Q, K, V, beta, N, update, eps, scale):
     if update == "linear":
         M, z = state_from_history(K, V, d, dv)
     return out, M, z
+
+
+def layer_with_projections(X, W_qkv, W_o, beta, N, update, eps, scale, H, d):
+    """The layer from its input: X is a list of rows (tokens) of d_model numbers for one
+    batch element; W_qkv is a list of 3 H d rows of d_model weights, W_o a list of
+    d_model rows of H d weights (row j of W_o: the weights output feature j gives to the
+    concatenated head outputs).  Eq. 5: q_h[t][j] = sum_i X[t][i] W_qkv[h d + j][i] (k, v
+    from the next two blocks of H d rows); the heads run with ``layer_one_head``; Eq. 11:
+    O[t][f] = sum_h sum_j A_h[t][j] W_o[f][h d + j].  Returns the rows of O.
+    """
+    L = len(X)
+    dm = len(X[0])
+    heads_out = []
+    for h in range(H):
+        blocks = []
+        for p in range(3):
+            rows = []
+            for t in range(L):
+                row = []
+                for j in range(d):
+                    w = W_qkv[p * H * d + h * d + j]
+                    acc = 0.0
+                    for i in range(dm):
+                        acc += X[t][i] * w[i]
+                    row.append(acc)
+                rows.append(row)
+            blocks.append(rows)
+        out, _, _ = layer_one_head(blocks[0], blocks[1], blocks[2], beta[h], N, update, eps, scale)
+        heads_out.append(out)
+    O = []
+    for t in range(L):
+        row = []
+        for f in range(len(W_o)):
+            acc = 0.0
+            for h in range(H):
+                for j in range(d):
+                    acc += heads_out[h][t][j] * W_o[f][h * d + j]
+            row.append(acc)
+        O.append(row)
+    return O

@@ -37,6 +37,14 @@ Readings taken where the page is silent or loose:
 7. Every batch element carries its own M and z.
 8. The final segment of a stream may be shorter than N (the summary's BookSum
    discussion of 500K tokens in 2048-token segments); it is processed with its own length.
+9. The projections around the heads (section "Standard Dot-Product Attention", Query,
+   Key, Value projections, Eq. 5; section "Multi-Head Infini-Attention", Eq. 11) take
+   the weights in the "out x in" layout: W_qkv [3 H d, d_model] holds, in its rows
+   h*d + j, H*d + h*d + j and 2*H*d + h*d + j, column j of head h's W_Q, W_K and W_V;
+   W_o [d_model, H d] is the transpose of the page's W_O, so column h*d + j multiplies
+   feature j of head h, heads concatenated in order.  ``layer_forward`` can round Q, K,
+   V and the head outputs to bfloat16 between the steps (``bf16_between``), the storage
+   precision of a bf16 layer; everything else stays float64.
 """
 
 from __future__ import annotations
@@ -56,6 +64,10 @@ __all__ = [
     "segment_bounds",
     "state_numbers_per_layer",
     "advance",
+    "round_to_bf16",
+    "project_qkv",
+    "project_out",
+    "layer_forward",
 ]
 
 LINEAR = "linear"
@@ -243,3 +255,60 @@ def advance(k, v, M, z, update, eps):
     if update == DELTA:
         return memory_update_delta(k, v, M, z, eps)
     raise ValueError(f"unknown update rule {update!r}")
+
+
+def round_to_bf16(x):
+    """Round to the nearest bfloat16 value (ties to even), kept as float64.
+
+    bfloat16 has 8 significant bits: with x = m 2^e, 1/2 <= |m| < 1, the result is
+    round(256 m) 2^(e - 8) (both scalings by powers of two are exact).  Infinities and
+    NaN pass through; bfloat16 overflow and subnormals are not modelled.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.round(m * 256.0), e - 8)   # np.round: ties to even
+    return np.where(np.isfinite(x), r, x)
+
+
+def project_qkv(X, W_qkv, heads, head_dim):
+    """Eq. 5 for every head: Q_h = X W_Q^(h), K_h = X W_K^(h), V_h = X W_V^(h).
+
+    X: [B, L, d_model]; W_qkv: [3 H d, d_model] ("out x in", reading 9).
+    Returns Q, K, V as [B, H, L, d] float64.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W_qkv, dtype=np.float64)
+    B, L, _ = X.shape
+    H, d = heads, head_dim
+    Y = X @ W.T   # [B, L, 3 H d]: feature p*H*d + h*d + j
+    parts = []
+    for p in range(3):
+        blk = Y[:, :, p * H * d:(p + 1) * H * d].reshape(B, L, H, d)
+        parts.append(blk.transpose(0, 2, 1, 3))
+    return tuple(parts)
+
+
+def project_out(A, W_o):
+    """Eq. 11: O = [A_1; ...; A_H] W_O, the head outputs concatenated along features.
+
+    A: [B, H, L, d]; W_o: [d_model, H d] (the page's W_O transposed, reading 9).
+    Returns O as [B, L, d_model] float64.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    W = np.asarray(W_o, dtype=np.float64)
+    B, H, L, d = A.shape
+    cat = A.transpose(0, 2, 1, 3).reshape(B, L, H * d)   # [A_1; ...; A_H] per token
+    return cat @ W.T
+
+
+def layer_forward(X, W_qkv, W_o, beta, segment_len, heads, head_dim, update=LINEAR, eps=1e-6,
+                  scale=None, M0=None, z0=None, bf16_between=False):
+    """The whole layer on a stream X [B, L, d_model]: Eq. 5, the per-head recurrence
+    (Eq. 4, 6-10, ``forward``), Eq. 11.  Returns (O [B, L, d_model], M, z)."""
+    Q, K, V = project_qkv(X, W_qkv, heads, head_dim)
+    if bf16_between:
+        Q, K, V = round_to_bf16(Q), round_to_bf16(K), round_to_bf16(V)
+    A, M, z = forward(Q, K, V, beta, segment_len, update, eps, scale, M0, z0)
+    if bf16_between:
+        A = round_to_bf16(A)
+    return project_out(A, W_o), M, z

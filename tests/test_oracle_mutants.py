@@ -78,6 +78,38 @@ def _segment_local_qk_in_memory(q, k, v, M, z, beta, update, eps, scale, q_local
     return orc.__dict__["_orig_segment_forward"](ql, kl, v, M, z, beta, update, eps, scale)
 
 
+def _project_out_feature_major(A, W_o):
+    A = np.asarray(A, dtype=np.float64)
+    B, H, L, d = A.shape
+    cat = A.transpose(0, 2, 3, 1).reshape(B, L, H * d)   # heads interleaved, not concatenated
+    return cat @ np.asarray(W_o, dtype=np.float64).T
+
+
+def _project_out_untransposed(A, W_o):
+    A = np.asarray(A, dtype=np.float64)
+    B, H, L, d = A.shape
+    return A.transpose(0, 2, 1, 3).reshape(B, L, H * d) @ np.asarray(W_o, dtype=np.float64)
+
+
+def _project_qkv_k_v_swapped(X, W_qkv, heads, head_dim):
+    q, k, v = orc.__dict__["_orig_project_qkv"](X, W_qkv, heads, head_dim)
+    return q, v, k
+
+
+def _project_qkv_head_interleaved(X, W_qkv, heads, head_dim):
+    X = np.asarray(X, dtype=np.float64)
+    Y = X @ np.asarray(W_qkv, dtype=np.float64).T
+    B, L, _ = X.shape
+    H, d = heads, head_dim
+    return tuple(Y[:, :, p * H * d:(p + 1) * H * d].reshape(B, L, d, H).transpose(0, 3, 1, 2) for p in range(3))
+
+
+def _round_truncates(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+
 def _elu_without_one(x):
     x = np.asarray(x, dtype=np.float64)
     return np.where(x > 0, x, np.expm1(np.minimum(x, 0.0)))
@@ -97,6 +129,11 @@ MUTANTS = {
     "elu-without-plus-one": ("elu_plus_one", _elu_without_one),
     "local-qk-ignored": ("segment_forward", _segment_ignores_local_qk),
     "local-qk-fed-to-memory": ("segment_forward", _segment_local_qk_in_memory),
+    "out-projection-heads-interleaved": ("project_out", _project_out_feature_major),
+    "out-projection-untransposed": ("project_out", _project_out_untransposed),
+    "qkv-projection-k-v-swapped": ("project_qkv", _project_qkv_k_v_swapped),
+    "qkv-projection-heads-interleaved": ("project_qkv", _project_qkv_head_interleaved),
+    "bf16-rounding-truncates": ("round_to_bf16", _round_truncates),
 }
 
 
@@ -118,6 +155,11 @@ def _all_pins(rng):
     yield lambda: pins.test_local_qk_with_gate_off_is_causal_sdpa_of_the_local_inputs(rng)
     for u in ("linear", "delta"):
         yield lambda u=u: pins.test_local_qk_leave_the_memory_path_unchanged(rng, u)
+    yield lambda: pins.test_round_to_bf16_matches_torch_and_ties_go_to_even(rng)
+    yield lambda: pins.test_output_projection_is_a_sum_of_per_head_blocks(rng)
+    yield lambda: pins.test_qkv_projection_per_head_columns(rng)
+    for u in ("linear", "delta"):
+        yield lambda u=u: pins.test_layer_with_projections_matches_scalar_loops(rng, u)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -125,6 +167,7 @@ def test_a_planted_mistake_fails_a_pin(monkeypatch, name):
     attr, fn = MUTANTS[name]
     monkeypatch.setitem(orc.__dict__, "_orig_attention", orc.local_causal_attention)
     monkeypatch.setitem(orc.__dict__, "_orig_segment_forward", orc.segment_forward)
+    monkeypatch.setitem(orc.__dict__, "_orig_project_qkv", orc.project_qkv)
     monkeypatch.setattr(orc, attr, fn)
     rng = np.random.default_rng(99)
     caught = []

@@ -348,3 +348,101 @@ def test_rope_is_a_rotation_and_shifts_scores_by_relative_position(rng):
     s1 = rope(q, pos0=7) @ rope(k, pos0=4).T
     s2 = rope(q, pos0=13) @ rope(k, pos0=10).T
     np.testing.assert_allclose(s1, s2, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- the projections (Eq. 5, Eq. 11)
+# Section "Standard Dot-Product Attention" (Query, Key, Value projections) and section
+# "Multi-Head Infini-Attention": each head has its own W_Q, W_K, W_V (d_model x d); the
+# head outputs are concatenated in order and multiplied by W_O (H d x d_model).  Weights
+# here are in the "out x in" layout the oracle takes.
+
+def test_round_to_bf16_matches_torch_and_ties_go_to_even(rng):
+    x = (rng.standard_normal(4000) * np.exp(rng.uniform(-20, 20, 4000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.round_to_bf16(x.astype(np.float64)), ref)
+    # ties: bf16 spacing at 1 is 2^-7
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3 * 2.0 ** -9])
+    np.testing.assert_array_equal(orc.round_to_bf16(ties), [1.0, 1 + 2.0 ** -6, -1.0, 3 * 2.0 ** -9])
+    assert orc.round_to_bf16(np.array([0.0]))[0] == 0.0
+
+
+def _layer_weights(rng, H, d, dm, scale=1.0):
+    w_qkv = rng.standard_normal((3 * H * d, dm)) * (scale / math.sqrt(dm))
+    w_o = rng.standard_normal((dm, H * d)) / math.sqrt(H * d)
+    return w_qkv, w_o
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_layer_with_projections_matches_scalar_loops(rng, update):
+    B, H, d, dm, L, N = 2, 2, 3, 5, 9, 4   # ragged last segment
+    X = rng.standard_normal((B, L, dm))
+    w_qkv, w_o = _layer_weights(rng, H, d, dm, scale=1.5)
+    beta = [0.7, -0.4]
+    O, _, _ = orc.layer_forward(X, w_qkv, w_o, beta, N, H, d, update)
+    assert O.shape == (B, L, dm)
+    for b in range(B):
+        ref = brute.layer_with_projections(X[b].tolist(), w_qkv.tolist(), w_o.tolist(), beta, N, update,
+                                           1e-6, 1 / math.sqrt(d), H, d)
+        np.testing.assert_allclose(O[b], ref, rtol=1e-10, atol=1e-13)
+
+
+def test_output_projection_is_a_sum_of_per_head_blocks(rng):
+    """[A_1; ...; A_H] W_O = sum_h A_h W_O[h d:(h+1) d, :] (block form of the concatenation)."""
+    B, H, L, d, dm = 2, 3, 7, 4, 6
+    A = rng.standard_normal((B, H, L, d))
+    W_O = rng.standard_normal((H * d, dm))   # the page's orientation
+    ref = sum(A[:, h] @ W_O[h * d:(h + 1) * d] for h in range(H))
+    np.testing.assert_allclose(orc.project_out(A, W_O.T), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_qkv_projection_per_head_columns(rng):
+    """Q_h = X W_Q^(h) with W_Q^(h) the d columns of head h, and K, V from their own blocks."""
+    B, L, H, d, dm = 2, 5, 3, 4, 7
+    X = rng.standard_normal((B, L, dm))
+    W = [[rng.standard_normal((dm, d)) for _ in range(H)] for _ in range(3)]   # [part][head]: dm x d
+    w_qkv = np.concatenate([W[p][h].T for p in range(3) for h in range(H)], axis=0)
+    Q, K, V = orc.project_qkv(X, w_qkv, H, d)
+    for p, got in enumerate((Q, K, V)):
+        for h in range(H):
+            np.testing.assert_allclose(got[:, h], X @ W[p][h], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_layer_identity_projections_reduce_to_the_heads(rng, update):
+    """d_model = H d, W_Q = W_K = W_V = W_O = I: O is the per-head layer on X cut into heads."""
+    B, H, d, L, N = 1, 2, 4, 11, 4
+    dm = H * d
+    X = rng.standard_normal((B, L, dm)) / math.sqrt(d)
+    eye = np.eye(dm)
+    beta = [0.3, -1.1]
+    O, M, z = orc.layer_forward(X, np.concatenate([eye, eye, eye]), eye, beta, N, H, d, update)
+    Xh = X.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    A, M2, z2 = orc.forward(Xh, Xh, Xh, beta, N, update)
+    np.testing.assert_allclose(O, A.transpose(0, 2, 1, 3).reshape(B, L, dm), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(M, M2, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_layer_relabelling_heads_changes_nothing(rng, update):
+    """Permuting the heads in W_qkv, W_O and beta together leaves O unchanged."""
+    H, d, dm, L, N = 3, 4, 10, 12, 5
+    X = rng.standard_normal((1, L, dm))
+    w_qkv, w_o = _layer_weights(rng, H, d, dm)
+    beta = np.array([0.5, -0.3, 1.2])
+    O, _, _ = orc.layer_forward(X, w_qkv, w_o, beta, N, H, d, update)
+    perm = [2, 0, 1]
+    rows = np.concatenate([np.arange(p * H * d + h * d, p * H * d + (h + 1) * d) for p in range(3) for h in perm])
+    cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in perm])
+    O2, _, _ = orc.layer_forward(X, w_qkv[rows], w_o[:, cols], beta[perm], N, H, d, update)
+    np.testing.assert_allclose(O2, O, rtol=1e-11, atol=1e-13)
+
+
+def test_layer_is_linear_in_the_output_weights(rng):
+    H, d, dm, L, N = 2, 4, 8, 10, 4
+    X = rng.standard_normal((2, L, dm))
+    w_qkv, w1 = _layer_weights(rng, H, d, dm)
+    w2 = rng.standard_normal(w1.shape)
+    O1, _, _ = orc.layer_forward(X, w_qkv, w1, [0.1, 0.2], N, H, d)
+    O2, _, _ = orc.layer_forward(X, w_qkv, w2, [0.1, 0.2], N, H, d)
+    O3, _, _ = orc.layer_forward(X, w_qkv, w1 - 3 * w2, [0.1, 0.2], N, H, d)
+    np.testing.assert_allclose(O3, O1 - 3 * O2, rtol=1e-10, atol=1e-12)
