@@ -39,11 +39,11 @@ class Config(ctypes.Structure):
     ]
 
 
-KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention")
+KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention", "proj_qkv", "proj_out")
 
 
 class Profile(ctypes.Structure):
-    _fields_ = [("total_ms", ctypes.c_double * 4), ("launches", ctypes.c_int64 * 4)]
+    _fields_ = [("total_ms", ctypes.c_double * len(KERNEL_KINDS)), ("launches", ctypes.c_int64 * len(KERNEL_KINDS))]
 
 
 class InfiniAttnError(RuntimeError):
@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
         "infini_attn_forward_stream": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_forward_stream_ex": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_forward_stream_local": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "infini_attn_project_qkv": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i32, vp]),
+        "infini_attn_project_out": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, vp]),
+        "infini_attn_forward_layer": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_reset_state": (ctypes.c_int, [vp, vp]),
         "infini_attn_get_state": (ctypes.c_int, [vp, vp, vp, vp]),
         "infini_attn_set_state": (ctypes.c_int, [vp, vp, vp, vp]),
@@ -213,6 +216,46 @@ class InfiniAttention:
         st = self._lib.infini_attn_forward_segment(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                                    q.shape[2], _stream_ptr(stream))
         _check("infini_attn_forward_segment", st)
+        return out
+
+    # ------------------------------------------------------------------ the layer (Eq. 5, 11)
+    def _check_layer_io(self, *tensors):
+        self._check_io(*tensors)
+        for t in tensors:
+            if t is not None and t.dtype != torch.bfloat16:
+                raise ValueError("the projections take bfloat16 tensors")
+
+    def project_qkv(self, x, w_qkv, q=None, k=None, v=None, stream=None):
+        """x [B, T, d_model], w_qkv [3 H d, d_model] -> Q, K, V [B, H, T, d]."""
+        self._check_layer_io(x, w_qkv, q, k, v)
+        B, T, dm = x.shape
+        shape = (B, self.heads, T, self.head_dim)
+        q, k, v = (torch.empty(shape, dtype=x.dtype, device=x.device) if t is None else t for t in (q, k, v))
+        st = self._lib.infini_attn_project_qkv(self._h, _ptr(x), _ptr(w_qkv), _ptr(q), _ptr(k), _ptr(v), T, dm,
+                                               _stream_ptr(stream))
+        _check("infini_attn_project_qkv", st)
+        return q, k, v
+
+    def project_out(self, a, w_o, out=None, stream=None):
+        """a [B, H, T, d], w_o [d_model, H d] -> O [B, T, d_model]."""
+        self._check_layer_io(a, w_o, out)
+        B, H, T, d = a.shape
+        dm = w_o.shape[0]
+        if out is None:
+            out = torch.empty((B, T, dm), dtype=a.dtype, device=a.device)
+        st = self._lib.infini_attn_project_out(self._h, _ptr(a), _ptr(w_o), _ptr(out), T, dm, _stream_ptr(stream))
+        _check("infini_attn_project_out", st)
+        return out
+
+    def forward_layer(self, x, w_qkv, w_o, out=None, stream=None):
+        """x [B, T, d_model] -> O [B, T, d_model] through the whole layer (Eq. 5 - Eq. 11)."""
+        self._check_layer_io(x, w_qkv, w_o, out)
+        B, T, dm = x.shape
+        if out is None:
+            out = torch.empty_like(x)
+        st = self._lib.infini_attn_forward_layer(self._h, _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(out), T, dm,
+                                                 _stream_ptr(stream))
+        _check("infini_attn_forward_layer", st)
         return out
 
     # ------------------------------------------------------------------ state

@@ -33,6 +33,8 @@ struct infini_attn {
   bool state_zero = false;   // M, z are logically zero: reset_state ran, memory not yet written
   void* ws_base;
   size_t ws_bytes;
+  void* layer_buf = nullptr;   // forward_layer: Q, K, V, A of one window (bf16)
+  size_t layer_bytes = 0;
   infini::Workspace ws;
   // per-kernel event timing (measurement only)
   bool profiling = false;
@@ -280,6 +282,72 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   return INFINI_OK;
 }
 
+// ---- projections (Eq. 5, Eq. 11) -------------------------------------------------------
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Shared argument checks of the projection calls.
+int check_layer(const infini_attn* h, int64_t n_tokens, int32_t d_model) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  if (!h->bf16) return INFINI_ERR_UNSUPPORTED;
+  if (n_tokens < 1 || n_tokens > (int64_t(1) << 31) - 1) return INFINI_ERR_INVALID_ARG;
+  if (d_model < 32 || d_model % 32 != 0 || d_model > (1 << 16)) return INFINI_ERR_INVALID_ARG;
+  return INFINI_OK;
+}
+
+// Q/K/V of tokens [t0, t0 + tc) of a stream of T tokens: x [B, T, dm] -> q, k, v
+// [B, H, tc, d].
+hipError_t launch_qkv(const infini_attn* h, const void* x, int64_t T, int64_t t0, int tc, int dm,
+                      const void* w_qkv, void* q, void* k, void* v, hipStream_t st) {
+  const int H = h->cfg.heads, D = h->D;
+  infini::GemmArgs g{};
+  g.a = static_cast<const uint16_t*>(x) + t0 * dm;
+  g.a_sb = T * dm;
+  g.a_sh = 0;
+  g.a_st = dm;
+  g.a_dk = dm;
+  g.w = w_qkv;
+  g.c[0] = q;
+  g.c[1] = k;
+  g.c[2] = v;
+  g.c_np = H * D;
+  g.c_dh = D;
+  g.c_sh = int64_t(tc) * D;
+  g.c_st = D;
+  g.c_sb = int64_t(H) * tc * D;
+  g.nb = h->cfg.batch;
+  g.T = tc;
+  g.N = 3 * H * D;
+  g.K = dm;
+  return infini::launch_gemm(g, st);
+}
+
+// O rows [t0, t0 + tc) of a stream of T tokens from A [B, H, tc, d]: out [B, T, dm].
+hipError_t launch_out(const infini_attn* h, const void* a, const void* w_o, void* out, int64_t T,
+                      int64_t t0, int tc, int dm, hipStream_t st) {
+  const int H = h->cfg.heads, D = h->D;
+  infini::GemmArgs g{};
+  g.a = a;
+  g.a_sb = int64_t(H) * tc * D;
+  g.a_sh = int64_t(tc) * D;
+  g.a_st = D;
+  g.a_dk = D;
+  g.w = w_o;
+  g.c[0] = static_cast<uint16_t*>(out) + t0 * dm;
+  g.c[1] = g.c[0];
+  g.c[2] = g.c[0];
+  g.c_np = dm;
+  g.c_dh = dm;
+  g.c_sh = 0;
+  g.c_st = dm;
+  g.c_sb = T * dm;
+  g.nb = h->cfg.batch;
+  g.T = tc;
+  g.N = dm;
+  g.K = H * D;
+  return infini::launch_gemm(g, st);
+}
+
 }  // namespace
 
 INFINI_EXPORT const char* infini_attn_status_string(int status) {
@@ -381,6 +449,7 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   (void)hipFree(h->M);   // also holds z
   (void)hipFree(h->gate);
   (void)hipFree(h->ws_base);
+  if (h->layer_buf) (void)hipFree(h->layer_buf);
   delete h;
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
@@ -469,7 +538,7 @@ INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   const int64_t DD = int64_t(h->D) * h->D;
   return int64_t(h->BH) * DD * 4 + int64_t(h->BH) * h->D * 4 + int64_t(2) * h->cfg.heads * 4 +
-         static_cast<int64_t>(h->ws_bytes);
+         static_cast<int64_t>(h->ws_bytes) + static_cast<int64_t>(h->layer_bytes);
 }
 
 INFINI_EXPORT int64_t infini_attn_window_tokens(infini_attn_t h) {
@@ -501,4 +570,96 @@ INFINI_EXPORT int infini_attn_profile_read(infini_attn_t h, infini_attn_profile_
   h->ev_used = 0;
   h->ev_marks.clear();
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_project_qkv(infini_attn_t h, const void* x, const void* w_qkv, void* q, void* k,
+                                          void* v, int64_t n_tokens, int32_t d_model, void* hip_stream) {
+  int rc = check_layer(h, n_tokens, d_model);
+  if (rc) return rc;
+  if (!x || !w_qkv || !q || !k || !v) return INFINI_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_qkv, 16)) return INFINI_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v})
+    if (!aligned(p, 8)) return INFINI_ERR_INVALID_ARG;
+  const size_t x_bytes = size_t(h->cfg.batch) * size_t(n_tokens) * size_t(d_model) * 2;
+  const size_t w_bytes = size_t(3) * h->cfg.heads * h->D * size_t(d_model) * 2;
+  const size_t o_bytes = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * 2;
+  for (const void* p : {q, k, v}) {
+    if (overlaps(p, o_bytes, x, x_bytes) || overlaps(p, o_bytes, w_qkv, w_bytes)) return INFINI_ERR_INVALID_ARG;
+  }
+  if (overlaps(q, o_bytes, k, o_bytes) || overlaps(q, o_bytes, v, o_bytes) || overlaps(k, o_bytes, v, o_bytes))
+    return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = timed(h, 4, st, [&] {
+    return launch_qkv(h, x, n_tokens, 0, static_cast<int>(n_tokens), d_model, w_qkv, q, k, v, st);
+  });
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_project_out(infini_attn_t h, const void* a, const void* w_o, void* out,
+                                          int64_t n_tokens, int32_t d_model, void* hip_stream) {
+  int rc = check_layer(h, n_tokens, d_model);
+  if (rc) return rc;
+  if (!a || !w_o || !out) return INFINI_ERR_INVALID_ARG;
+  if (!aligned(a, 16) || !aligned(w_o, 16) || !aligned(out, 8)) return INFINI_ERR_INVALID_ARG;
+  const size_t a_bytes = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * 2;
+  const size_t w_bytes = size_t(d_model) * h->cfg.heads * h->D * 2;
+  const size_t o_bytes = size_t(h->cfg.batch) * size_t(n_tokens) * size_t(d_model) * 2;
+  if (overlaps(out, o_bytes, a, a_bytes) || overlaps(out, o_bytes, w_o, w_bytes)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = timed(h, 5, st, [&] {
+    return launch_out(h, a, w_o, out, n_tokens, 0, static_cast<int>(n_tokens), d_model, st);
+  });
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
+}
+
+INFINI_EXPORT int infini_attn_forward_layer(infini_attn_t h, const void* x, const void* w_qkv, const void* w_o,
+                                            void* out, int64_t n_tokens, int32_t d_model, void* hip_stream) {
+  int rc = check_layer(h, n_tokens, d_model);
+  if (rc) return rc;
+  if (!x || !w_qkv || !w_o || !out) return INFINI_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(out, 8)) return INFINI_ERR_INVALID_ARG;
+  const size_t HD = size_t(h->cfg.heads) * h->D;
+  const size_t x_bytes = size_t(h->cfg.batch) * size_t(n_tokens) * size_t(d_model) * 2;
+  if (overlaps(out, x_bytes, x, x_bytes) || overlaps(out, x_bytes, w_qkv, 3 * HD * d_model * 2) ||
+      overlaps(out, x_bytes, w_o, HD * d_model * 2))
+    return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  // scratch for one window: Q, K, V, A [B, H, tc, d] bf16
+  const int64_t win = int64_t(h->window) * h->N;
+  const int64_t tc_max = std::min<int64_t>(win, n_tokens);
+  const size_t part = size_t(h->BH) * size_t(tc_max) * size_t(h->D) * 2;
+  const size_t part_al = align_up(part, 256);
+  if (h->layer_bytes < 4 * part_al) {
+    if (h->layer_buf) {
+      if (hipStreamSynchronize(st) != hipSuccess) return INFINI_ERR_HIP;   // earlier calls may still use it
+      (void)hipFree(h->layer_buf);
+      h->layer_buf = nullptr;
+      h->layer_bytes = 0;
+    }
+    if (hipMalloc(&h->layer_buf, 4 * part_al) != hipSuccess) {
+      (void)hipGetLastError();
+      h->layer_buf = nullptr;
+      return INFINI_ERR_OOM;
+    }
+    h->layer_bytes = 4 * part_al;
+  }
+  for (int64_t t0 = 0; t0 < n_tokens; t0 += win) {
+    const int tc = static_cast<int>(std::min<int64_t>(win, n_tokens - t0));
+    const size_t pb = align_up(size_t(h->BH) * size_t(tc) * size_t(h->D) * 2, 256);
+    char* base = static_cast<char*>(h->layer_buf);
+    void *q = base, *k = base + pb, *v = base + 2 * pb, *a = base + 3 * pb;
+    hipError_t e = timed(h, 4, st, [&] { return launch_qkv(h, x, n_tokens, t0, tc, d_model, w_qkv, q, k, v, st); });
+    if (e != hipSuccess) return INFINI_ERR_HIP;
+    rc = run_stream(h, q, k, v, a, nullptr, nullptr, tc, hip_stream);
+    if (rc) return rc;
+    e = timed(h, 5, st, [&] { return launch_out(h, a, w_o, out, n_tokens, t0, tc, d_model, st); });
+    if (e != hipSuccess) return INFINI_ERR_HIP;
+  }
+  return INFINI_OK;
 }

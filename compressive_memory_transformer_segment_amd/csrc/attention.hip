@@ -5,16 +5,17 @@
 //   A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1} + eps)                          (Eq. 7)
 //   out   = sigmoid(beta_h) A_mem + (1 - sigmoid(beta_h)) A_dot                   (Eq. 10)
 //
-// One workgroup = 4 waves = 128 queries of one (batch, head, segment); every wave owns 32
-// queries.  The kernel works in the transposed frame: S^T = K Q^T and O^T = V^T P^T, so
+// bf16 path: one workgroup = 8 waves = 256 queries of one (batch, head, segment); every
+// wave owns 32 queries.  The kernel works in the transposed frame: S^T = K Q^T and O^T = V^T P^T, so
 // that a lane holds one query (lane % 32) in every MFMA result.  Softmax statistics are
 // then per-lane scalars (plus one exchange with lane ^ 32), the S^T result registers are
 // directly the B operand of O^T += V^T P^T, and the retrieval sigma(Q) reuses the Q
 // registers (Q is the B operand of S^T) as the B operand of A_mem^T = M^T sigma(Q)^T.
 //
 // K and V tiles (64 keys x d) go from HBM straight into LDS with buffer -> LDS copies,
-// double buffered: the copy of tile j + 1 (in the last iteration: M^T_{s-1} and z_{s-1})
-// is in flight while tile j is consumed, and no registers hold data in transit.  Rows past
+// four buffers deep: the copies of tiles j + 1 .. j + 3 (after the last tile: M^T_{s-1}
+// and z_{s-1}) are in flight while tile j is consumed, and no registers hold data in
+// transit.  The scores of tile j + 1 are computed while the softmax of tile j runs.  Rows past
 // the segment end arrive as zeros (buffer range check), so ragged tails need no branches.
 // The V^T operand of O^T += V^T P^T is read with LDS transpose reads, in the key order the
 // S^T result registers hold.  The online softmax is in the exp2 domain with the scale
@@ -30,7 +31,6 @@ namespace infini {
 
 namespace {
 
-constexpr int kThreads = 256;    // float32 path
 constexpr int kThreadsA = 512;   // bf16 path: 8 waves
 constexpr int kBMA = 256;        // bf16 path: queries per workgroup (8 waves x 32)
 constexpr int kBN = 64;          // keys per tile
@@ -61,28 +61,6 @@ __device__ __forceinline__ void tile_of_block(int units, int nq, int& u, int& qt
   const int r = i - gi * kGroup * nq;        // position inside the group
   qt = nq - 1 - r / g_units;
   u = x + 8 * (gi * kGroup + r % g_units);
-}
-
-// s_waitcnt with vmcnt <= vm and lgkmcnt = 0 (expcnt not waited on); gfx9 encoding.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-}
-__device__ __forceinline__ void wait_vm_le(int vm) {   // vm wave-uniform, 0 .. 15
-  switch (vm) {
-    case 0: wait_vm_lgkm0<0>(); break;
-    case 1: wait_vm_lgkm0<1>(); break;
-    case 2: wait_vm_lgkm0<2>(); break;
-    case 3: wait_vm_lgkm0<3>(); break;
-    case 4: wait_vm_lgkm0<4>(); break;
-    case 5: wait_vm_lgkm0<5>(); break;
-    case 6: wait_vm_lgkm0<6>(); break;
-    case 7: wait_vm_lgkm0<7>(); break;
-    case 8: wait_vm_lgkm0<8>(); break;
-    case 9: wait_vm_lgkm0<9>(); break;
-    case 10: wait_vm_lgkm0<10>(); break;
-    default: wait_vm_lgkm0<0>(); break;
-  }
 }
 
 template <int D, bool PARTS>

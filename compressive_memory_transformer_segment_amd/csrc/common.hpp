@@ -129,6 +129,34 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_base), 16, static_cast<int>(voffset), 0, 0, 0);
 }
 
+// s_waitcnt with vmcnt <= vm and lgkmcnt = 0 (expcnt not waited on); gfx9 encoding.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm_le(int vm) {   // vm wave-uniform, 0 .. 16
+  switch (vm) {
+    case 0: wait_vm_lgkm0<0>(); break;
+    case 1: wait_vm_lgkm0<1>(); break;
+    case 2: wait_vm_lgkm0<2>(); break;
+    case 3: wait_vm_lgkm0<3>(); break;
+    case 4: wait_vm_lgkm0<4>(); break;
+    case 5: wait_vm_lgkm0<5>(); break;
+    case 6: wait_vm_lgkm0<6>(); break;
+    case 7: wait_vm_lgkm0<7>(); break;
+    case 8: wait_vm_lgkm0<8>(); break;
+    case 9: wait_vm_lgkm0<9>(); break;
+    case 10: wait_vm_lgkm0<10>(); break;
+    case 11: wait_vm_lgkm0<11>(); break;
+    case 12: wait_vm_lgkm0<12>(); break;
+    case 13: wait_vm_lgkm0<13>(); break;
+    case 14: wait_vm_lgkm0<14>(); break;
+    case 15: wait_vm_lgkm0<15>(); break;
+    case 16: wait_vm_lgkm0<16>(); break;
+    default: wait_vm_lgkm0<0>(); break;   // anything else: wait for everything
+  }
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

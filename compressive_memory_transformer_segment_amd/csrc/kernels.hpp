@@ -50,6 +50,27 @@ struct WindowArgs {
   __host__ __device__ int seg_tokens(int s_local) const { return (s0 + s_local == S - 1) ? n_last : N; }
 };
 
+// Dense projection C = A W^T (bf16 in and out, fp32 accumulation) over rows grouped in
+// nb batches of T rows: A[b][t][k] (k < K), W[n][k] row-major (n < N), C[b][t][n].
+// Row and column maps let one kernel read the attention output head-major and write
+// Q / K / V head-major:
+//   A[b][t][k] at a + b*a_sb + (k / a_dk)*a_sh + t*a_st + k % a_dk        (elements)
+//   C[b][t][n] at c[n / c_np] + b*c_sb + ((n % c_np) / c_dh)*c_sh + t*c_st + n % c_dh
+// Requirements (checked by the caller): K and a_dk multiples of 32, a_st >= 32;
+// N, c_np, c_dh multiples of 8; a, w 16-byte aligned, c 8-byte aligned.
+struct GemmArgs {
+  const void* a;
+  int64_t a_sb, a_sh, a_st;
+  int a_dk;
+  const void* w;
+  void* c[3];
+  int64_t c_sb, c_sh, c_st;
+  int c_np, c_dh;
+  int nb, T, N, K;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
 hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
 hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T
 hipError_t launch_chain(const WindowArgs& a, hipStream_t st);          // M/z recurrence

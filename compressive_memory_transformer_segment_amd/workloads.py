@@ -23,7 +23,14 @@ Recipe (fixed, so any segment of any stream can be regenerated on its own):
 * beta ~ N(0, 1) per head from SeedSequence([seed, BETA_TAG]), or 0;
 * the planted pair (1M-token workload): k* = g / ||g|| with g ~ N(0, I_d), normalised
   in float64 and then rounded; v* ~ N(0, 1) / sqrt(d).  It replaces K and V at token 0
-  of segment 0 in every head, and Q at the stream's final token is k*.
+  of segment 0 in every head, and Q at the stream's final token is k*;
+* the whole layer (input X and the projection weights, section "Standard Dot-Product
+  Attention" and "Multi-Head Infini-Attention"): X [B, L, d_model] ~ N(0, 1) per entry,
+  W_qkv [3 H d, d_model] ~ N(0, 1 / (d_model d)) so that the projected Q, K, V have the
+  N(0, 1) / sqrt(d) entries of the per-head workloads, W_o [d_model, H d] ~ N(0, 1 / (H d));
+  drawn as float32 from SeedSequence([seed, LAYER_TAG, tensor id]) (X per batch element:
+  [seed, LAYER_TAG, 0, b]) and rounded to bf16.  d_model = H d unless stated (the pages'
+  small models: 8 heads of 128 in d_model = 1024).
 """
 
 from __future__ import annotations
@@ -36,6 +43,7 @@ import numpy as np
 
 BETA_TAG = 0xBE7A
 PLANT_TAG = 0x9A55
+LAYER_TAG = 0x1A7E
 
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SCALE = 0, 1, 2, 3
 
@@ -129,6 +137,20 @@ def planted_pair(w: Workload):
     if w.io_dtype == "bf16":
         k_star, v_star = round_to_bf16(k_star), round_to_bf16(v_star)
     return k_star, v_star
+
+
+def layer_inputs(w: Workload, d_model: int | None = None):
+    """(X [B, L, d_model], W_qkv [3 H d, d_model], W_o [d_model, H d]) as float32 arrays
+    holding bf16 values (the recipe above)."""
+    H, d = w.heads, w.head_dim
+    dm = H * d if d_model is None else d_model
+    X = np.empty((w.batch, w.n_tokens, dm), dtype=np.float32)
+    for b in range(w.batch):
+        X[b] = _rng(w.seed, LAYER_TAG, 0, b).standard_normal((w.n_tokens, dm), dtype=np.float32)
+    w_qkv = _rng(w.seed, LAYER_TAG, 1).standard_normal((3 * H * d, dm), dtype=np.float32) / np.float32(
+        math.sqrt(dm * d))
+    w_o = _rng(w.seed, LAYER_TAG, 2).standard_normal((dm, H * d), dtype=np.float32) / np.float32(math.sqrt(H * d))
+    return round_to_bf16(X), round_to_bf16(w_qkv), round_to_bf16(w_o)
 
 
 _POOL = None

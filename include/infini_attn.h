@@ -16,9 +16,10 @@
  * with sigma = ELU + 1 (alpha = 1).  The state (M, z) is carried from segment to segment
  * and from call to call (Eq. 4, "The Recurrent Formulation of Infini-Attention").
  *
- * Boundary.  The library sits after the Q/K/V projections (Eq. 5) and before the output
- * projection W_O (Eq. 11): callers pass per-head Q, K, V and receive the per-head gated
- * context A.
+ * Boundary.  The core calls sit after the Q/K/V projections (Eq. 5) and before the
+ * output projection W_O (Eq. 11): callers pass per-head Q, K, V and receive the per-head
+ * gated context A.  The layer calls at the end of this header add the two projections
+ * (project_qkv, project_out, and forward_layer for the whole of Eq. 5 -> Eq. 11).
  *
  * Layout.  Q, K, V and out are dense [B, H, T, d] arrays (d fastest), T = tokens of the
  * call, element type io_dtype.  Segments start at the first token of every call; a last
@@ -125,20 +126,55 @@ int infini_attn_set_state(infini_attn_t h, const float* M, const float* z, void*
 /* Replace the H gate logits (host memory).  Waits for the device to be idle first. */
 int infini_attn_set_beta(infini_attn_t h, const float* beta_host);
 
-/* Device bytes the handle holds: state + gate values + workspace.  Constant for the
- * handle's life, independent of how many tokens have been processed. */
+/* Device bytes the handle holds: state + gate values + workspace, plus the layer scratch
+ * once forward_layer has run (at most one window's worth).  Independent of how many
+ * tokens have been processed. */
 int64_t infini_attn_device_bytes(infini_attn_t h);
 
 /* Tokens per internal window of forward_stream (window segments * N). */
 int64_t infini_attn_window_tokens(infini_attn_t h);
+
+/* ---- The layer around the heads (Eq. 5 and Eq. 11; bf16 io_dtype only) ----------------
+ *
+ * X and O are [B, T, d_model] (d_model fastest), T = n_tokens.  Weights are bf16 in the
+ * "out x in" layout (row j holds the d_model, resp. H*d, input weights of output feature
+ * j), i.e. the transposes of the pages' W_Q, W_K, W_V (d_model x d each per head) and
+ * W_O (H*d x d_model):
+ *   w_qkv: [3*H*d, d_model]; row h*d + j is column j of head h's W_Q, row H*d + h*d + j
+ *          of its W_K, row 2*H*d + h*d + j of its W_V;
+ *   w_o:   [d_model, H*d]; column h*d + j multiplies feature j of head h's output A_h,
+ *          so O = [A_1; ...; A_H] W_O with the heads concatenated in order (Eq. 11).
+ * Products accumulate in float32 and are rounded once to bf16 where they are stored:
+ * Q, K, V and A are bf16 between the steps, as in the per-head calls.
+ * Requirements: d_model a multiple of 32; X, weights 16-byte aligned; outputs 8-byte
+ * aligned; outputs must not overlap inputs.  Errors: INFINI_ERR_UNSUPPORTED for an f32
+ * handle, INFINI_ERR_INVALID_ARG otherwise, before anything is enqueued. */
+
+/* Q, K, V [B, H, n_tokens, d] (the per-head layout above) from X (Eq. 5). */
+int infini_attn_project_qkv(infini_attn_t h, const void* x, const void* w_qkv, void* q, void* k,
+                            void* v, int64_t n_tokens, int32_t d_model, void* hip_stream);
+
+/* O [B, n_tokens, d_model] = [A_1; ...; A_H] W_O from the per-head A [B, H, n_tokens, d]
+ * (Eq. 11). */
+int infini_attn_project_out(infini_attn_t h, const void* a, const void* w_o, void* out,
+                            int64_t n_tokens, int32_t d_model, void* hip_stream);
+
+/* The whole layer on a stream of n_tokens tokens: project_qkv, forward_stream,
+ * project_out, one internal window (window_tokens tokens) at a time, with Q, K, V and A
+ * in library-owned device memory (allocated on first use and grown when a call needs more;
+ * released by destroy; 4 * B * H * d * 2 bytes per window token).  Same result as the
+ * three calls on the whole stream; the state advances as in forward_stream. */
+int infini_attn_forward_layer(infini_attn_t h, const void* x, const void* w_qkv, const void* w_o,
+                              void* out, int64_t n_tokens, int32_t d_model, void* hip_stream);
 
 /* Per-kernel timing with HIP events, for measurement.  While enabled, every kernel the
  * handle launches is bracketed by two events on the call's stream.  profile_read waits
  * for the recorded events, reports the summed durations per kernel kind, and clears the
  * record.  Kernel kinds: 0 = key sums (delta rule only), 1 = state pass (per-segment
  * sigma(K)^T V, key sums, delta Gram term, V transpose), 2 = memory chain (Eq. 8/9
- * recurrence), 3 = fused local attention + retrieval + gate (Eq. 6, 7, 10). */
-#define INFINI_KERNEL_KINDS 4
+ * recurrence), 3 = fused local attention + retrieval + gate (Eq. 6, 7, 10),
+ * 4 = Q/K/V projection (Eq. 5), 5 = output projection (Eq. 11). */
+#define INFINI_KERNEL_KINDS 6
 typedef struct {
   double total_ms[INFINI_KERNEL_KINDS];
   int64_t launches[INFINI_KERNEL_KINDS];

@@ -16,6 +16,7 @@ EXPECTED = {
     "infini_attn_set_state", "infini_attn_set_beta", "infini_attn_device_bytes",
     "infini_attn_window_tokens", "infini_attn_destroy", "infini_attn_status_string",
     "infini_attn_profile_enable", "infini_attn_profile_read",
+    "infini_attn_project_qkv", "infini_attn_project_out", "infini_attn_forward_layer",
 }
 
 
@@ -89,3 +90,6 @@ def test_calls_on_a_missing_handle_fail_cleanly(lib):
         assert lib.infini_attn_window_tokens(h) == -1
         assert lib.infini_attn_profile_enable(h, 1) == -1
         assert lib.infini_attn_profile_read(h, ctypes.byref(binding.Profile())) == -1
+        assert lib.infini_attn_project_qkv(h, p, p, p, p, p, 16, 64, None) == -1
+        assert lib.infini_attn_project_out(h, p, p, p, 16, 64, None) == -1
+        assert lib.infini_attn_forward_layer(h, p, p, p, p, 16, 64, None) == -1
