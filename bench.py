@@ -7,7 +7,11 @@ the roofline of the dominant kernel (the fused local-attention + retrieval + gat
 timed with HIP events on its own stream inside the timed region), and the CPU oracle's
 throughput on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --layer a step is one ``infini_attn_forward_layer`` instead: the whole layer from
+its input X [B, T, d_model] to O, the Q/K/V projection (Eq. 5) and the output projection
+(Eq. 11) included; the roofline is then that of the kernel with the most time per step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer]
 """
 
 from __future__ import annotations
@@ -35,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--local-qk", action="store_true",
                     help="separate (position-embedded) Q/K for the local attention: forward_stream_local")
+    ap.add_argument("--layer", action="store_true",
+                    help="the whole layer X -> O (Q/K/V and output projections included): forward_layer")
+    ap.add_argument("--d-model", type=int, default=0, help="--layer: model width (default H * d)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -88,6 +95,33 @@ def cpu_baseline(w, budget_s: float):
                        f"{w.heads} heads ({elapsed:.1f} s), scaled to all heads")}
 
 
+def cpu_baseline_layer(w, d_model: int, budget_s: float):
+    """The oracle's whole layer (projections included) on the stream's first segments,
+    doubling the sample until about budget_s seconds of CPU work; tokens/s."""
+    import numpy as np
+    from compressive_memory_transformer_segment_amd import workloads as wl
+    from oracle import infini_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    X, w_qkv, w_o = wl.layer_inputs(w.with_tokens(min(w.n_tokens, 4 * w.segment_len)), d_model)
+    beta = wl.beta_for(w)
+    n_seg, elapsed = 1, 0.0
+    while True:
+        n = min(n_seg * w.segment_len, X.shape[1])
+        t0 = time.perf_counter()
+        orc.layer_forward(X[:, :n], w_qkv, w_o, beta, w.segment_len, w.heads, w.head_dim, w.update, eps=w.eps)
+        elapsed = time.perf_counter() - t0
+        if 2 * elapsed > budget_s or n >= X.shape[1]:
+            break
+        n_seg *= 2
+    return {"value": w.batch * n / elapsed, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "sample": f"oracle.layer_forward on the first {n} tokens (all heads, d_model={d_model}), {elapsed:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -107,14 +141,21 @@ def main():
     dev = torch.device("cuda", 0)
 
     # inputs resident in HBM before the timed region
-    shape = (w.batch, w.heads, w.n_tokens, w.head_dim)
-    Q, K, V = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
-    for b in range(w.batch):
-        for s in range(w.n_segments):
-            lo = s * w.segment_len
-            for x, p in zip((Q, K, V), wl.segment_inputs(w, b, s)):
-                x[b, :, lo:lo + p.shape[1]] = torch.from_numpy(p).to(dev, torch.bfloat16)
-    out = torch.empty_like(Q)
+    d_model = args.d_model or w.heads * w.head_dim
+    if args.layer:   # the layer's input X and its weights
+        Xh, Wqh, Woh = wl.layer_inputs(w, d_model)
+        X, Wq, Wo = (torch.from_numpy(a).to(dev, torch.bfloat16).contiguous() for a in (Xh, Wqh, Woh))
+        del Xh, Wqh, Woh
+        out_l = torch.empty_like(X)
+    else:            # per-head Q, K, V
+        shape = (w.batch, w.heads, w.n_tokens, w.head_dim)
+        Q, K, V = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
+        for b in range(w.batch):
+            for s in range(w.n_segments):
+                lo = s * w.segment_len
+                for x, p in zip((Q, K, V), wl.segment_inputs(w, b, s)):
+                    x[b, :, lo:lo + p.shape[1]] = torch.from_numpy(p).to(dev, torch.bfloat16)
+        out = torch.empty_like(Q)
     layer = binding.InfiniAttention(w.batch, w.heads, w.head_dim, w.segment_len, update=w.update,
                                     io_dtype="bf16", eps=w.eps, beta=wl.beta_for(w))
     stream = torch.cuda.current_stream()
@@ -126,12 +167,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.local_qk:   # distinct buffers; the values do not change the kernels' work
+    if args.local_qk and not args.layer:   # distinct buffers; the values do not change the kernels' work
         Ql, Kl = Q.clone(), K.clone()
 
     def step():
         layer.reset_state(stream)
-        if args.local_qk:
+        if args.layer:
+            layer.forward_layer(X, Wq, Wo, out=out_l, stream=stream)
+        elif args.local_qk:
             layer.forward_stream_local(Q, K, V, Ql, Kl, out=out, stream=stream)
         else:
             layer.forward_stream(Q, K, V, out=out, stream=stream)
@@ -164,12 +207,23 @@ def main():
     tokens = w.batch * w.n_tokens
     value = tokens / (ms / 1e3)
     flops_step = profiling.layer_flops(w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens, w.update)
-    attn_ms, attn_launches = prof["attention"]
-    attn_avg_s = attn_ms / attn_launches / 1e3
     attn_flops = profiling.attention_kernel_flops(w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens)
-    attn_flops_launch = attn_flops * args.steps / attn_launches
-    achieved = attn_flops_launch / attn_avg_s / 1e12
-    traffic = traffic_from_profiles(profiling.kernel_source_hash())
+    mfma_kernels = {"attention": ("k_attn_bf16 (local attention + retrieval + gate)", attn_flops)}
+    if args.layer:
+        f_qkv, f_out = profiling.projection_flops(w.batch, w.n_tokens, d_model, w.heads, w.head_dim)
+        flops_step += f_qkv + f_out
+        mfma_kernels["proj_qkv"] = ("k_gemm (Q/K/V projection)", f_qkv)
+        mfma_kernels["proj_out"] = ("k_gemm (output projection)", f_out)
+    rooflines = {}
+    for kind, (kname, flops) in mfma_kernels.items():
+        t_ms, n = prof[kind]
+        avg_s = t_ms / n / 1e3
+        ach = flops * args.steps / n / avg_s / 1e12
+        rooflines[kind] = {"kernel": kname, "achieved": ach, "frac": ach / (profiling.PEAK_BF16_FLOPS / 1e12),
+                           "avg_launch_us": avg_s * 1e6, "total_ms_per_step": t_ms / args.steps}
+    dominant = max(rooflines, key=lambda k: rooflines[k]["total_ms_per_step"])
+    achieved = rooflines[dominant]["achieved"]
+    traffic = traffic_from_profiles(profiling.kernel_source_hash()) if dominant == "attention" else None
 
     rec = {
         "metric": METRIC,
@@ -184,28 +238,32 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
-                   "segment_len": w.segment_len, "n_tokens": w.n_tokens, "update": w.update,
-                   "local_qk": bool(args.local_qk), "parallelism": "none"},
+        "config": {"workload": w.name + ("-layer" if args.layer else ""), "batch": w.batch, "heads": w.heads,
+                   "head_dim": w.head_dim, "segment_len": w.segment_len, "n_tokens": w.n_tokens,
+                   "update": w.update, "local_qk": bool(args.local_qk),
+                   "projections": bool(args.layer), "d_model": d_model if args.layer else None,
+                   "parallelism": "none"},
         "pct_bf16_peak": 100.0 * flops_step / (ms / 1e3) / profiling.PEAK_BF16_FLOPS,
         "roofline": {
-            "kernel": "k_attn_bf16 (local attention + retrieval + gate)",
+            "kernel": rooflines[dominant]["kernel"],
             "bound": "mfma",
             "achieved": achieved,
             "peak": profiling.PEAK_BF16_FLOPS / 1e12,
             "unit": "TFLOP/s",
             "frac": achieved / (profiling.PEAK_BF16_FLOPS / 1e12),
             "traffic": traffic,
-            "algorithmic_bytes": profiling.attention_kernel_bytes(
-                w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens),
-            "avg_launch_us": attn_avg_s * 1e6,
+            "algorithmic_bytes": (profiling.attention_kernel_bytes(
+                w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens) if dominant == "attention" else None),
+            "avg_launch_us": rooflines[dominant]["avg_launch_us"],
         },
+        "mfma_kernels": rooflines,
         "kernels_avg_us": {k: (t / n * 1e3 if n else None) for k, (t, n) in prof.items()},
         "wall_ms_per_step": wall_ms / args.steps,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+        rec["cpu_baseline"] = (cpu_baseline_layer(w, d_model, args.cpu_budget_s) if args.layer
+                               else cpu_baseline(w, args.cpu_budget_s))
     else:
         rec["cpu_baseline"] = None
     layer.close()

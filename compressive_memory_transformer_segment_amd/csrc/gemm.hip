@@ -5,8 +5,9 @@
 // attention output and writes per-head Q / K / V in the [B, H, T, d] layout the attention
 // kernels use, without separate transpose passes.
 //
-// Tiling (gfx950): a workgroup = 4 waves (one per SIMD) computes a 256-token x 256-feature
-// tile; each wave owns 128 x 128 of it, 16 MFMA 32x32x16 accumulators (256 registers).
+// Tiling (gfx950): a workgroup = 8 waves (two per SIMD, so one wave's waits are covered
+// by the other's products) computes a 256-token x 256-feature tile; each wave owns 128
+// features x 64 tokens of it, 8 MFMA 32x32x16 accumulators (128 registers).
 // The MFMAs run in the transposed frame, D[n][t] = (W A^T)[n][t]: a lane then holds one
 // token and four consecutive output features in each result register quad, which become
 // one 8-byte store.  Both operands go HBM -> LDS by buffer -> LDS copies in stages of 32 k,
@@ -26,12 +27,19 @@ namespace infini {
 
 namespace {
 
-constexpr int kGT = 256;                      // 4 waves
+constexpr int kWaves = 8;                     // 2 per SIMD
+constexpr int kGT = 64 * kWaves;
 constexpr int kGM = 256;                      // tokens per tile
 constexpr int kGN = 256;                      // output features per tile
 constexpr int kGK = 32;                       // k per stage
 constexpr int kStage = (kGN + kGM) * kGK;     // elements of one buffer: [W tile | A tile]
 constexpr int kGroupM = 4;                    // token tiles per group of the tile order
+constexpr int kWN = 2;                        // waves along the features
+constexpr int kWM = kWaves / kWN;             // waves along the tokens
+constexpr int kTI = kGN / kWN / 32;           // 32-feature blocks per wave
+constexpr int kTJ = kGM / kWM / 32;           // 32-token blocks per wave
+constexpr int kCPW = 16 / kWaves;             // row groups of each operand a wave copies per stage
+static_assert(kCPW * kWaves == 16 && kTI * kWN * 32 == kGN && kTJ * kWM * 32 == kGM, "tile split");
 
 template <int N_>
 using IC = std::integral_constant<int, N_>;
@@ -89,10 +97,10 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int wn = wave & 1, wm = wave >> 1;   // the wave's 128 features / 128 tokens
+  const int wn = wave % kWN, wm = wave / kWN;   // the wave's features / tokens
   const int S = g.K / kGK;
 
-  // copies: wave w fills row groups 4w .. 4w + 3 of the W tile and of the A tile; lane i
+  // copies: wave w fills row groups kCPW w .. kCPW w + kCPW - 1 of the W tile and of the A tile; lane i
   // takes row 16 grp + i % 16, chunk i / 16 of the stage.  One buffer resource per operand
   // starts at row 0 of the tile at the stage's first k and spans the valid rows (rows past
   // the end read as zeros); the row group is in the lane offset.
@@ -103,10 +111,10 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
   const int w_rows = min(g.N - n0, kGN), a_rows = min(g.T - t0, kGM);
   const uint32_t w_bytes = static_cast<uint32_t>((w_rows - 1) * K2 + 64);
   const uint32_t a_bytes = static_cast<uint32_t>((a_rows - 1) * a_st2 + 64);
-  uint32_t vo_w[4], vo_a[4];
+  uint32_t vo_w[kCPW], vo_a[kCPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * (4 * wave + j) + (lane & 15);
+  for (int j = 0; j < kCPW; ++j) {
+    const int r = 16 * (kCPW * wave + j) + (lane & 15);
     vo_w[j] = static_cast<uint32_t>(r * K2) + 16 * (lane >> 4);
     vo_a[j] = static_cast<uint32_t>(r * a_st2) + 16 * (lane >> 4);
   }
@@ -126,10 +134,10 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
     const bool live = s_next < S;
     ++s_next;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) copy_to_lds(wcur, live ? w_bytes : 0u, dst + 512 * (4 * wave + j), vo_w[j]);
+    for (int j = 0; j < kCPW; ++j) copy_to_lds(wcur, live ? w_bytes : 0u, dst + 512 * (kCPW * wave + j), vo_w[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      copy_to_lds(acur, live ? a_bytes : 0u, dst + kGN * kGK + 512 * (4 * wave + j), vo_a[j]);
+    for (int j = 0; j < kCPW; ++j)
+      copy_to_lds(acur, live ? a_bytes : 0u, dst + kGN * kGK + 512 * (kCPW * wave + j), vo_a[j]);
     if (live) {
       wcur += 2 * kGK;
       acur += 2 * kGK;
@@ -141,37 +149,37 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
     }
   };
 
-  // operand reads: row 32 blk + l32 of the wave's 128 rows, chunk 2 ks + hl
+  // operand reads: row 32 blk + l32 of the wave's rows, chunk 2 ks + hl
   const int rd = ((l32 >> 4) * 64 + 16 * hl + (l32 & 15)) * 8;
-  const int rw = 4096 * wn + rd, ra = kGN * kGK + 4096 * wm + rd;
+  const int rw = kTI * 1024 * wn + rd, ra = kGN * kGK + kTJ * 1024 * wm + rd;
 
-  f32x16 acc[4][4];
+  f32x16 acc[kTI][kTJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kTI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero16();
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    for (int j = 0; j < kTJ; ++j) acc[i][j] = zero16();
+  bf16x8 fa0[kTI], fb0[kTJ], fa1[kTI], fb1[kTJ];
 
-  auto load = [&](const uint16_t* buf, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+  auto load = [&](const uint16_t* buf, int ks, bf16x8 (&fa)[kTI], bf16x8 (&fb)[kTJ]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = as_bf16x8(ld16(buf + rw + 1024 * i + 256 * ks));
+    for (int i = 0; i < kTI; ++i) fa[i] = as_bf16x8(ld16(buf + rw + 1024 * i + 256 * ks));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fb[i] = as_bf16x8(ld16(buf + ra + 1024 * i + 256 * ks));
+    for (int j = 0; j < kTJ; ++j) fb[j] = as_bf16x8(ld16(buf + ra + 1024 * j + 256 * ks));
   };
-  auto mma = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+  auto mma = [&](const bf16x8 (&fa)[kTI], const bf16x8 (&fb)[kTJ]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < kTJ; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
   };
-  // the 8 operand reads of the next half go out one by one between the first 8 products
+  // the operand reads of the next half go out one by one between the first products
   auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kTI + kTJ; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kTI * kTJ - kTI - kTJ, 0);
   };
   // stage s from buffer s % 4; its first half's operands are already in fa0 / fb0
   auto step = [&](auto bc, int s) __attribute__((always_inline)) {
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
     load(bufp(IC<bi>{}), 1, fa1, fb1);
     mma(fa0, fb0);
     interleave();
-    wait_vm_lgkm0<8>();             // this wave's copies of stage s + 1 have landed
+    wait_vm_lgkm0<2 * kCPW>();      // this wave's copies of stage s + 1 have landed
     __builtin_amdgcn_s_barrier();   // ... everyone's; and everyone is done with stage s - 1
     issue(bufp(IC<bi + 3>{}));   // stage s + 3
     load(bufp(IC<bi + 1>{}), 0, fa0, fb0);   // (past the last stage: unused)
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
   issue(buf0);
   issue(buf1);
   issue(buf2);
-  wait_vm_lgkm0<16>();   // stage 0
+  wait_vm_lgkm0<4 * kCPW>();   // stage 0
   __builtin_amdgcn_s_barrier();
   load(buf0, 0, fa0, fb0);
   for (int s = 0; s < S; s += 4) {
@@ -202,27 +210,27 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const GemmArgs g) {
   wait_vm_lgkm0<0>();   // no copy may land in LDS after the workgroup ends
 
   // epilogue: register quad q of accumulator (i, j) holds features
-  // n0 + 128 wn + 32 i + 8 q + 4 hl + 0..3 of token t0 + 128 wm + 32 j + l32
-  int64_t trow[4];
-  bool tok_ok[4];
+  // n0 + 32 (kTI wn + i) + 8 q + 4 hl + 0..3 of token t0 + 32 (kTJ wm + j) + l32
+  int64_t trow[kTJ];
+  bool tok_ok[kTJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + 128 * wm + 32 * j + l32;
+  for (int j = 0; j < kTJ; ++j) {
+    const int t = t0 + 32 * (kTJ * wm + j) + l32;
     tok_ok[j] = t < g.T;
     trow[j] = b * g.c_sb + static_cast<int64_t>(t) * g.c_st;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kTI; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int nu = n0 + 128 * wn + 32 * i + 8 * q;   // wave-uniform
+      const int nu = n0 + 32 * (kTI * wn + i) + 8 * q;   // wave-uniform
       if (nu >= g.N) continue;
       const int part = nu / g.c_np, rem = nu - part * g.c_np;
       const int hh = rem / g.c_dh, jj = rem - hh * g.c_dh;
       uint16_t* cb = static_cast<uint16_t*>(part == 0 ? g.c[0] : (part == 1 ? g.c[1] : g.c[2])) +
                      hh * g.c_sh + jj + 4 * hl;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kTJ; ++j) {
         if (!tok_ok[j]) continue;
         const f32x16& v = acc[i][j];
         st8(cb + trow[j], u32x2{pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3])});

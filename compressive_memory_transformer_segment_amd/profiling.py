@@ -68,6 +68,12 @@ def attention_kernel_bytes(batch, heads, head_dim, segment_len, n_tokens) -> flo
     return batch * heads * (n_tokens * d * 2 * 4 + segs * (d * d * 2 + d * 4))
 
 
+def projection_flops(batch, n_tokens, d_model, heads, head_dim):
+    """(Q/K/V projection, output projection) FLOPs: 2 B T d_model (3 H d) and 2 B T (H d) d_model."""
+    hd = heads * head_dim
+    return 2.0 * batch * n_tokens * d_model * 3 * hd, 2.0 * batch * n_tokens * hd * d_model
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in ("attention.hip", "common.hpp", "kernels.hpp"):
