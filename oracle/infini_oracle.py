@@ -68,6 +68,8 @@ __all__ = [
     "project_qkv",
     "project_out",
     "layer_forward",
+    "decode_token",
+    "decode_stream",
 ]
 
 LINEAR = "linear"
@@ -312,3 +314,62 @@ def layer_forward(X, W_qkv, W_o, beta, segment_len, heads, head_dim, update=LINE
     if bf16_between:
         A = round_to_bf16(A)
     return project_out(A, W_o), M, z
+
+
+def decode_token(q, k, v, cache_k, cache_v, M, z, beta, eps, scale):
+    """One token of incremental decoding for one head (the summary's "fast streaming
+    inference": tokens arrive one at a time inside a segment).
+
+    The token's key and value join the segment's cache; the local attention (Eq. 6) is a
+    softmax over every cached token, all of which precede or are the current one; the
+    memory read (Eq. 7) uses the state from before the segment; Eq. 10 gates the two.
+    q, k, v: [d]; cache_k, cache_v: [n, d], the segment's earlier tokens.
+    Returns (a [d], cache_k', cache_v').
+    """
+    q = np.asarray(q, dtype=np.float64)
+    ck = np.vstack([np.asarray(cache_k, dtype=np.float64).reshape(-1, q.shape[0]),
+                    np.asarray(k, dtype=np.float64)[None]])
+    cv = np.vstack([np.asarray(cache_v, dtype=np.float64).reshape(-1, np.asarray(v).shape[0]),
+                    np.asarray(v, dtype=np.float64)[None]])
+    s = scale * (ck @ q)
+    w = np.exp(s - s.max())
+    a_dot = (w @ cv) / w.sum()
+    a_mem = memory_retrieval(q[None], M, z, eps)[0]
+    return gate(a_mem, a_dot, beta), ck, cv
+
+
+def decode_stream(Q, K, V, beta, segment_len, update=LINEAR, eps=1e-6, scale=None, M0=None, z0=None,
+                  flush=True):
+    """A stream fed one token at a time through ``decode_token``.
+
+    The memory is written (Eq. 8 / Eq. 9 over the cached segment, ``advance``) when the
+    cache holds segment_len tokens, and, with ``flush``, once more for a partial last
+    segment.  Q, K, V: [B, H, L, d].  Returns (O [B, H, L, d], M, z, open_tokens), where
+    open_tokens is the number of cached tokens not yet written to the memory.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, L, d = Q.shape
+    dv = V.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    beta = np.asarray(beta, dtype=np.float64).reshape(H)
+    M = np.zeros((B, H, d, dv)) if M0 is None else np.array(M0, dtype=np.float64)
+    z = np.zeros((B, H, d)) if z0 is None else np.array(z0, dtype=np.float64)
+    O = np.empty((B, H, L, dv))
+    open_tokens = 0
+    for b in range(B):
+        for h in range(H):
+            ck, cv = np.zeros((0, d)), np.zeros((0, dv))
+            for t in range(L):
+                O[b, h, t], ck, cv = decode_token(Q[b, h, t], K[b, h, t], V[b, h, t], ck, cv, M[b, h], z[b, h],
+                                                  beta[h], eps, scale)
+                if ck.shape[0] == segment_len:
+                    M[b, h], z[b, h] = advance(ck, cv, M[b, h], z[b, h], update, eps)
+                    ck, cv = np.zeros((0, d)), np.zeros((0, dv))
+            if flush and ck.shape[0] > 0:
+                M[b, h], z[b, h] = advance(ck, cv, M[b, h], z[b, h], update, eps)
+                ck = np.zeros((0, d))
+            open_tokens = ck.shape[0]
+    return O, M, z, open_tokens

@@ -110,6 +110,20 @@ def _round_truncates(x):
     return np.ldexp(np.trunc(m * 256.0), e - 8)
 
 
+def _decode_excludes_current_token(q, k, v, cache_k, cache_v, M, z, beta, eps, scale):
+    a, ck, cv = orc.__dict__["_orig_decode_token"](q, k, v, cache_k, cache_v, M, z, beta, eps, scale)
+    if np.asarray(cache_k).size == 0:
+        return a, ck, cv
+    a2, _, _ = orc.__dict__["_orig_decode_token"](q, np.asarray(cache_k)[-1], np.asarray(cache_v)[-1],
+                                                   np.asarray(cache_k)[:-1], np.asarray(cache_v)[:-1],
+                                                   M, z, beta, eps, scale)
+    return a2, ck, cv
+
+
+def _decode_unscaled(q, k, v, cache_k, cache_v, M, z, beta, eps, scale):
+    return orc.__dict__["_orig_decode_token"](q, k, v, cache_k, cache_v, M, z, beta, eps, 1.0)
+
+
 def _elu_without_one(x):
     x = np.asarray(x, dtype=np.float64)
     return np.where(x > 0, x, np.expm1(np.minimum(x, 0.0)))
@@ -134,6 +148,8 @@ MUTANTS = {
     "qkv-projection-k-v-swapped": ("project_qkv", _project_qkv_k_v_swapped),
     "qkv-projection-heads-interleaved": ("project_qkv", _project_qkv_head_interleaved),
     "bf16-rounding-truncates": ("round_to_bf16", _round_truncates),
+    "decode-excludes-current-token": ("decode_token", _decode_excludes_current_token),
+    "decode-unscaled-scores": ("decode_token", _decode_unscaled),
 }
 
 
@@ -160,6 +176,7 @@ def _all_pins(rng):
     yield lambda: pins.test_qkv_projection_per_head_columns(rng)
     for u in ("linear", "delta"):
         yield lambda u=u: pins.test_layer_with_projections_matches_scalar_loops(rng, u)
+        yield lambda u=u: pins.test_token_by_token_decoding_equals_the_segment_forward(rng, u)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -168,6 +185,7 @@ def test_a_planted_mistake_fails_a_pin(monkeypatch, name):
     monkeypatch.setitem(orc.__dict__, "_orig_attention", orc.local_causal_attention)
     monkeypatch.setitem(orc.__dict__, "_orig_segment_forward", orc.segment_forward)
     monkeypatch.setitem(orc.__dict__, "_orig_project_qkv", orc.project_qkv)
+    monkeypatch.setitem(orc.__dict__, "_orig_decode_token", orc.decode_token)
     monkeypatch.setattr(orc, attr, fn)
     rng = np.random.default_rng(99)
     caught = []

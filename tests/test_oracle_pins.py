@@ -446,3 +446,33 @@ def test_layer_is_linear_in_the_output_weights(rng):
     O2, _, _ = orc.layer_forward(X, w_qkv, w2, [0.1, 0.2], N, H, d)
     O3, _, _ = orc.layer_forward(X, w_qkv, w1 - 3 * w2, [0.1, 0.2], N, H, d)
     np.testing.assert_allclose(O3, O1 - 3 * O2, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- incremental decoding
+# Tokens fed one at a time (the summary's "fast streaming inference"): a per-token softmax
+# over the segment's cache and a memory written when the segment closes must give the
+# segment formulation's outputs and states exactly (causality inside the segment).
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_token_by_token_decoding_equals_the_segment_forward(rng, update):
+    B, H, L, N, d = 2, 2, 23, 8, 5   # two closed segments and a partial one
+    Q, K, V = _rand_qkv(rng, B, H, L, d, scale=1.5)
+    beta = [0.6, -0.8]
+    O, M, z = orc.forward(Q, K, V, beta, N, update)
+    O2, M2, z2, open_tokens = orc.decode_stream(Q, K, V, beta, N, update)
+    assert open_tokens == 0
+    np.testing.assert_allclose(O2, O, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(M2, M, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(z2, z, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_decoding_leaves_an_open_segment_out_of_the_memory(rng, update):
+    B, H, L, N, d = 1, 2, 19, 8, 4
+    Q, K, V = _rand_qkv(rng, B, H, L, d)
+    beta = [0.2, 0.9]
+    _, M, z, open_tokens = orc.decode_stream(Q, K, V, beta, N, update, flush=False)
+    assert open_tokens == L % N
+    _, M_ref, z_ref = orc.forward(Q[:, :, :16], K[:, :, :16], V[:, :, :16], beta, N, update)
+    np.testing.assert_allclose(M, M_ref, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(z, z_ref, rtol=1e-13, atol=0)
