@@ -39,7 +39,7 @@ class Config(ctypes.Structure):
     ]
 
 
-KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention", "proj_qkv", "proj_out")
+KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention", "proj_qkv", "proj_out", "decode")
 
 
 class Profile(ctypes.Structure):
@@ -83,6 +83,9 @@ def load() -> ctypes.CDLL:
         "infini_attn_project_qkv": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_project_out": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_forward_layer": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i32, vp]),
+        "infini_attn_decode_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp]),
+        "infini_attn_decode_flush": (ctypes.c_int, [vp, vp]),
+        "infini_attn_decode_position": (i64, [vp]),
         "infini_attn_reset_state": (ctypes.c_int, [vp, vp]),
         "infini_attn_get_state": (ctypes.c_int, [vp, vp, vp, vp]),
         "infini_attn_set_state": (ctypes.c_int, [vp, vp, vp, vp]),
@@ -257,6 +260,22 @@ class InfiniAttention:
                                                  _stream_ptr(stream))
         _check("infini_attn_forward_layer", st)
         return out
+
+    # ------------------------------------------------------------------ decoding
+    def decode_step(self, q, k, v, out=None, stream=None):
+        """One token per sequence: q, k, v [B, H, d] (or [B, H, 1, d]) -> out of the same shape."""
+        self._check_io(q, k, v, out)
+        if out is None:
+            out = torch.empty_like(q)
+        st = self._lib.infini_attn_decode_step(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream_ptr(stream))
+        _check("infini_attn_decode_step", st)
+        return out
+
+    def decode_flush(self, stream=None) -> None:
+        _check("infini_attn_decode_flush", self._lib.infini_attn_decode_flush(self._h, _stream_ptr(stream)))
+
+    def decode_position(self) -> int:
+        return int(self._lib.infini_attn_decode_position(self._h))
 
     # ------------------------------------------------------------------ state
     def reset_state(self, stream=None) -> None:

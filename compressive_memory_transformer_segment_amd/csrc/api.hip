@@ -35,6 +35,8 @@ struct infini_attn {
   size_t ws_bytes;
   void* layer_buf = nullptr;   // forward_layer: Q, K, V, A of one window (bf16)
   size_t layer_bytes = 0;
+  void* dec_cache = nullptr;   // decoding: K then V cache of the open segment, [B,H,N,D] each
+  int dec_p = 0;               // tokens of the open decode segment (0: none open)
   infini::Workspace ws;
   // per-kernel event timing (measurement only)
   bool profiling = false;
@@ -217,6 +219,7 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
                float* a_dot, int64_t n_tokens, void* hip_stream, const void* q_loc = nullptr,
                const void* k_loc = nullptr) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  if (h->dec_p > 0) return INFINI_ERR_INVALID_ARG;   // a decode segment is open: flush it first
   int rc = check_io(h, q, k, v, out, n_tokens);
   if (rc) return rc;
   if (!q_loc) q_loc = q;
@@ -450,6 +453,7 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   (void)hipFree(h->gate);
   (void)hipFree(h->ws_base);
   if (h->layer_buf) (void)hipFree(h->layer_buf);
+  if (h->dec_cache) (void)hipFree(h->dec_cache);
   delete h;
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
@@ -481,6 +485,7 @@ INFINI_EXPORT int infini_attn_forward_segment(infini_attn_t h, const void* q, co
 INFINI_EXPORT int infini_attn_reset_state(infini_attn_t h, void* hip_stream) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   (void)hip_stream;
+  h->dec_p = 0;   // an open decode segment is dropped
   // No device work: the next call that reads the state treats it as zero (the chain and
   // the state pass of its first window read 0 instead of M and z); get_state and
   // set_state write the zeros out first.
@@ -538,7 +543,8 @@ INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   const int64_t DD = int64_t(h->D) * h->D;
   return int64_t(h->BH) * DD * 4 + int64_t(h->BH) * h->D * 4 + int64_t(2) * h->cfg.heads * 4 +
-         static_cast<int64_t>(h->ws_bytes) + static_cast<int64_t>(h->layer_bytes);
+         static_cast<int64_t>(h->ws_bytes) + static_cast<int64_t>(h->layer_bytes) +
+         (h->dec_cache ? int64_t(2) * h->BH * h->N * h->D * (h->bf16 ? 2 : 4) : 0);
 }
 
 INFINI_EXPORT int64_t infini_attn_window_tokens(infini_attn_t h) {
@@ -620,6 +626,7 @@ INFINI_EXPORT int infini_attn_forward_layer(infini_attn_t h, const void* x, cons
                                             void* out, int64_t n_tokens, int32_t d_model, void* hip_stream) {
   int rc = check_layer(h, n_tokens, d_model);
   if (rc) return rc;
+  if (h->dec_p > 0) return INFINI_ERR_INVALID_ARG;
   if (!x || !w_qkv || !w_o || !out) return INFINI_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(w_o, 16) || !aligned(out, 8)) return INFINI_ERR_INVALID_ARG;
   const size_t HD = size_t(h->cfg.heads) * h->D;
@@ -662,4 +669,118 @@ INFINI_EXPORT int infini_attn_forward_layer(infini_attn_t h, const void* x, cons
     if (e != hipSuccess) return INFINI_ERR_HIP;
   }
   return INFINI_OK;
+}
+
+// ---- incremental decoding ------------------------------------------------------------
+
+namespace {
+
+// Writes the open decode segment (its n cached tokens) into M, z: the state pass and the
+// chain of forward_stream over the cache as a one-segment window.
+int close_decode_segment(infini_attn* h, int n, hipStream_t st) {
+  const size_t es = h->bf16 ? 2 : 4;
+  const char* kc = static_cast<const char*>(h->dec_cache);
+  const char* vc = kc + size_t(h->BH) * h->N * h->D * es;
+  infini::WindowArgs a{};
+  a.q = kc;   // not read by the memory-write kernels
+  a.k = kc;
+  a.v = vc;
+  a.q_loc = kc;
+  a.k_loc = kc;
+  a.B = h->cfg.batch;
+  a.H = h->cfg.heads;
+  a.D = h->D;
+  a.T = h->N;   // the cache's row stride: N rows per (b, h)
+  a.N = h->N;
+  a.S = 1;
+  a.n_last = n;
+  a.s0 = 0;
+  a.W = 1;
+  a.delta = h->delta;
+  a.bf16 = h->bf16;
+  a.eps = h->cfg.eps;
+  a.scale = h->scale;
+  a.scale_log2 = static_cast<float>(double(h->scale) * 1.4426950408889634);
+  a.gate_g = h->gate;
+  a.gate_omg = h->gate + h->cfg.heads;
+  a.M = h->M;
+  a.z = h->z;
+  a.ws = h->ws;
+  a.zero_state = h->state_zero;
+  a.chk = chunks_for(*h, 1);
+  a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
+  hipError_t e = hipSuccess;
+  if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
+  if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
+  if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+  if (e != hipSuccess) return INFINI_ERR_HIP;
+  h->state_zero = false;
+  return INFINI_OK;
+}
+
+}  // namespace
+
+INFINI_EXPORT int infini_attn_decode_step(infini_attn_t h, const void* q, const void* k, const void* v, void* out,
+                                          void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return INFINI_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v})
+    if (!aligned(p, 16)) return INFINI_ERR_INVALID_ARG;
+  const size_t es = h->bf16 ? 2 : 4;
+  if (!aligned(out, es)) return INFINI_ERR_INVALID_ARG;
+  const size_t tok_bytes = size_t(h->BH) * h->D * es;
+  for (const void* p : {q, k, v})
+    if (overlaps(out, tok_bytes, p, tok_bytes)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (!h->dec_cache) {
+    if (hipMalloc(&h->dec_cache, 2 * size_t(h->BH) * h->N * h->D * es) != hipSuccess) {
+      (void)hipGetLastError();
+      h->dec_cache = nullptr;
+      return INFINI_ERR_OOM;
+    }
+  }
+  infini::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.kc = h->dec_cache;
+  a.vc = static_cast<char*>(h->dec_cache) + size_t(h->BH) * h->N * h->D * es;
+  a.M = h->M;
+  a.z = h->z;
+  a.gate_g = h->gate;
+  a.gate_omg = h->gate + h->cfg.heads;
+  a.B = h->cfg.batch;
+  a.H = h->cfg.heads;
+  a.D = h->D;
+  a.N = h->N;
+  a.p = h->dec_p;
+  a.bf16 = h->bf16;
+  a.zero_state = h->state_zero;
+  a.scale_log2 = static_cast<float>(double(h->scale) * 1.4426950408889634);
+  a.eps = h->cfg.eps;
+  const hipError_t e = timed(h, 6, st, [&] { return infini::launch_decode(a, st); });
+  if (e != hipSuccess) return INFINI_ERR_HIP;
+  if (++h->dec_p == h->N) {   // the segment is complete: write it to the memory
+    h->dec_p = 0;
+    return close_decode_segment(h, h->N, st);
+  }
+  return INFINI_OK;
+}
+
+INFINI_EXPORT int infini_attn_decode_flush(infini_attn_t h, void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  if (h->dec_p == 0) return INFINI_OK;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  const int n = h->dec_p;
+  h->dec_p = 0;
+  return close_decode_segment(h, n, static_cast<hipStream_t>(hip_stream));
+}
+
+INFINI_EXPORT int64_t infini_attn_decode_position(infini_attn_t h) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  return h->dec_p;
 }

@@ -1,0 +1,200 @@
+// Incremental decoding of the Infini-attention layer: one new token per (batch element,
+// head) per launch, inside the current segment (the architecture summary of
+// arXiv 2404.07143, section 1 on streaming inference and section 3.4's segment-wise
+// recurrence, Eq. 4).  For the token at position p of segment s:
+//
+//   A_dot = softmax(scale * q [K_s[0..p]]^T) V_s[0..p]            (Eq. 6, its row p)
+//   A_mem = sigma(q) M_{s-1} / (sigma(q) z_{s-1} + eps)            (Eq. 7)
+//   out   = sigmoid(beta_h) A_mem + (1 - sigmoid(beta_h)) A_dot     (Eq. 10)
+//
+// and the token's key and value are appended to the segment's cache.  The memory is
+// written (Eq. 8 / 9) by the state-pass and chain kernels over the cache when the segment
+// closes; this kernel only reads M_{s-1}, z_{s-1}.
+//
+// The work is a read of the segment's cached keys and values (p rows of d each) and of
+// M_{s-1}: bound by HBM bandwidth.  One workgroup (4 waves) per (batch, head): d/8 lanes
+// share a key (8 values per lane, one 16-byte load for bf16), so one wave-wide load covers
+// 64/(d/8) keys and is fully coalesced; every lane group keeps its own online-softmax
+// state (exp2 domain, scale folded into q) over a strided subset of the keys, 8 rounds of
+// loads in flight, and the partial states are merged through LDS.  The retrieval reads
+// the fp32 M_{s-1} row by row with 16-byte loads, in parallel with the key loop's loads.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infini {
+
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kRounds = 8;   // rounds of key loads in flight per lane
+
+// 8 consecutive elements as float, from bf16 (one 16-byte load) or f32 (two).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, float (&x)[8]) {
+  if constexpr (BF16) {
+    const u32x4 w = ld16(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16lo_to_f32(w[i]);
+      x[2 * i + 1] = bf16hi_to_f32(w[i]);
+    }
+  } else {
+    const u32x4 w0 = ld16(p), w1 = ld16(static_cast<const float*>(p) + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __uint_as_float(w0[i]);
+      x[4 + i] = __uint_as_float(w1[i]);
+    }
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
+  using T = std::conditional_t<BF16, uint16_t, float>;
+  constexpr int LPK = D / 8;           // lanes per key
+  constexpr int KPW = 64 / LPK;        // keys per wave per round
+  constexpr int NG = 4 * KPW;          // lane groups (keys per round) in the workgroup
+  constexpr int RS = kDecThreads * 4 / D;   // row slices of the retrieval (4 columns per thread)
+  __shared__ float part_m[NG], part_l[NG];
+  __shared__ __align__(16) float part_acc[NG][D];
+  __shared__ __align__(16) float sq[D];        // sigma(q)
+  __shared__ __align__(16) float red[RS][D];   // retrieval partial sums
+  __shared__ float zden[4];
+
+  const int bh = static_cast<int>(blockIdx.x), h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave * KPW + lane / LPK;   // lane group: keys grp, grp + NG, ...
+  const int e = lane % LPK;                  // values 8e .. 8e + 7 of each key
+  const T* qg = static_cast<const T*>(a.q) + static_cast<int64_t>(bh) * D;
+  const T* kg = static_cast<const T*>(a.k) + static_cast<int64_t>(bh) * D;
+  const T* vg = static_cast<const T*>(a.v) + static_cast<int64_t>(bh) * D;
+  T* kc = static_cast<T*>(a.kc) + static_cast<int64_t>(bh) * a.N * D;
+  T* vc = static_cast<T*>(a.vc) + static_cast<int64_t>(bh) * a.N * D;
+
+  // append the token to the cache (read back by later launches only) and form sigma(q)
+  if (tid < D) {
+    kc[static_cast<int64_t>(a.p) * D + tid] = kg[tid];
+    vc[static_cast<int64_t>(a.p) * D + tid] = vg[tid];
+    float qf;
+    if constexpr (BF16) qf = bf16_to_f32(qg[tid]);
+    else qf = qg[tid];
+    sq[tid] = elu_plus_one(qf);
+  }
+
+  // ---- retrieval partial sums: thread (slice, column quad) over D / RS rows of M_{s-1}
+  const int cq = tid % (D / 4), slice = tid / (D / 4);
+  constexpr int RPS = D / RS;   // rows per slice
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();   // sq
+  if (!a.zero_state) {
+    const float* Mb = a.M + static_cast<int64_t>(bh) * D * D + 4 * cq;
+#pragma unroll 8
+    for (int r = 0; r < RPS; ++r) {
+      const int i = slice * RPS + r;
+      const u32x4 w = ld16(Mb + static_cast<int64_t>(i) * D);
+      const float s = sq[i];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = fmaf(s, __uint_as_float(w[c]), num[c]);
+    }
+    if (wave == 0) {   // sigma(q) . z_{s-1}
+      float zs = 0.f;
+      for (int i = lane; i < D; i += 64) zs = fmaf(sq[i], a.z[static_cast<int64_t>(bh) * D + i], zs);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) zs += __shfl_xor(zs, off);
+      if (lane == 0) zden[0] = zs;
+    }
+  } else if (tid == 0) {
+    zden[0] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) red[slice][4 * cq + c] = num[c];
+
+  // ---- local attention over keys 0 .. p (key p is this token, from the inputs)
+  float qv[8];
+  load8<BF16>(qg + 8 * e, qv);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] *= a.scale_log2;
+  const int nk = a.p + 1;
+  float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int r0 = 0; r0 < nk; r0 += NG * kRounds) {
+    float kk[kRounds][8], vv[kRounds][8];
+#pragma unroll
+    for (int u = 0; u < kRounds; ++u) {
+      const int t = r0 + u * NG + grp;
+      const T* kr = t < a.p ? kc + static_cast<int64_t>(t) * D : kg;   // past the end: any valid row
+      const T* vr = t < a.p ? vc + static_cast<int64_t>(t) * D : vg;
+      load8<BF16>(kr + 8 * e, kk[u]);
+      load8<BF16>(vr + 8 * e, vv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRounds; ++u) {
+      const int t = r0 + u * NG + grp;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kk[u][i], s);
+#pragma unroll
+      for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (t < nk) {   // uniform across the lane group
+        const float m_new = fmaxf(m, s);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // m = -inf on the first key: 0
+        const float pw = __builtin_amdgcn_exp2f(s - m_new);
+        l = fmaf(l, alpha, pw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(acc[i], alpha, pw * vv[u][i]);
+        m = m_new;
+      }
+    }
+  }
+  if (e == 0) {
+    part_m[grp] = m;
+    part_l[grp] = l;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part_acc[grp][8 * e + i] = acc[i];
+  __syncthreads();
+
+  // ---- merge the lane groups, gate, store
+  if (tid < D) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) mx = fmaxf(mx, part_m[g]);   // finite: group 0 holds key 0
+    float nd = 0.f, dd = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float w = __builtin_amdgcn_exp2f(part_m[g] - mx);   // empty group: exp2(-inf) = 0
+      nd = fmaf(w, part_acc[g][tid], nd);
+      dd = fmaf(w, part_l[g], dd);
+    }
+    const float a_dot = nd / dd;
+    float nm = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < RS; ++sl) nm += red[sl][tid];
+    const float a_mem = nm / (zden[0] + a.eps);
+    const float o = a.gate_g[h] * a_mem + a.gate_omg[h] * a_dot;
+    T* og = static_cast<T*>(a.out) + static_cast<int64_t>(bh) * D;
+    if constexpr (BF16) og[tid] = f32_to_bf16(o);
+    else og[tid] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kDecThreads);
+  if (a.D == 128) {
+    if (a.bf16) hipLaunchKernelGGL((k_decode<128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_decode<128, false>), grid, block, 0, st, a);
+  } else if (a.D == 64) {
+    if (a.bf16) hipLaunchKernelGGL((k_decode<64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_decode<64, false>), grid, block, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace infini

@@ -71,6 +71,28 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
+// One decoding step: one token per (batch, head) inside the current segment.
+struct DecodeArgs {
+  const void* q;          // [B, H, D] this token (io dtype)
+  const void* k;
+  const void* v;
+  void* out;              // [B, H, D]
+  void* kc;               // [B, H, N, D] the segment's cached keys; this token goes to row p
+  void* vc;
+  const float* M;         // [B, H, D, D] M_{s-1}
+  const float* z;         // [B, H, D]    z_{s-1}
+  const float* gate_g;    // [H]
+  const float* gate_omg;  // [H]
+  int B, H, D, N;
+  int p;                  // tokens of the segment already cached
+  bool bf16;
+  bool zero_state;        // M_{s-1}, z_{s-1} are zero (read as 0)
+  float scale_log2;
+  float eps;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
 hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
 hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T
 hipError_t launch_chain(const WindowArgs& a, hipStream_t st);          // M/z recurrence

@@ -127,8 +127,8 @@ int infini_attn_set_state(infini_attn_t h, const float* M, const float* z, void*
 int infini_attn_set_beta(infini_attn_t h, const float* beta_host);
 
 /* Device bytes the handle holds: state + gate values + workspace, plus the layer scratch
- * once forward_layer has run (at most one window's worth).  Independent of how many
- * tokens have been processed. */
+ * once forward_layer has run (at most one window's worth) and the decode cache once
+ * decode_step has run (one segment).  Independent of how many tokens have been processed. */
 int64_t infini_attn_device_bytes(infini_attn_t h);
 
 /* Tokens per internal window of forward_stream (window segments * N). */
@@ -167,14 +167,41 @@ int infini_attn_project_out(infini_attn_t h, const void* a, const void* w_o, voi
 int infini_attn_forward_layer(infini_attn_t h, const void* x, const void* w_qkv, const void* w_o,
                               void* out, int64_t n_tokens, int32_t d_model, void* hip_stream);
 
+/* ---- Incremental decoding (one token per sequence per call) ------------------------------
+ *
+ * Streaming generation inside a segment (the summary's "fast streaming inference", with
+ * the segment-wise recurrence of Eq. 4): the handle keeps the open segment's keys and
+ * values (a cache of at most N tokens per (b, h), library-owned, allocated on the first
+ * decode_step: 2 * B * H * N * d elements of io_dtype) next to M, z.  For each token the
+ * output is, per (b, h), row p of the segment computation: the local softmax attention
+ * (Eq. 6) over the segment's tokens 0 .. p (the cached ones and this one), the memory read
+ * (Eq. 7) from the state before the segment, gated by Eq. 10.  When the N-th token of the
+ * segment has been processed the segment is written to the memory (Eq. 8 / 9) and the next
+ * call starts a new segment.  Feeding a stream token by token therefore gives the outputs
+ * of forward_stream on the same stream, and, once the last segment is complete or
+ * flushed, the same state.
+ *
+ * decode_step: q, k, v, out are [B, H, d] (this token of every sequence), io_dtype; q, k,
+ *   v 16-byte aligned; out must not overlap them.
+ * decode_flush: writes an open partial segment to the memory (as forward_stream does with a
+ *   short last segment); no-op when none is open.
+ * decode_position: tokens of the open segment (0 .. N-1).
+ * While a segment is open, forward_segment / forward_stream* / forward_layer return
+ * INFINI_ERR_INVALID_ARG (flush first); reset_state drops the open segment; get_state
+ * returns the state before it; set_state replaces the state its remaining tokens read. */
+int infini_attn_decode_step(infini_attn_t h, const void* q, const void* k, const void* v, void* out,
+                            void* hip_stream);
+int infini_attn_decode_flush(infini_attn_t h, void* hip_stream);
+int64_t infini_attn_decode_position(infini_attn_t h);
+
 /* Per-kernel timing with HIP events, for measurement.  While enabled, every kernel the
  * handle launches is bracketed by two events on the call's stream.  profile_read waits
  * for the recorded events, reports the summed durations per kernel kind, and clears the
  * record.  Kernel kinds: 0 = key sums (delta rule only), 1 = state pass (per-segment
  * sigma(K)^T V, key sums, delta Gram term, V transpose), 2 = memory chain (Eq. 8/9
  * recurrence), 3 = fused local attention + retrieval + gate (Eq. 6, 7, 10),
- * 4 = Q/K/V projection (Eq. 5), 5 = output projection (Eq. 11). */
-#define INFINI_KERNEL_KINDS 6
+ * 4 = Q/K/V projection (Eq. 5), 5 = output projection (Eq. 11), 6 = decoding step. */
+#define INFINI_KERNEL_KINDS 7
 typedef struct {
   double total_ms[INFINI_KERNEL_KINDS];
   int64_t launches[INFINI_KERNEL_KINDS];

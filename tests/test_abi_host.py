@@ -17,6 +17,7 @@ EXPECTED = {
     "infini_attn_window_tokens", "infini_attn_destroy", "infini_attn_status_string",
     "infini_attn_profile_enable", "infini_attn_profile_read",
     "infini_attn_project_qkv", "infini_attn_project_out", "infini_attn_forward_layer",
+    "infini_attn_decode_step", "infini_attn_decode_flush", "infini_attn_decode_position",
 }
 
 
@@ -93,3 +94,6 @@ def test_calls_on_a_missing_handle_fail_cleanly(lib):
         assert lib.infini_attn_project_qkv(h, p, p, p, p, p, 16, 64, None) == -1
         assert lib.infini_attn_project_out(h, p, p, p, 16, 64, None) == -1
         assert lib.infini_attn_forward_layer(h, p, p, p, p, 16, 64, None) == -1
+        assert lib.infini_attn_decode_step(h, p, p, p, p, None) == -1
+        assert lib.infini_attn_decode_flush(h, None) == -1
+        assert lib.infini_attn_decode_position(h) == -1
