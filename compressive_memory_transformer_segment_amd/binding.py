@@ -39,7 +39,7 @@ class Config(ctypes.Structure):
     ]
 
 
-KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention", "proj_qkv", "proj_out", "decode")
+KERNEL_KINDS = ("key_sums", "state_pass", "chain", "attention", "proj_qkv", "proj_out", "decode", "backward")
 
 
 class Profile(ctypes.Structure):
@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
         "infini_attn_project_out": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_forward_layer": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_decode_step": (ctypes.c_int, [vp, vp, vp, vp, vp, vp]),
+        "infini_attn_backward": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_decode_flush": (ctypes.c_int, [vp, vp]),
         "infini_attn_decode_position": (i64, [vp]),
         "infini_attn_reset_state": (ctypes.c_int, [vp, vp]),
@@ -276,6 +277,29 @@ class InfiniAttention:
 
     def decode_position(self) -> int:
         return int(self._lib.infini_attn_decode_position(self._h))
+
+    # ------------------------------------------------------------------ backward
+    def backward(self, q, k, v, d_out, m0=None, z0=None, dm_final=None, dz_final=None, want_state_grads=True,
+                 stream=None):
+        """Gradients of <d_out, O> (+ <dm_final, M_final> + <dz_final, z_final>) for the stream
+        q, k, v [B, H, T, d] started from (m0, z0) (zeros when None).  Returns a dict of float32
+        tensors dq, dk, dv, dbeta and, with want_state_grads, dm0, dz0."""
+        self._check_io(q, k, v, d_out)
+        f32 = lambda t: None if t is None else t.to(device="cuda", dtype=torch.float32).contiguous()   # noqa: E731
+        m0, z0, dm_final, dz_final = f32(m0), f32(z0), f32(dm_final), f32(dz_final)
+        B, H, T, d = q.shape
+        res = {n: torch.empty((B, H, T, d), dtype=torch.float32, device=q.device) for n in ("dq", "dk", "dv")}
+        res["dbeta"] = torch.empty((H,), dtype=torch.float32, device=q.device)
+        if want_state_grads:
+            res["dm0"] = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+            res["dz0"] = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+        opt = lambda t: _ptr(t) if t is not None else None   # noqa: E731
+        st = self._lib.infini_attn_backward(
+            self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(d_out), opt(m0), opt(z0), opt(dm_final), opt(dz_final),
+            _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dbeta"]), opt(res.get("dm0")),
+            opt(res.get("dz0")), T, _stream_ptr(stream))
+        _check("infini_attn_backward", st)
+        return res
 
     # ------------------------------------------------------------------ state
     def reset_state(self, stream=None) -> None:

@@ -35,6 +35,8 @@ struct infini_attn {
   size_t ws_bytes;
   void* layer_buf = nullptr;   // forward_layer: Q, K, V, A of one window (bf16)
   size_t layer_bytes = 0;
+  void* bwd_buf = nullptr;     // backward: recomputed forward parts and gradient scratch
+  size_t bwd_bytes = 0;
   void* dec_cache = nullptr;   // decoding: K then V cache of the open segment, [B,H,N,D] each
   int dec_p = 0;               // tokens of the open decode segment (0: none open)
   infini::Workspace ws;
@@ -454,6 +456,7 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   (void)hipFree(h->ws_base);
   if (h->layer_buf) (void)hipFree(h->layer_buf);
   if (h->dec_cache) (void)hipFree(h->dec_cache);
+  if (h->bwd_buf) (void)hipFree(h->bwd_buf);
   delete h;
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
@@ -544,7 +547,8 @@ INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
   const int64_t DD = int64_t(h->D) * h->D;
   return int64_t(h->BH) * DD * 4 + int64_t(h->BH) * h->D * 4 + int64_t(2) * h->cfg.heads * 4 +
          static_cast<int64_t>(h->ws_bytes) + static_cast<int64_t>(h->layer_bytes) +
-         (h->dec_cache ? int64_t(2) * h->BH * h->N * h->D * (h->bf16 ? 2 : 4) : 0);
+         (h->dec_cache ? int64_t(2) * h->BH * h->N * h->D * (h->bf16 ? 2 : 4) : 0) +
+         static_cast<int64_t>(h->bwd_bytes);
 }
 
 INFINI_EXPORT int64_t infini_attn_window_tokens(infini_attn_t h) {
@@ -783,4 +787,159 @@ INFINI_EXPORT int infini_attn_decode_flush(infini_attn_t h, void* hip_stream) {
 INFINI_EXPORT int64_t infini_attn_decode_position(infini_attn_t h) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   return h->dec_p;
+}
+
+// ---- backward --------------------------------------------------------------------------
+
+INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const void* k, const void* v,
+                                       const void* d_out, const float* m0, const float* z0,
+                                       const float* dm_final, const float* dz_final, float* dq, float* dk,
+                                       float* dv, float* dbeta, float* dm0, float* dz0, int64_t n_tokens,
+                                       void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  if (h->dec_p > 0) return INFINI_ERR_INVALID_ARG;
+  int rc = check_io(h, q, k, v, d_out, n_tokens);
+  if (rc) return rc;
+  if (!dq || !dk || !dv || !dbeta) return INFINI_ERR_INVALID_ARG;
+  if ((m0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_INVALID_ARG;
+  const int64_t S64 = (n_tokens + h->N - 1) / h->N;
+  if (S64 > h->window) return INFINI_ERR_UNSUPPORTED;   // the whole call must fit one window
+  for (const void* p : {static_cast<const void*>(m0), static_cast<const void*>(z0),
+                        static_cast<const void*>(dm_final), static_cast<const void*>(dz_final),
+                        static_cast<const void*>(dq), static_cast<const void*>(dk), static_cast<const void*>(dv),
+                        static_cast<const void*>(dbeta), static_cast<const void*>(dm0),
+                        static_cast<const void*>(dz0)})
+    if (!aligned(p, 4)) return INFINI_ERR_INVALID_ARG;
+  const size_t es = h->bf16 ? 2 : 4;
+  const size_t io_bytes = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * es;
+  const size_t g_bytes = size_t(h->BH) * size_t(n_tokens) * size_t(h->D) * 4;
+  for (const float* out : {dq, dk, dv})
+    for (const void* in : {q, k, v, d_out})
+      if (overlaps(out, g_bytes, in, io_bytes)) return INFINI_ERR_INVALID_ARG;
+  if (overlaps(dq, g_bytes, dk, g_bytes) || overlaps(dq, g_bytes, dv, g_bytes) || overlaps(dk, g_bytes, dv, g_bytes))
+    return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+  const int S = static_cast<int>(S64);
+  const int64_t U = int64_t(S) * h->BH;
+  const int D = h->D;
+  const int pt = (h->N + 63) / 64;
+  int rch = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (512 + U - 1) / U)));
+  const size_t rows = size_t(h->BH) * size_t(n_tokens);
+  // scratch layout (256-byte aligned pieces)
+  const size_t sz[] = {
+      rows * D * es,                      // 0 forward output
+      rows * D * 4,                       // 1 A_mem
+      rows * D * 4,                       // 2 A_dot
+      rows * 4, rows * 4, rows * 4, rows * 4,   // 3-6 lse, dd, den, dden
+      size_t(U) * rch * D * D * 4,        // 7 rpart
+      size_t(U) * rch * D * 4,            // 8 rzpart
+      size_t(U) * D * D * 4,              // 9 gm
+      size_t(U) * pt * D * 4,             // 10 cpart
+      size_t(U) * D * 4,                  // 11 gz
+      size_t(U) * pt * 4,                 // 12 bpart
+      size_t(h->BH) * D * D * 4,          // 13 state copy M
+      size_t(h->BH) * D * 4,              // 14 state copy z
+  };
+  constexpr int NP = sizeof(sz) / sizeof(sz[0]);
+  size_t total = 0;
+  for (size_t x : sz) total += align_up(x, 256);
+  if (h->bwd_bytes < total) {
+    if (h->bwd_buf) {
+      if (hipStreamSynchronize(st) != hipSuccess) return INFINI_ERR_HIP;
+      (void)hipFree(h->bwd_buf);
+      h->bwd_buf = nullptr;
+      h->bwd_bytes = 0;
+    }
+    if (hipMalloc(&h->bwd_buf, total) != hipSuccess) {
+      (void)hipGetLastError();
+      h->bwd_buf = nullptr;
+      return INFINI_ERR_OOM;
+    }
+    h->bwd_bytes = total;
+  }
+  void* part[NP];
+  {
+    char* p = static_cast<char*>(h->bwd_buf);
+    for (int i = 0; i < NP; ++i) {
+      part[i] = p;
+      p += align_up(sz[i], 256);
+    }
+  }
+  float* Ms = static_cast<float*>(part[13]);
+  float* zs = static_cast<float*>(part[14]);
+  hipError_t e = hipSuccess;
+  if (m0) {
+    e = hipMemcpyAsync(Ms, m0, sz[13], hipMemcpyDefault, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(zs, z0, sz[14], hipMemcpyDefault, st);
+    if (e != hipSuccess) return INFINI_ERR_HIP;
+  }
+
+  // the forward over the call, from (m0, z0) or zero, keeping A_mem, A_dot, lse and the
+  // per-segment states in the workspace; the handle's own state is not touched
+  infini::WindowArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_loc = q;
+  a.k_loc = k;
+  a.out = part[0];
+  a.a_mem = static_cast<float*>(part[1]);
+  a.a_dot = static_cast<float*>(part[2]);
+  a.lse = static_cast<float*>(part[3]);
+  a.B = h->cfg.batch;
+  a.H = h->cfg.heads;
+  a.D = D;
+  a.T = n_tokens;
+  a.N = h->N;
+  a.S = S;
+  a.n_last = static_cast<int>(n_tokens - int64_t(S - 1) * h->N);
+  a.s0 = 0;
+  a.W = S;
+  a.delta = h->delta;
+  a.bf16 = h->bf16;
+  a.eps = h->cfg.eps;
+  a.scale = h->scale;
+  a.scale_log2 = static_cast<float>(double(h->scale) * 1.4426950408889634);
+  a.gate_g = h->gate;
+  a.gate_omg = h->gate + h->cfg.heads;
+  a.M = Ms;
+  a.z = zs;
+  a.ws = h->ws;
+  a.zero_state = (m0 == nullptr);
+  a.chk = chunks_for(*h, S);
+  a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
+  if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
+  if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
+  if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+  if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(a, st); });
+  if (e != hipSuccess) return INFINI_ERR_HIP;
+
+  infini::BackwardArgs bw{};
+  bw.w = a;
+  bw.w.zero_state = false;
+  bw.dout = d_out;
+  bw.dd = static_cast<float*>(part[4]);
+  bw.den = static_cast<float*>(part[5]);
+  bw.dden = static_cast<float*>(part[6]);
+  bw.dq = dq;
+  bw.dk = dk;
+  bw.dv = dv;
+  bw.rpart = static_cast<float*>(part[7]);
+  bw.rzpart = static_cast<float*>(part[8]);
+  bw.gm = static_cast<float*>(part[9]);
+  bw.cpart = static_cast<float*>(part[10]);
+  bw.gz = static_cast<float*>(part[11]);
+  bw.bpart = static_cast<float*>(part[12]);
+  bw.dm_final = dm_final;
+  bw.dz_final = dz_final;
+  bw.dm0 = dm0;
+  bw.dz0 = dz0;
+  bw.dbeta = dbeta;
+  bw.rch = rch;
+  bw.pt = pt;
+  e = timed(h, 7, st, [&] { return infini::launch_backward(bw, st); });
+  return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }

@@ -382,6 +382,9 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   uint16_t* ost = buf_at(nkv + 1 + (wave >> 2)) + (wave & 3) * 32 * D;
   const float l_tot = sum_across_halves(l_part);
   const float inv_l = 1.f / l_tot;
+  if constexpr (PARTS) {
+    if (a.lse && hl == 0 && q < n) a.lse[row0 + q] = m_run + __log2f(l_tot);
+  }
 
   // With a separate local Q the retrieval needs the PE-free Q rows: each wave copies its
   // own 32 rows into its (not yet used) staging region and reads them back, as in the
@@ -558,13 +561,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_attn_f32(const WindowArgs a) 
       if (a.a_dot) a.a_dot[e] = adot;
     }
   }
+  // natural-log softmax state -> the log2 domain of the bf16 path
+  if (a.lse && part == 0 && q < n) a.lse[row0 + q] = (m + __logf(l)) * kLog2e;
 }
 
 template <int D>
 hipError_t launch_attention_d(const WindowArgs& a, hipStream_t st) {
   if (a.bf16) {
     const dim3 grid(a.units() * ((a.N + kBMA - 1) / kBMA));
-    if (a.a_mem || a.a_dot) hipLaunchKernelGGL((k_attn_bf16<D, true>), grid, dim3(kThreadsA), 0, st, a);
+    if (a.a_mem || a.a_dot || a.lse) hipLaunchKernelGGL((k_attn_bf16<D, true>), grid, dim3(kThreadsA), 0, st, a);
     else hipLaunchKernelGGL((k_attn_bf16<D, false>), grid, dim3(kThreadsA), 0, st, a);
   } else {
     const dim3 grid(a.units() * ((a.N + 63) / 64));

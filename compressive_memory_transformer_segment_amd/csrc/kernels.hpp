@@ -25,6 +25,8 @@ struct WindowArgs {
   void* out;
   float* a_mem;      // optional fp32 [B,H,T,D]
   float* a_dot;      // optional fp32 [B,H,T,D]
+  float* lse;        // optional fp32 [B,H,T]: log2 of the softmax row sum, in the scaled
+                     // log2 domain (P = exp2(scale log2e q.k - lse)); written with a_mem / a_dot
   int B, H, D;
   int64_t T;         // tokens in the call
   int N;             // segment length
@@ -92,6 +94,35 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// Backward pass over one window holding the whole call (s0 = 0, W = S): the forward has
+// run on `w` with a_mem, a_dot and lse written, so w.ws holds M_{s-1}^T (mt), z_{s-1} (zb)
+// and, for the delta rule, the Gram partials (g) of every segment.
+struct BackwardArgs {
+  WindowArgs w;
+  const void* dout;      // [B,H,T,D] upstream gradient of the output (io dtype)
+  float* dd;             // [B,H,T] sum_j dO_tj A_dot_tj
+  float* den;            // [B,H,T] sigma(q_t) z_{s-1} + eps
+  float* dden;           // [B,H,T] gradient of the retrieval denominator
+  float* dq;             // [B,H,T,D] fp32 outputs
+  float* dk;
+  float* dv;
+  float* rpart;          // [U][rch][D][D] sigma(Q)^T dnum over chunks of the segment
+  float* rzpart;         // [U][rch][D]    sigma(Q)^T dden
+  float* gm;             // [U][D][D]      dL/dM_s (the state after segment s)
+  float* cpart;          // [U][ut][D]     delta: sigma(K)^T ddenk per token tile
+  float* gz;             // [U][D]         dL/dz_s
+  float* bpart;          // [U * pt]       gate partials
+  const float* dm_final; // optional [B,H,D,D] gradient of the final M
+  const float* dz_final; // optional [B,H,D]
+  float* dm0;            // optional [B,H,D,D] gradient of the initial M
+  float* dz0;            // optional [B,H,D]
+  float* dbeta;          // [H]
+  int rch;               // token chunks of the R pass per segment
+  int pt;                // 64-token tiles per segment (prep, dq, dkv, update, final)
+};
+
+hipError_t launch_backward(const BackwardArgs& b, hipStream_t st);
 
 hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
 hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T

@@ -194,14 +194,36 @@ int infini_attn_decode_step(infini_attn_t h, const void* q, const void* k, const
 int infini_attn_decode_flush(infini_attn_t h, void* hip_stream);
 int64_t infini_attn_decode_position(infini_attn_t h);
 
+/* ---- Backward (training): gradients through the whole stream -----------------------------
+ *
+ * For a call's stream (n_tokens tokens from the initial state (m0, z0); NULL for both means
+ * zero), the gradients of  loss = <d_out, O> + <dm_final, M_final> + <dz_final, z_final>
+ * with respect to Q, K, V, the gate logits beta and the initial state, back through the
+ * M / z recurrence over all the call's segments (backpropagation through time,
+ * "Training Infrastructure for Recurrent Attention"; the forward is recomputed segment by
+ * segment first).  Same readings as the forward (eps in both retrieval denominators, one
+ * beta per head, the delta rule's retrieved value from the state before the segment).
+ *   q, k, v, d_out: [B, H, n_tokens, d] io_dtype (16-byte aligned for bf16);
+ *   m0 [B, H, d, d], z0 [B, H, d], dm_final, dz_final: float32 device pointers or NULL;
+ *   dq, dk, dv: float32 [B, H, n_tokens, d]; dbeta: float32 [H];
+ *   dm0 [B, H, d, d], dz0 [B, H, d]: float32 or NULL (not wanted).
+ * The handle's own state is neither read nor changed.  The call must fit one internal
+ * window (n_tokens <= window_tokens): INFINI_ERR_UNSUPPORTED otherwise.  Device memory for
+ * the recomputed forward and the gradient scratch is library-owned and kept for reuse. */
+int infini_attn_backward(infini_attn_t h, const void* q, const void* k, const void* v, const void* d_out,
+                         const float* m0, const float* z0, const float* dm_final, const float* dz_final,
+                         float* dq, float* dk, float* dv, float* dbeta, float* dm0, float* dz0,
+                         int64_t n_tokens, void* hip_stream);
+
 /* Per-kernel timing with HIP events, for measurement.  While enabled, every kernel the
  * handle launches is bracketed by two events on the call's stream.  profile_read waits
  * for the recorded events, reports the summed durations per kernel kind, and clears the
  * record.  Kernel kinds: 0 = key sums (delta rule only), 1 = state pass (per-segment
  * sigma(K)^T V, key sums, delta Gram term, V transpose), 2 = memory chain (Eq. 8/9
  * recurrence), 3 = fused local attention + retrieval + gate (Eq. 6, 7, 10),
- * 4 = Q/K/V projection (Eq. 5), 5 = output projection (Eq. 11), 6 = decoding step. */
-#define INFINI_KERNEL_KINDS 7
+ * 4 = Q/K/V projection (Eq. 5), 5 = output projection (Eq. 11), 6 = decoding step,
+ * 7 = backward (all gradient kernels of one call; the recomputed forward counts as 0-3). */
+#define INFINI_KERNEL_KINDS 8
 typedef struct {
   double total_ms[INFINI_KERNEL_KINDS];
   int64_t launches[INFINI_KERNEL_KINDS];

@@ -18,6 +18,7 @@ EXPECTED = {
     "infini_attn_profile_enable", "infini_attn_profile_read",
     "infini_attn_project_qkv", "infini_attn_project_out", "infini_attn_forward_layer",
     "infini_attn_decode_step", "infini_attn_decode_flush", "infini_attn_decode_position",
+    "infini_attn_backward",
 }
 
 
@@ -97,3 +98,5 @@ def test_calls_on_a_missing_handle_fail_cleanly(lib):
         assert lib.infini_attn_decode_step(h, p, p, p, p, None) == -1
         assert lib.infini_attn_decode_flush(h, None) == -1
         assert lib.infini_attn_decode_position(h) == -1
+        assert lib.infini_attn_backward(h, p, p, p, p, None, None, None, None, p, p, p, p, None, None, 16,
+                                        None) == -1

@@ -1,0 +1,126 @@
+"""GPU parity of the backward pass (gradients back through the M / z recurrence) through
+the C-ABI against the CPU backward oracle (float64 autograd of the layer), plus
+full-size properties.
+
+Tolerances (relative Frobenius error of each gradient tensor against the oracle): 2e-2
+for bf16 inputs (the recomputed forward rounds P and M_{s-1} to bf16 as the forward does,
+and the upstream gradient is bf16), 1e-4 for the all-float32 path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from compressive_memory_transformer_segment_amd import binding
+from compressive_memory_transformer_segment_amd import workloads as wl
+from oracle import infini_backward as ob
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _check_grad(got, ref, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    r = gu.rel(got, ref)
+    assert r <= tol, f"{what}: relative error {r:.3e} > {tol}"
+    return r
+
+
+CASES = [
+    # name, B, H, d, N, L, dtype, update, with initial state, with final-state gradient
+    ("bf16-linear-d128", 1, 2, 128, 128, 3 * 128 + 29, "bf16", "linear", False, False),
+    ("bf16-delta-d128", 1, 2, 128, 128, 3 * 128 + 29, "bf16", "delta", False, False),
+    ("bf16-linear-d64-state", 2, 2, 64, 96, 2 * 96 + 40, "bf16", "linear", True, True),
+    ("bf16-delta-d64-state", 2, 1, 64, 96, 2 * 96 + 40, "bf16", "delta", True, True),
+    ("f32-linear-d128", 1, 2, 128, 64, 2 * 64 + 17, "f32", "linear", True, True),
+    ("f32-delta-d128", 1, 2, 128, 64, 2 * 64 + 17, "f32", "delta", True, True),
+    ("f32-delta-d64-n1", 1, 2, 64, 1, 5, "f32", "delta", False, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(case):
+    gu.require_gpu()
+    name, B, H, d, N, L, dtype, update, with_state, with_dstate = case
+    gu.note(f"[backward] {name}: B={B} H={H} d={d} N={N} L={L} {dtype} {update}")
+    w = wl.Workload(name, B, H, d, N, L, dtype, update, seed=61)
+    Q, K, V = wl.stream_inputs(w)
+    beta = wl.beta_for(w)
+    rng = np.random.default_rng(62)
+    dO = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    if dtype == "bf16":
+        dO = wl.round_to_bf16(dO)
+    M0 = z0 = dM = dz = None
+    if with_state:   # a state as a previous stream would leave it
+        _, M0, z0 = ob.forward_torch(*(torch.tensor(x, dtype=torch.float64) for x in wl.stream_inputs(
+            wl.Workload(name + "-pre", B, H, d, N, 2 * N, dtype, update, seed=63))),
+            torch.tensor(beta, dtype=torch.float64), N, update)
+        M0, z0 = M0.numpy().astype(np.float32), z0.numpy().astype(np.float32)
+    if with_dstate:
+        dM = (rng.standard_normal((B, H, d, d)) * 0.05).astype(np.float32)
+        dz = (rng.standard_normal((B, H, d)) * 0.05).astype(np.float32)
+    dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to("cuda")   # noqa: E731
+    with binding.InfiniAttention(B, H, d, N, update=update, io_dtype=dtype, eps=w.eps, beta=beta) as layer:
+        res = layer.backward(*(gu.to_dev(x, dtype) for x in (Q, K, V, dO)), m0=dev(M0), z0=dev(z0),
+                             dm_final=dev(dM), dz_final=dev(dz))
+        torch.cuda.synchronize()
+        got = {k_: t.cpu().numpy() for k_, t in res.items()}
+    ref = ob.gradients(Q, K, V, beta, dO, N, update, w.eps, None, M0, z0, dM, dz)
+    tol = GRAD_TOL[dtype]
+    for gname, rname in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV"), ("dbeta", "dbeta"), ("dm0", "dM0"),
+                         ("dz0", "dz0")):
+        _check_grad(got[gname], ref[rname], tol, gname)
+
+
+def test_backward_leaves_the_handle_state_alone():
+    gu.require_gpu()
+    B, H, d, N, L = 1, 2, 64, 64, 150
+    w = wl.Workload("bwd-state", B, H, d, N, L, "bf16", "linear", seed=64)
+    Q, K, V = (gu.to_dev(x, "bf16") for x in wl.stream_inputs(w))
+    with binding.InfiniAttention(B, H, d, N, eps=w.eps, beta=wl.beta_for(w)) as layer:
+        layer.forward_stream(Q, K, V)
+        M1, z1 = layer.get_state()
+        layer.backward(Q, K, V, torch.ones_like(Q))
+        M2, z2 = layer.get_state()
+        torch.cuda.synchronize()
+        assert torch.equal(M1, M2) and torch.equal(z1, z2)
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_full_size_backward_properties(update):
+    """8 heads, d=128, N=2048, 32K tokens: (1) with the gate closed (beta = -inf) and no
+    state gradient, sampled heads and segments of dQ, dK, dV equal causal attention's
+    gradient (float32 on the CPU); (2) the gradients are linear in the upstream gradient."""
+    gu.require_gpu()
+    base = wl.WORKLOADS[wl.THROUGHPUT_WORKLOAD]
+    w = wl.Workload(base.name + "-" + update, 1, base.heads, base.head_dim, base.segment_len, base.n_tokens,
+                    "bf16", update, seed=base.seed)
+    H, d, N, L = w.heads, w.head_dim, w.segment_len, w.n_tokens
+    gu.note(f"[backward] full size {w.name}")
+    Q, K, V = wl.stream_inputs(w)
+    rng = np.random.default_rng(65)
+    dO1 = wl.round_to_bf16(rng.standard_normal((1, H, L, d)).astype(np.float32))
+    dO2 = wl.round_to_bf16(rng.standard_normal((1, H, L, d)).astype(np.float32))
+    dev = [gu.to_dev(x, "bf16") for x in (Q, K, V)]
+    with binding.InfiniAttention(1, H, d, N, update=update, eps=w.eps, beta=[-np.inf] * H) as closed:
+        g = closed.backward(*dev, gu.to_dev(dO1, "bf16"))
+        torch.cuda.synchronize()
+        for h, s in ((0, 0), (3, 7), (7, L // N - 1)):
+            lo, hi = s * N, (s + 1) * N
+            q, k, v = (torch.tensor(x[0, h, lo:hi], dtype=torch.float32, requires_grad=True) for x in (Q, K, V))
+            o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True)[0]
+            dq, dk, dv = torch.autograd.grad((o * torch.tensor(dO1[0, h, lo:hi])).sum(), [q, k, v])
+            for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+                _check_grad(g[name][0, h, lo:hi].cpu().numpy(), ref.numpy(), 2e-2, f"{name} h{h} s{s}")
+    beta = wl.beta_for(w)
+    with binding.InfiniAttention(1, H, d, N, update=update, eps=w.eps, beta=beta) as layer:
+        ga = layer.backward(*dev, gu.to_dev(dO1, "bf16"))
+        gb = layer.backward(*dev, gu.to_dev(dO2, "bf16"))
+        gs = layer.backward(*dev, gu.to_dev(dO1 + dO2, "bf16"))   # sums of two bf16 values: rounded once more
+        torch.cuda.synchronize()
+        for name in ("dq", "dk", "dv", "dbeta", "dm0", "dz0"):
+            _check_grad((gs[name]).cpu().numpy(), (ga[name] + gb[name]).cpu().numpy(), 2e-2, f"linearity {name}")
