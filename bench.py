@@ -7,6 +7,10 @@ the roofline of the dominant kernel (the fused local-attention + retrieval + gat
 timed with HIP events on its own stream inside the timed region), and the CPU oracle's
 throughput on a bounded sample of the same workload.
 
+With --decode a step is one whole segment decoded token by token for --decode-batch
+sequences (``infini_attn_decode_step`` N times; the last call writes the segment to the
+memory), and the roofline is the decode kernel's HBM bandwidth.
+
 With --layer a step is one ``infini_attn_forward_layer`` instead: the whole layer from
 its input X [B, T, d_model] to O, the Q/K/V projection (Eq. 5) and the output projection
 (Eq. 11) included; the roofline is then that of the kernel with the most time per step.
@@ -42,6 +46,11 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="the whole layer X -> O (Q/K/V and output projections included): forward_layer")
     ap.add_argument("--d-model", type=int, default=0, help="--layer: model width (default H * d)")
+    ap.add_argument("--backward", action="store_true",
+                    help="training: one step = infini_attn_backward over the stream (forward recomputed)")
+    ap.add_argument("--decode", action="store_true",
+                    help="incremental decoding: one step = one whole segment (N tokens) per sequence, token by token")
+    ap.add_argument("--decode-batch", type=int, default=64, help="--decode: sequences decoded together")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -122,8 +131,256 @@ def cpu_baseline_layer(w, d_model: int, budget_s: float):
             "sample": f"oracle.layer_forward on the first {n} tokens (all heads, d_model={d_model}), {elapsed:.1f} s"}
 
 
+def decode_bytes(batch, heads, d, segment_len, es):
+    """Algorithmic HBM bytes of the decode launches over one segment: per (b, h) and token
+    at position p, the p cached key and value rows, M_{s-1} (fp32) and z_{s-1}, this
+    token's q, k, v in and its output out, and the key and value appended to the cache."""
+    per_bh = 0
+    for p in range(segment_len):
+        per_bh += 2 * p * d * es + 4 * d * d + 4 * d + 3 * d * es + d * es + 2 * d * es
+    return batch * heads * per_bh
+
+
+def cpu_baseline_decode(w, batch, budget_s: float):
+    """The oracle's token-by-token decoding on one sequence of the same shape (all heads)
+    until about budget_s seconds; tokens/s scaled to the batch is not claimed (it is one
+    sequence's rate)."""
+    import numpy as np
+    from compressive_memory_transformer_segment_amd import workloads as wl
+    from oracle import infini_oracle as orc
+    n = min(w.segment_len, 256)
+    ws = w.with_tokens(n).with_batch(1)
+    Q, K, V = wl.stream_inputs(ws)
+    beta = wl.beta_for(w)
+    scale = 1.0 / np.sqrt(w.head_dim)
+    t0 = time.perf_counter()
+    done = 0
+    M = np.zeros((w.head_dim, w.head_dim))
+    z = np.zeros(w.head_dim)
+    for t in range(n):
+        for h in range(w.heads):
+            orc.decode_token(Q[0, h, t], K[0, h, t], V[0, h, t], K[0, h, :t], V[0, h, :t], M, z, beta[h],
+                             w.eps, scale)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "sample": (f"oracle.decode_token for the first {done} tokens of one sequence, all {w.heads} heads "
+                       f"({el:.1f} s); per-sequence rate, positions 0..{done - 1} of a segment (short caches)")}
+
+
+def main_decode(args):
+    import torch
+    from compressive_memory_transformer_segment_amd import binding, profiling
+    from compressive_memory_transformer_segment_amd import workloads as wl
+
+    base = wl.WORKLOADS[args.workload or wl.THROUGHPUT_WORKLOAD]
+    B, H, d, N = args.decode_batch, base.heads, base.head_dim, base.segment_len
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(base.seed)
+    # one segment of tokens per sequence, resident in HBM: [N, B, H, d] so a token is contiguous
+    Q, K, V = ((torch.randn((N, B, H, d), generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
+               for _ in range(3))
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    layer = binding.InfiniAttention(B, H, d, N, update=base.update, io_dtype="bf16", eps=base.eps,
+                                    beta=wl.beta_for(base))
+    stream = torch.cuda.current_stream()
+
+    def step():   # one whole segment token by token; the last token closes it into the memory
+        for t in range(N):
+            layer.decode_step(Q[t], K[t], V[t], out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] decode B={B}: warmup {args.warmup} done, timing {args.steps} segments", file=sys.stderr,
+          flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    layer.profile_enable(True)
+    step()
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    torch.cuda.synchronize()
+    dec_ms, dec_n = prof["decode"]
+    bytes_seg = decode_bytes(B, H, d, N, 2)
+    achieved = bytes_seg / (dec_ms / 1e3) / 1e9
+    tokens = B * N
+    rec = {
+        "metric": METRIC + " [incremental decoding]",
+        "value": tokens / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode-b{B}-h{H}-d{d}-n{N}-{base.update}", "batch": B, "heads": H,
+                   "head_dim": d, "segment_len": N, "tokens_per_step": tokens,
+                   "step": "one segment per sequence, token by token, incl. the memory write at its end",
+                   "parallelism": "none"},
+        "roofline": {
+            "kernel": "k_decode (one token per (batch, head))",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": profiling.PEAK_HBM_BYTES / 1e9,
+            "unit": "GB/s",
+            "frac": achieved / (profiling.PEAK_HBM_BYTES / 1e9),
+            "traffic": None,
+            "algorithmic_bytes": bytes_seg / dec_n,
+            "avg_launch_us": dec_ms / dec_n * 1e3,
+        },
+        "kernels_avg_us": {k: (t / n * 1e3 if n else None) for k, (t, n) in prof.items()},
+        "kernels_total_ms_per_step": {k: t for k, (t, n) in prof.items()},
+        "wall_ms_per_step": wall_ms / args.steps,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_decode(base, B, args.cpu_budget_s)
+    else:
+        rec["cpu_baseline"] = None
+    layer.close()
+    print(json.dumps(rec), flush=True)
+
+
+def backward_flops(batch, heads, d, segment_len, n_tokens, update):
+    """Matrix-class FLOPs of the gradient kernels (the recomputed forward not included):
+    local attention 5 causal n x n x d products (scores, dP, dV, dQ, dK), the retrieval
+    gradient 2 n x d x d products (du, sigma(Q)^T dnum) and the update gradient 2 (linear:
+    sigma(K) G, G v) or 4 (delta: also R and M dW) per segment and head, plus the chain's
+    d x d x d product per segment for the delta rule."""
+    import compressive_memory_transformer_segment_amd.profiling as pf
+    tot = 0.0
+    for n in pf.segment_lengths(n_tokens, segment_len):
+        tot += 2.5 * pf.local_attention_flops(n, d)
+        tot += (2 + (4 if update == "delta" else 2)) * 2.0 * n * d * d
+        if update == "delta":
+            tot += 2.0 * d * d * d
+    return tot * batch * heads
+
+
+def main_backward(args):
+    import numpy as np
+    import torch
+    from compressive_memory_transformer_segment_amd import binding, profiling
+    from compressive_memory_transformer_segment_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload or wl.THROUGHPUT_WORKLOAD]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    shape = (w.batch, w.heads, w.n_tokens, w.head_dim)
+    Q, K, V = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    for b in range(w.batch):
+        for s in range(w.n_segments):
+            lo = s * w.segment_len
+            for x, p in zip((Q, K, V), wl.segment_inputs(w, b, s)):
+                x[b, :, lo:lo + p.shape[1]] = torch.from_numpy(p).to(dev, torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    dO = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    layer = binding.InfiniAttention(w.batch, w.heads, w.head_dim, w.segment_len, update=w.update, io_dtype="bf16",
+                                    eps=w.eps, beta=wl.beta_for(w))
+    stream = torch.cuda.current_stream()
+    outs = None
+
+    def step():
+        nonlocal outs
+        outs = layer.backward(Q, K, V, dO, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] backward {w.name}: warmup {args.warmup} done, timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms = ev0.elapsed_time(ev1) / args.steps
+    layer.profile_enable(True)
+    step()
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    torch.cuda.synchronize()
+    bwd_ms, bwd_n = prof["backward"]
+    fl = backward_flops(w.batch, w.heads, w.head_dim, w.segment_len, w.n_tokens, w.update)
+    achieved = fl / (bwd_ms / bwd_n / 1e3) / 1e12
+    tokens = w.batch * w.n_tokens
+    rec = {
+        "metric": METRIC + " [backward]",
+        "value": tokens / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + "-backward", "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "segment_len": w.segment_len, "n_tokens": w.n_tokens, "update": w.update,
+                   "step": "infini_attn_backward: forward recomputed, then all gradients", "parallelism": "none"},
+        "roofline": {
+            "kernel": "gradient kernels of one backward call (fp32 SIMT)",
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": 157.3,
+            "unit": "TFLOP/s",
+            "frac": achieved / 157.3,
+            "traffic": None,
+            "algorithmic_flops": fl,
+            "avg_launch_us": bwd_ms / bwd_n * 1e3,
+        },
+        "kernels_total_ms_per_step": {k: t for k, (t, n) in prof.items()},
+        "wall_ms_per_step": wall_ms / args.steps,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import infini_backward as ob
+        n = w.segment_len
+        ws = w.with_tokens(2 * n)
+        Qh, Kh, Vh = wl.stream_inputs(ws)
+        dOh = np.random.default_rng(1).standard_normal(Qh.shape)
+        t0 = time.perf_counter()
+        ob.gradients(Qh[:, :2], Kh[:, :2], Vh[:, :2], wl.beta_for(w)[:2], dOh[:, :2], n, w.update)
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": w.batch * 2 * n * 2 / w.heads / el, "unit": "tokens/s",
+                               "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": f"oracle gradients (float64 autograd) of 2 heads x {2 * n} tokens, "
+                                         f"{el:.1f} s, scaled to all {w.heads} heads"}
+    layer.close()
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
+    if args.decode and args.gpus == 1:
+        return main_decode(args)
+    if args.backward and args.gpus == 1:
+        return main_backward(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
