@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_NAME = "libinfini_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "state_pass.hip", "chain.hip", "attention.hip", "gemm.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.hip", "state_pass.hip", "chain.hip", "attention.hip", "gemm.hip", "decode.hip", "backward.hip", "attention_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,433 @@
+// Matrix-core kernels of the backward pass's local-attention gradients (Eq. 6, bf16 path),
+// plus the retrieval part of dQ (Eq. 7).  See backward.hip for the formulas; here
+// P = exp2(c q.k - lse) is recomputed from the forward's log-sum-exp, D_t = dO_t . A_dot_t and
+// the upstream gradient dO is used unscaled (the (1 - g) factor of the local arm is applied
+// to the results).
+//
+// dQ (k_bwd_dq_mfma): one workgroup = 4 waves = 128 queries of one (segment, batch, head);
+// every wave owns 32 queries and works in the forward kernel's transposed frame:
+//   S^T = K Q^T and dP^T = V dO^T (Q and dO rows are the B operands, held in registers),
+//   dS^T = P^T o (dP^T - D), dQ^T += K^T dS^T (the dS^T registers, converted to bf16, are the
+//   B operand, with K^T read from LDS by transpose reads in the key order they hold),
+// so softmax statistics are per-lane scalars.  K and V tiles of 64 keys go HBM -> LDS by
+// buffer -> LDS copies, double buffered.  The epilogue adds the retrieval part
+// (g / den) M dO^T + dden z, with M_{s-1} read from the forward's M^T copy by transpose
+// reads, multiplies by sigma'(Q), and stores fp32 dQ rows.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infini {
+
+namespace {
+
+constexpr int kBwdThreads = 256;   // 4 waves
+constexpr int kBwdQ = 128;         // queries per workgroup
+constexpr int kBwdK = 64;          // keys per tile
+
+// Copy `rows` rows of a [*, D] bf16 array into LDS in the 16-row-group layout (chunk c of
+// row r in slot (r / 16) * 16 CPR + 16 c + r % 16): copy number c of the tile (1 KB) covers
+// rows 16 g + lane % 16, chunks 4 j + lane / 16 with g = c / (CPR / 4), j = c % (CPR / 4).
+// Rows at or past `valid_rows` read as zeros.  The caller spreads the copies over its waves.
+template <int D>
+__device__ __forceinline__ void copy_rows(const uint16_t* src, int valid_rows, uint16_t* lds, int c, int lane) {
+  constexpr int CPR = D / 8;
+  const int g = c / (CPR / 4), j = c % (CPR / 4);
+  const int shift = g * 32 * D + 64 * j;   // bytes
+  const int left = __builtin_amdgcn_readfirstlane(max(valid_rows * 2 * D - shift, 0));
+  const uint32_t lp = static_cast<uint32_t>((lane & 15) * 2 * D + 16 * (lane >> 4));
+  copy_to_lds(reinterpret_cast<const char*>(src) + shift, static_cast<uint32_t>(left), lds + 512 * c, lp);
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2) void k_bwd_dq_mfma(const BackwardArgs b) {
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int TILE = kBwdK * D;           // elements of a K (or V) tile
+  constexpr int CPT = kBwdK * D * 2 / 1024; // 1 KB copies per tensor tile
+  constexpr int CPW = CPT / 4;              // ... per wave
+  static_assert(D * D <= 2 * TILE, "M^T fits one buffer");
+  __shared__ __align__(16) uint16_t buf0[2 * TILE];
+  __shared__ __align__(16) uint16_t buf1[2 * TILE];
+
+  const WindowArgs& w = b.w;
+  const int units = w.units();
+  const int nq = (w.N + kBwdQ - 1) / kBwdQ;
+  const int u = static_cast<int>(blockIdx.x) % units;
+  const int qt = nq - 1 - static_cast<int>(blockIdx.x) / units;   // longest tiles first
+  const int BH = w.B * w.H;
+  const int s_local = u / BH, bh = u % BH, h = bh % w.H;
+  const int n = w.seg_tokens(s_local);
+  const int q0 = qt * kBwdQ;
+  if (q0 >= n) return;
+  const int64_t row0 = static_cast<int64_t>(bh) * w.T + static_cast<int64_t>(w.s0 + s_local) * w.N;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int qw0 = q0 + 32 * wave;
+  const int q = qw0 + l32;
+  const bool live = q < n;
+  const int64_t row = row0 + q;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(w.q_loc) + row0 * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(w.k_loc) + row0 * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(w.v) + row0 * D;
+  const uint16_t* og = static_cast<const uint16_t*>(b.dout) + row0 * D;
+
+  // this lane's query as the B operand: Q[q][16 ks + 8 hl .. +7], dO likewise
+  u32x4 qreg[KS], oreg[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qreg[ks] = live ? ld16(qg + static_cast<int64_t>(q) * D + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+    oreg[ks] = live ? ld16(og + static_cast<int64_t>(q) * D + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+  }
+  const float lse = live ? w.lse[row] : INFINITY;   // P = 0 for rows past the segment
+  const float dd = live ? b.dd[row] : 0.f;
+  const float c2 = w.scale_log2;
+
+  const int kv_end = min(q0 + kBwdQ, n);
+  const int nkv = (kv_end + kBwdK - 1) / kBwdK;
+  // tile i (keys 64 i ..) into dst: CPW copies of K and of V per wave; past the last tile
+  // the copies are zero fills, so every tile is 2 CPW copies and the waits are constants
+  auto issue = [&](int i, uint16_t* dst) __attribute__((always_inline)) {
+    const int rows = i < nkv ? n - i * kBwdK : 0;
+    const int64_t off = static_cast<int64_t>(min(i, nkv) * kBwdK) * D;
+#pragma unroll
+    for (int t = 0; t < CPW; ++t) copy_rows<D>(kg + off, rows, dst, wave * CPW + t, lane);
+#pragma unroll
+    for (int t = 0; t < CPW; ++t) copy_rows<D>(vg + off, rows, dst + TILE, wave * CPW + t, lane);
+  };
+
+  // LDS read offsets (elements)
+  //  row-group operand read (K, V rows as the A operand): row 32 blk + l32, chunk 2 ks + hl
+  const int g_rd = ((l32 >> 4) * 16 * CPR + 16 * hl + (l32 & 15)) * 8;
+  //  K^T by transpose reads: lane j of 16-lane group G addresses key row
+  //  16 j4 + 4 (G / 2) + j / 4 (+ 8), columns 32 db + 16 (G % 2) + 4 (j % 4) .. +3
+  const int G = lane >> 4, jl = lane & 15;
+  const int t_rd = (16 * (2 * (G & 1) + ((jl & 3) >> 1)) + 4 * (G >> 1) + (jl >> 2)) * 8 + 4 * (jl & 1);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero16();
+
+  auto compute = [&](const uint16_t* kt, int j) __attribute__((always_inline)) {
+    const int kv0 = j * kBwdK;
+    if (kv0 > qw0 + 31) return;   // every key of the tile lies past this wave's queries
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = zero16();
+      dp[kb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s[kb] = mfma32x32x16(as_bf16x8(ld16(kt + g_rd + kb * 256 * CPR + 256 * ks)), as_bf16x8(qreg[ks]), s[kb]);
+        dp[kb] = mfma32x32x16(as_bf16x8(ld16(kt + TILE + g_rd + kb * 256 * CPR + 256 * ks)), as_bf16x8(oreg[ks]),
+                              dp[kb]);
+      }
+    }
+    // register r of block kb holds key kv0 + 32 kb + 8 (r / 4) + 4 hl + r % 4
+    const bool masked = kv0 + kBwdK - 1 > qw0 || kv0 + kBwdK > n;
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse));
+        if (masked) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          pr = (key > q || key >= n) ? 0.f : pr;
+        }
+        v[r] = pr * (dp[kb][r] - dd);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        dsb[2 * kb + half] = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(v[8 * half], v[8 * half + 1]), pack_bf16x2(v[8 * half + 2], v[8 * half + 3]),
+                          pack_bf16x2(v[8 * half + 4], v[8 * half + 5]), pack_bf16x2(v[8 * half + 6], v[8 * half + 7])});
+    }
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* p = kt + t_rd + j4 * 128 * CPR + db * 512;
+        const u32x2 a0 = lds_read_tr16(p);
+        const u32x2 a1 = lds_read_tr16(p + 64);
+        acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}), dsb[j4], acc[db]);
+      }
+  };
+
+  issue(0, buf0);
+  issue(1, buf1);
+  for (int j = 0; j < nkv; j += 2) {
+    wait_vm_lgkm0<2 * CPW>();   // tile j (tile j + 1 may still be in flight)
+    __builtin_amdgcn_s_barrier();
+    compute(buf0, j);
+    wait_vm_lgkm0<2 * CPW>();   // this wave's reads of buffer 0 are done
+    __builtin_amdgcn_s_barrier();
+    issue(j + 2, buf0);
+    if (j + 1 < nkv) {
+      wait_vm_lgkm0<2 * CPW>();   // tile j + 1
+      __builtin_amdgcn_s_barrier();
+      compute(buf1, j + 1);
+      wait_vm_lgkm0<2 * CPW>();
+      __builtin_amdgcn_s_barrier();
+      issue(j + 3, buf1);
+    }
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+
+  // ---- retrieval part: X^T = M dO^T (rows i, columns queries), M_{s-1}[i][j] = mt[j][i]
+  const uint16_t* mt = static_cast<const uint16_t*>(w.ws.mt) + static_cast<int64_t>(u) * D * D;
+#pragma unroll
+  for (int t = 0; t < D * D * 2 / 1024 / 4; ++t) copy_rows<D>(mt, D, buf0, wave * (D * D * 2 / 1024 / 4) + t, lane);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  //  A operand M[i][16 ks + 8 hl + 0..7] = mt rows 16 ks + 8 hl + 0..7 at column i: lane j of
+  //  group G addresses mt row 16 ks + 8 (G / 2) + j / 4 (+ 4), columns 32 db + 16 (G % 2) + 4 (j % 4)
+  const int m_rd = (16 * (2 * (G & 1) + ((jl & 3) >> 1)) + 8 * (G >> 1) + (jl >> 2)) * 8 + 4 * (jl & 1);
+  const float g = w.gate_g[h], omg = w.gate_omg[h];
+  const float den = live ? b.den[row] : 1.f, dden = live ? b.dden[row] : 0.f;
+  const float gd = g / den;
+  const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
+  const uint16_t* qm = static_cast<const uint16_t*>(w.q) + row * D;   // PE-free Q of the retrieval
+  const float sc = w.scale * omg;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    f32x16 x = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint16_t* p = buf0 + m_rd + ks * 128 * CPR + db * 512;
+      const u32x2 a0 = lds_read_tr16(p);
+      const u32x2 a1 = lds_read_tr16(p + 32);
+      x = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}), as_bf16x8(oreg[ks]), x);
+    }
+    if (!live) continue;
+    // register quad r4 holds features 32 db + 8 r4 + 4 hl + 0..3 of this lane's query
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int i0 = 32 * db + 8 * r4 + 4 * hl;
+      const u32x2 qv = ld8(qm + i0);
+      const f32x4 zv = *reinterpret_cast<const f32x4*>(zb + i0);
+      const float qf[4] = {bf16lo_to_f32(qv[0]), bf16hi_to_f32(qv[0]), bf16lo_to_f32(qv[1]), bf16hi_to_f32(qv[1])};
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float qe = qf[e];
+        const float ds = qe > 0.f ? 1.f : __builtin_amdgcn_exp2f(qe * kLog2e);
+        o[e] = acc[db][4 * r4 + e] * sc + (gd * x[4 * r4 + e] + dden * zv[e]) * ds;
+      }
+      *reinterpret_cast<f32x4*>(b.dq + row * D + i0) = o;
+    }
+  }
+}
+
+// dK, dV (k_bwd_dkv_mfma): one workgroup = 4 waves = 128 keys; every wave owns 32 keys and
+// works in the mirror frame, keys on lanes: S = Q K^T and dP = dO V^T (this wave's K and V
+// rows are the B operands, held in registers), P and dS = P o (dP - D) per query row, then
+// dV^T += dO^T P and dK^T += Q^T dS with the P / dS registers as B operands and dO^T, Q^T
+// read from LDS by transpose reads in the query order those registers hold.  Query tiles of
+// 64 (Q, dO, lse, D) go HBM -> LDS by buffer -> LDS copies, double buffered.
+// (d = 128: the K, V operands and the dK, dV accumulators need more than 256 registers, so
+// one workgroup per CU with the accumulators in AGPRs.)
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(const BackwardArgs b) {
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int TILE = kBwdK * D;            // elements of a Q (or dO) tile
+  constexpr int CPT = kBwdK * D * 2 / 1024;  // 1 KB copies per tensor tile
+  constexpr int CPW = CPT / 4;
+  __shared__ __align__(16) uint16_t buf0[2 * TILE];
+  __shared__ __align__(16) uint16_t buf1[2 * TILE];
+  __shared__ __align__(16) float st0[2][256];   // lse, D of the tile in buffer 0 (first 64 used)
+  __shared__ __align__(16) float st1[2][256];
+
+  const WindowArgs& w = b.w;
+  const int units = w.units();
+  const int u = static_cast<int>(blockIdx.x) % units;
+  const int kt = static_cast<int>(blockIdx.x) / units;   // key tile; the first ones are the longest
+  const int BH = w.B * w.H;
+  const int s_local = u / BH, bh = u % BH, h = bh % w.H;
+  const int n = w.seg_tokens(s_local);
+  const int k0 = kt * kBwdQ;
+  if (k0 >= n) return;
+  const int64_t row0 = static_cast<int64_t>(bh) * w.T + static_cast<int64_t>(w.s0 + s_local) * w.N;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int kw0 = k0 + 32 * wave;
+  const int key = kw0 + l32;
+  const bool live = key < n;
+
+  const uint16_t* qg = static_cast<const uint16_t*>(w.q_loc) + row0 * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(w.k_loc) + row0 * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(w.v) + row0 * D;
+  const uint16_t* og = static_cast<const uint16_t*>(b.dout) + row0 * D;
+  const float* lg = w.lse + row0;
+  const float* dg = b.dd + row0;
+
+  u32x4 kreg[KS], vreg[KS];   // this lane's key as the B operand
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kreg[ks] = live ? ld16(kg + static_cast<int64_t>(key) * D + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+    vreg[ks] = live ? ld16(vg + static_cast<int64_t>(key) * D + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+  }
+  const float c2 = w.scale_log2;
+
+  const int t_first = k0 / kBwdK;                  // first query tile (queries >= the first key)
+  const int nqt = (n + kBwdK - 1) / kBwdK - t_first;   // query tiles to visit
+  // query tile t_first + i into (dst, stats): CPW copies of Q and of dO per wave, plus the
+  // tile's lse (wave 0) and D (wave 1); past the last tile the copies are zero fills
+  auto issue = [&](int i, uint16_t* dst, float (*stats)[256]) __attribute__((always_inline)) {
+    const int t = t_first + min(i, nqt);
+    const int rows = i < nqt ? n - t * kBwdK : 0;
+    const int64_t off = static_cast<int64_t>(t * kBwdK) * D;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) copy_rows<D>(qg + off, rows, dst, wave * CPW + c, lane);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) copy_rows<D>(og + off, rows, dst + TILE, wave * CPW + c, lane);
+    if (wave < 2) {   // 64 floats (lanes 16 .. 63 write zeros into the rest of the 1 KB row)
+      const float* src = (wave == 0 ? lg : dg) + t * kBwdK;
+      const uint32_t bytes = static_cast<uint32_t>(max(min(rows, kBwdK), 0)) * 4;
+      copy_to_lds(src, bytes, reinterpret_cast<const uint16_t*>(stats[wave]), static_cast<uint32_t>(lane) * 16);
+    }
+  };
+  const int cnt = 2 * CPW + (wave < 2 ? 1 : 0);   // copies per tile issued by this wave
+
+  const int g_rd = ((l32 >> 4) * 16 * CPR + 16 * hl + (l32 & 15)) * 8;
+  const int G = lane >> 4, jl = lane & 15;
+  const int t_rd = (16 * (2 * (G & 1) + ((jl & 3) >> 1)) + 4 * (G >> 1) + (jl >> 2)) * 8 + 4 * (jl & 1);
+
+  f32x16 adv[DB], adk[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    adv[db] = zero16();
+    adk[db] = zero16();
+  }
+
+  auto compute = [&](const uint16_t* qt_, const float (*stats)[256], int i) __attribute__((always_inline)) {
+    const int t0 = (t_first + i) * kBwdK;
+    if (t0 + kBwdK - 1 < kw0) return;   // every query of the tile precedes this wave's keys
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = zero16();
+      dp[qb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s[qb] = mfma32x32x16(as_bf16x8(ld16(qt_ + g_rd + qb * 256 * CPR + 256 * ks)), as_bf16x8(kreg[ks]), s[qb]);
+        dp[qb] = mfma32x32x16(as_bf16x8(ld16(qt_ + TILE + g_rd + qb * 256 * CPR + 256 * ks)), as_bf16x8(vreg[ks]),
+                              dp[qb]);
+      }
+    }
+    // register r of block qb holds query t0 + 32 qb + 8 (r / 4) + 4 hl + r % 4
+    const bool masked = t0 < kw0 + 31 || t0 + kBwdK > n;
+    bf16x8 pb[4], dsb[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float pv[16], dv[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rl = 32 * qb + 8 * r4 + 4 * hl;   // tile row of register 4 r4
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&stats[0][rl]);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&stats[1][rl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c2, -lv[e]));
+          if (masked) {
+            const int qr = t0 + rl + e;
+            pr = (qr < key || qr >= n) ? 0.f : pr;
+          }
+          pv[r] = pr;
+          dv[r] = pr * (dp[qb][r] - dv4[e]);
+        }
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        pb[2 * qb + half] = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(pv[8 * half], pv[8 * half + 1]), pack_bf16x2(pv[8 * half + 2], pv[8 * half + 3]),
+                          pack_bf16x2(pv[8 * half + 4], pv[8 * half + 5]),
+                          pack_bf16x2(pv[8 * half + 6], pv[8 * half + 7])});
+        dsb[2 * qb + half] = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(dv[8 * half], dv[8 * half + 1]), pack_bf16x2(dv[8 * half + 2], dv[8 * half + 3]),
+                          pack_bf16x2(dv[8 * half + 4], dv[8 * half + 5]),
+                          pack_bf16x2(dv[8 * half + 6], dv[8 * half + 7])});
+      }
+    }
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* po = qt_ + TILE + t_rd + j4 * 128 * CPR + db * 512;
+        const u32x2 o0 = lds_read_tr16(po);
+        const u32x2 o1 = lds_read_tr16(po + 64);
+        adv[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), pb[j4], adv[db]);
+        const uint16_t* pq = qt_ + t_rd + j4 * 128 * CPR + db * 512;
+        const u32x2 q0_ = lds_read_tr16(pq);
+        const u32x2 q1_ = lds_read_tr16(pq + 64);
+        adk[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{q0_[0], q0_[1], q1_[0], q1_[1]}), dsb[j4], adk[db]);
+      }
+  };
+
+  issue(0, buf0, st0);
+  issue(1, buf1, st1);
+  for (int i = 0; i < nqt; i += 2) {
+    wait_vm_le(cnt);   // tile i (tile i + 1 may still be in flight)
+    __builtin_amdgcn_s_barrier();
+    compute(buf0, st0, i);
+    wait_vm_le(cnt);   // this wave's LDS reads of buffer 0 are done
+    __builtin_amdgcn_s_barrier();
+    issue(i + 2, buf0, st0);
+    if (i + 1 < nqt) {
+      wait_vm_le(cnt);
+      __builtin_amdgcn_s_barrier();
+      compute(buf1, st1, i + 1);
+      wait_vm_le(cnt);
+      __builtin_amdgcn_s_barrier();
+      issue(i + 3, buf1, st1);
+    }
+  }
+  wait_vm_le(0);   // no copy may land in LDS after the workgroup ends
+  if (!live) return;
+  const float omg = w.gate_omg[h], sc = w.scale * omg;
+  const int64_t krow = row0 + key;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int i0 = 32 * db + 8 * r4 + 4 * hl;
+      f32x4 ov, ok;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ov[e] = adv[db][4 * r4 + e] * omg;
+        ok[e] = adk[db][4 * r4 + e] * sc;
+      }
+      *reinterpret_cast<f32x4*>(b.dv + krow * D + i0) = ov;
+      *reinterpret_cast<f32x4*>(b.dk + krow * D + i0) = ok;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, hipStream_t st) {
+  const WindowArgs& w = b.w;
+  const int nk = (w.N + kBwdQ - 1) / kBwdQ;
+  const dim3 grid(static_cast<unsigned>(w.units() * nk)), block(kBwdThreads);
+  if (w.D == 128) hipLaunchKernelGGL((k_bwd_dkv_mfma<128>), grid, block, 0, st, b);
+  else if (w.D == 64) hipLaunchKernelGGL((k_bwd_dkv_mfma<64>), grid, block, 0, st, b);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_mfma(const BackwardArgs& b, hipStream_t st) {
+  const WindowArgs& w = b.w;
+  const int nq = (w.N + kBwdQ - 1) / kBwdQ;
+  const dim3 grid(static_cast<unsigned>(w.units() * nq)), block(kBwdThreads);
+  if (w.D == 128) hipLaunchKernelGGL((k_bwd_dq_mfma<128>), grid, block, 0, st, b);
+  else if (w.D == 64) hipLaunchKernelGGL((k_bwd_dq_mfma<64>), grid, block, 0, st, b);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace infini

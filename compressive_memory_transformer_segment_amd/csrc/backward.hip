@@ -536,8 +536,18 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
   const unsigned tiles = static_cast<unsigned>(w.units() * b.pt);
   const unsigned BH = static_cast<unsigned>(w.B * w.H);
   hipLaunchKernelGGL((k_bwd_prep<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
-  hipLaunchKernelGGL((k_bwd_dq<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
-  hipLaunchKernelGGL((k_bwd_dkv<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
+  if constexpr (BF16) {
+    const hipError_t e = launch_bwd_dq_mfma(b, st);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((k_bwd_dq<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
+  }
+  if constexpr (BF16) {
+    const hipError_t e = launch_bwd_dkv_mfma(b, st);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((k_bwd_dkv<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
+  }
   hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
   hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH), dim3(kBT), 0, st, b);
   hipLaunchKernelGGL((k_bwd_update<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);

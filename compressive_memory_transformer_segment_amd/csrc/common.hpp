@@ -157,6 +157,32 @@ __device__ __forceinline__ void wait_vm_le(int vm) {   // vm wave-uniform, 0 .. 
   }
 }
 
+// Buffer -> LDS copy of 16 bytes per lane (lane i to lds + 16 i; offsets at or past
+// `bytes` read zeros), issued as inline assembly so that the compiler adds no waits of its
+// own for it: the kernel orders copies and LDS reads itself, with explicit vmcnt waits
+// and barriers.  (The compiler's tracking of the builtin form loses which buffer a copy
+// writes across the unrolled pipeline and then holds every operand read until all copies
+// in flight have landed.)  M0 must be written one wait state before the copy.
+// (Kernels that use it keep no value of their own in M0 and do not mix it with the builtin
+// form, so clobbering M0 is safe.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t bytes, const uint16_t* lds, uint32_t voffset) {
+  typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+  // every operand is wave-uniform; readfirstlane states it, so that they stay in SGPRs
+  const uint32_t m0 = static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)lds))));
+  const uint64_t a = reinterpret_cast<uint64_t>(src);
+  const u32x4 rsrc = {static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu)),
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000u};
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
