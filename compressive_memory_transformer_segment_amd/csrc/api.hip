@@ -940,6 +940,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   bw.dbeta = dbeta;
   bw.rch = rch;
   bw.pt = pt;
+  bw.ct = h->bf16 ? (h->N + 127) / 128 : pt;   // the bf16 update kernel works on 128-token tiles
   e = timed(h, 7, st, [&] { return infini::launch_backward(bw, st); });
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }

@@ -408,7 +408,245 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
     }
 }
 
+// Memory-update part of dK, dV (k_bwd_update_mfma, Eq. 8 / 9 differentiated; formulas in
+// backward.hip): one workgroup = 4 waves = 128 tokens of one segment; every wave owns 32
+// tokens on lanes, with the feature dimension in the result registers:
+//   Y^T = G_s^T sigma(K)^T                      (-> dV)
+//   linear: dsigma(K)^T = G_s V^T
+//   delta:  R^T = M_{s-1}^T sigma(K)^T / denk,  dsigma(K)^T = G_s (V - R)^T + M_{s-1} dW^T
+//           + z ddenk with dW = -Y / denk, ddenk = Y . R / denk (per token)
+// G_s (fp32) and, for the delta rule, M_{s-1} are staged in LDS as bf16 in both orientations
+// (16-row-group layout); sigma(K) and V come from registers; the (V - R) and dW results are
+// the B operands of the last products, with G_s and M_{s-1} read in the order their
+// registers hold.  dV, dK are updated in place (fp32); the tile's sigma(K)^T ddenk partial
+// goes to cpart.
+__device__ __forceinline__ int rg_index(int r, int c, int cpr) {
+  return ((r >> 4) * 16 * cpr + 16 * (c >> 3) + (r & 15)) * 8 + (c & 7);
+}
+
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(const BackwardArgs b) {
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, DD = D * D;
+  __shared__ __align__(16) uint16_t gt_l[DD];               // G_s^T (rows j)
+  __shared__ __align__(16) uint16_t gr_l[DD];               // G_s (rows i)
+  __shared__ __align__(16) uint16_t mt_l[DELTA ? DD : 8];   // M_{s-1}^T (rows j)
+  __shared__ __align__(16) uint16_t mr_l[DELTA ? DD : 8];   // M_{s-1} (rows i)
+  __shared__ float cacc[D];
+
+  const WindowArgs& w = b.w;
+  const int u = static_cast<int>(blockIdx.x) / b.ct, tile = static_cast<int>(blockIdx.x) % b.ct;
+  const int BH = w.B * w.H;
+  const int s_local = u / BH, bh = u % BH;
+  const int n = w.seg_tokens(s_local);
+  const int t0 = tile * 128;
+  if (t0 >= n) return;
+  const int64_t row0 = static_cast<int64_t>(bh) * w.T + static_cast<int64_t>(w.s0 + s_local) * w.N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  // ---- stage G_s (and M_{s-1}) as bf16 in both orientations
+  const float* gm = b.gm + static_cast<int64_t>(u) * DD;
+  for (int e = tid; e < D * CPR; e += kBwdThreads) {
+    {  // G rows: chunk (i, cj)
+      const int i = e / CPR, cj = e % CPR;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(gm + i * D + 8 * cj);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(gm + i * D + 8 * cj + 4);
+      st16(gr_l + rg_index(i, 8 * cj, CPR), u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
+                                                 pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])});
+    }
+    {  // G^T rows: chunk (j, ci) = G[8 ci .. + 7][j]
+      const int j = e % D, ci = e / D;
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = gm[(8 * ci + k) * D + j];
+      st16(gt_l + rg_index(j, 8 * ci, CPR), u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                 pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
+    }
+    if constexpr (DELTA) {
+      const uint16_t* mt = static_cast<const uint16_t*>(w.ws.mt) + static_cast<int64_t>(u) * DD;
+      {  // M^T rows (as recorded): chunk (j, ci)
+        const int j = e / CPR, ci = e % CPR;
+        st16(mt_l + rg_index(j, 8 * ci, CPR), ld16(mt + j * D + 8 * ci));
+      }
+      {  // M rows: chunk (i, cj) = M^T[8 cj .. + 7][i]
+        const int i = e % D, cj = e / D;
+        uint16_t x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = mt[(8 * cj + k) * D + i];
+        st16(mr_l + rg_index(i, 8 * cj, CPR),
+             u32x4{x[0] | (uint32_t(x[1]) << 16), x[2] | (uint32_t(x[3]) << 16), x[4] | (uint32_t(x[5]) << 16),
+                   x[6] | (uint32_t(x[7]) << 16)});
+      }
+    }
+  }
+  if (tid < D) cacc[tid] = 0.f;
+  __syncthreads();
+
+  const int t = t0 + 32 * wave + l32;
+  const bool live = t < n;
+  const int64_t row = row0 + t;
+  const uint16_t* kr = static_cast<const uint16_t*>(w.k) + row * D;
+  const uint16_t* vr = static_cast<const uint16_t*>(w.v) + row * D;
+  const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
+
+  // sigma(k) of this lane's token as the B operand (k = i natural), and sigma(k) . z
+  bf16x8 wreg[KS];
+  float wf[KS][8];
+  float zs = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 kv = live ? ld16(kr + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wf[ks][2 * e] = live ? elu_plus_one(bf16lo_to_f32(kv[e])) : 0.f;
+      wf[ks][2 * e + 1] = live ? elu_plus_one(bf16hi_to_f32(kv[e])) : 0.f;
+    }
+    wreg[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(wf[ks][0], wf[ks][1]), pack_bf16x2(wf[ks][2], wf[ks][3]),
+                                               pack_bf16x2(wf[ks][4], wf[ks][5]), pack_bf16x2(wf[ks][6], wf[ks][7])});
+    if constexpr (DELTA) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zs = fmaf(wf[ks][e], zb[16 * ks + 8 * hl + e], zs);
+    }
+  }
+  const int g_rd = ((l32 >> 4) * 16 * CPR + 16 * hl + (l32 & 15)) * 8;
+  const int p_rd = ((l32 >> 4) * 16 * CPR + (l32 & 15)) * 8 + 4 * hl;
+
+  f32x16 Y[DB], S[DB];
+#pragma unroll
+  for (int jb = 0; jb < DB; ++jb) {
+    Y[jb] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      Y[jb] = mfma32x32x16(as_bf16x8(ld16(gt_l + g_rd + jb * 256 * CPR + 256 * ks)), wreg[ks], Y[jb]);
+  }
+  float ddk = 0.f;
+  if constexpr (!DELTA) {
+    u32x4 vreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) vreg[ks] = live ? ld16(vr + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ib = 0; ib < DB; ++ib) {
+      S[ib] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        S[ib] = mfma32x32x16(as_bf16x8(ld16(gr_l + g_rd + ib * 256 * CPR + 256 * ks)), as_bf16x8(vreg[ks]), S[ib]);
+    }
+  } else {
+    const float denk = sum_across_halves(zs) + w.eps;
+    const float inv = 1.f / denk;
+    f32x16 R[DB];
+#pragma unroll
+    for (int jb = 0; jb < DB; ++jb) {
+      R[jb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        R[jb] = mfma32x32x16(as_bf16x8(ld16(mt_l + g_rd + jb * 256 * CPR + 256 * ks)), wreg[ks], R[jb]);
+    }
+    // register r of block jb holds feature j = 32 jb + 8 (r / 4) + 4 hl + r % 4 of this token
+    float yr = 0.f;
+    bf16x8 vrb[KS], dwb[KS];
+#pragma unroll
+    for (int jb = 0; jb < DB; ++jb) {
+      float vmr[16], dw[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const u32x2 vv = live ? ld8(vr + 32 * jb + 8 * r4 + 4 * hl) : u32x2{0, 0};
+        const float vf[4] = {bf16lo_to_f32(vv[0]), bf16hi_to_f32(vv[0]), bf16lo_to_f32(vv[1]), bf16hi_to_f32(vv[1])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float rv = R[jb][r] * inv;
+          yr = fmaf(Y[jb][r], rv, yr);
+          vmr[r] = vf[e] - rv;
+          dw[r] = -Y[jb][r] * inv;
+        }
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        vrb[2 * jb + half] = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(vmr[8 * half], vmr[8 * half + 1]), pack_bf16x2(vmr[8 * half + 2], vmr[8 * half + 3]),
+                          pack_bf16x2(vmr[8 * half + 4], vmr[8 * half + 5]),
+                          pack_bf16x2(vmr[8 * half + 6], vmr[8 * half + 7])});
+        dwb[2 * jb + half] = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(dw[8 * half], dw[8 * half + 1]), pack_bf16x2(dw[8 * half + 2], dw[8 * half + 3]),
+                          pack_bf16x2(dw[8 * half + 4], dw[8 * half + 5]), pack_bf16x2(dw[8 * half + 6], dw[8 * half + 7])});
+      }
+    }
+    ddk = sum_across_halves(yr) * inv;
+#pragma unroll
+    for (int ib = 0; ib < DB; ++ib) {
+      S[ib] = zero16();
+#pragma unroll
+      for (int j4 = 0; j4 < KS; ++j4) {
+        const uint16_t* pg = gr_l + p_rd + ib * 256 * CPR + 256 * j4;
+        const u32x2 g0 = ld8(pg), g1 = ld8(pg + 128);
+        S[ib] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]}), vrb[j4], S[ib]);
+        const uint16_t* pm = mr_l + p_rd + ib * 256 * CPR + 256 * j4;
+        const u32x2 m0 = ld8(pm), m1 = ld8(pm + 128);
+        S[ib] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), dwb[j4], S[ib]);
+      }
+    }
+    // this tile's share of sigma(K)^T ddenk
+    if (live) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) atomicAdd(&cacc[16 * ks + 8 * hl + e], wf[ks][e] * ddk);
+    }
+  }
+  if (live) {
+#pragma unroll
+    for (int jb = 0; jb < DB; ++jb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int j0 = 32 * jb + 8 * r4 + 4 * hl;
+        f32x4* pv = reinterpret_cast<f32x4*>(b.dv + row * D + j0);
+        f32x4 o = *pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += Y[jb][4 * r4 + e];
+        *pv = o;
+      }
+#pragma unroll
+    for (int ib = 0; ib < DB; ++ib)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int i0 = 32 * ib + 8 * r4 + 4 * hl;
+        const u32x2 kv = ld8(kr + i0);
+        const float kf[4] = {bf16lo_to_f32(kv[0]), bf16hi_to_f32(kv[0]), bf16lo_to_f32(kv[1]), bf16hi_to_f32(kv[1])};
+        f32x4* pk = reinterpret_cast<f32x4*>(b.dk + row * D + i0);
+        f32x4 o = *pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float a = S[ib][4 * r4 + e];
+          if constexpr (DELTA) a = fmaf(ddk, zb[i0 + e], a);
+          o[e] += a * (kf[e] > 0.f ? 1.f : __builtin_amdgcn_exp2f(kf[e] * kLog2e));
+        }
+        *pk = o;
+      }
+  }
+  if constexpr (DELTA) {
+    __syncthreads();
+    if (tid < D) b.cpart[(static_cast<int64_t>(u) * b.ct + tile) * D + tid] = cacc[tid];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st) {
+  const WindowArgs& w = b.w;
+  const dim3 grid(static_cast<unsigned>(w.units() * b.ct)), block(kBwdThreads);
+  if (w.D == 128) {
+    if (w.delta) hipLaunchKernelGGL((k_bwd_update_mfma<128, true>), grid, block, 0, st, b);
+    else hipLaunchKernelGGL((k_bwd_update_mfma<128, false>), grid, block, 0, st, b);
+  } else if (w.D == 64) {
+    if (w.delta) hipLaunchKernelGGL((k_bwd_update_mfma<64, true>), grid, block, 0, st, b);
+    else hipLaunchKernelGGL((k_bwd_update_mfma<64, false>), grid, block, 0, st, b);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, hipStream_t st) {
   const WindowArgs& w = b.w;

@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kBT) void k_bwd_update(const BackwardArgs b) {
     for (int o = 0; o < OPT; ++o) wk[tk][sub + 16 * o] = cacc[o];
     __syncthreads();
     if (tk == 0) {
-      float* cp = b.cpart + (static_cast<int64_t>(u) * b.pt + tile) * D;
+      float* cp = b.cpart + (static_cast<int64_t>(u) * b.ct + tile) * D;
 #pragma unroll
       for (int o = 0; o < OPT; ++o) {
         float sacc = 0.f;
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(D) void k_bwd_zchain(const BackwardArgs b) {
     b.gz[static_cast<int64_t>(u) * D + i] = gz;
     for (int ch = 0; ch < b.rch; ++ch) gz += b.rzpart[(static_cast<int64_t>(u) * b.rch + ch) * D + i];
     if (w.delta)
-      for (int t = 0; t < b.pt; ++t) gz += b.cpart[(static_cast<int64_t>(u) * b.pt + t) * D + i];
+      for (int t = 0; t < b.ct; ++t) gz += b.cpart[(static_cast<int64_t>(u) * b.ct + t) * D + i];
   }
   if (b.dz0) b.dz0[static_cast<int64_t>(bh) * D + i] = gz;
 }
@@ -550,7 +550,12 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
   }
   hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
   hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH), dim3(kBT), 0, st, b);
-  hipLaunchKernelGGL((k_bwd_update<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
+  if constexpr (BF16) {
+    const hipError_t e = launch_bwd_update_mfma(b, st);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((k_bwd_update<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
+  }
   hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
   hipLaunchKernelGGL((k_bwd_final<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
   hipLaunchKernelGGL(k_bwd_dbeta, dim3(static_cast<unsigned>(w.H)), dim3(kBT), 0, st, b);

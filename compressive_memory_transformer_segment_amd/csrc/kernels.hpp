@@ -110,7 +110,7 @@ struct BackwardArgs {
   float* rpart;          // [U][rch][D][D] sigma(Q)^T dnum over chunks of the segment
   float* rzpart;         // [U][rch][D]    sigma(Q)^T dden
   float* gm;             // [U][D][D]      dL/dM_s (the state after segment s)
-  float* cpart;          // [U][ut][D]     delta: sigma(K)^T ddenk per token tile
+  float* cpart;          // [U][ct][D]     delta: sigma(K)^T ddenk per token tile
   float* gz;             // [U][D]         dL/dz_s
   float* bpart;          // [U * pt]       gate partials
   const float* dm_final; // optional [B,H,D,D] gradient of the final M
@@ -120,11 +120,13 @@ struct BackwardArgs {
   float* dbeta;          // [H]
   int rch;               // token chunks of the R pass per segment
   int pt;                // 64-token tiles per segment (prep, dq, dkv, update, final)
+  int ct;                // token tiles per segment of the cpart partials (pt, or 128-token tiles)
 };
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const BackwardArgs& b, hipStream_t st);    // bf16: dQ (local + retrieval)
 hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, hipStream_t st);   // bf16: dK, dV (local)
+hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st);   // bf16: memory-update part of dK, dV
 
 hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
 hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T
