@@ -826,7 +826,9 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   const int64_t U = int64_t(S) * h->BH;
   const int D = h->D;
   const int pt = (h->N + 63) / 64;
-  int rch = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (512 + U - 1) / U)));
+  // chunks of the sigma(Q)^T dnum pass: 512-token chunks on the matrix-core path
+  int rch = h->bf16 ? std::max(1, (h->N + 511) / 512)
+                    : static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (512 + U - 1) / U)));
   const size_t rows = size_t(h->BH) * size_t(n_tokens);
   // scratch layout (256-byte aligned pieces)
   const size_t sz[] = {

@@ -631,7 +631,118 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
   }
 }
 
+// R_s = sigma(Q)^T dnum and r_s = sigma(Q)^T dden over one chunk of a segment (dnum = g dO /
+// den), the retrieval's contribution to dL/dM_{s-1} and dL/dz_{s-1}: the contraction runs
+// over tokens, so both operands are read from 64-token LDS tiles ([token][d], 16-row
+// groups) by transpose reads; the d x d result is spread over the 4 waves.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_r_mfma(const BackwardArgs b) {
+  constexpr int DB = D / 32, CPR = D / 8, SUB = 64;
+  constexpr int NBW = DB * DB / 4;          // 32 x 32 result blocks per wave
+  constexpr int PH = kBwdThreads / CPR;     // row phases of the tile loads
+  __shared__ __align__(16) uint16_t sq_l[SUB * D];
+  __shared__ __align__(16) uint16_t dn_l[SUB * D];
+  __shared__ float rz_l[PH][D];
+  const WindowArgs& w = b.w;
+  const int u = static_cast<int>(blockIdx.x) / b.rch, ch = static_cast<int>(blockIdx.x) % b.rch;
+  const int BH = w.B * w.H;
+  const int s_local = u / BH, bh = u % BH, h = bh % w.H;
+  const int n = w.seg_tokens(s_local);
+  const int64_t row0 = static_cast<int64_t>(bh) * w.T + static_cast<int64_t>(w.s0 + s_local) * w.N;
+  const int per = (w.N + b.rch - 1) / b.rch;
+  const int t_lo = ch * per, t_hi = min(n, t_lo + per);
+  const float g = w.gate_g[h];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int G = lane >> 4, jl = lane & 15;
+  const int m_rd = (16 * (2 * (G & 1) + ((jl & 3) >> 1)) + 8 * (G >> 1) + (jl >> 2)) * 8 + 4 * (jl & 1);
+  (void)l32;
+
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) acc[k] = zero16();
+  float rzp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rzp[e] = 0.f;
+  const int cl = tid % CPR, rp = tid / CPR;   // this thread's chunk (columns 8 cl ..) and row phase
+  const uint16_t* qg = static_cast<const uint16_t*>(w.q);
+  const uint16_t* og = static_cast<const uint16_t*>(b.dout);
+
+  for (int t0 = t_lo; t0 < t_hi; t0 += SUB) {
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < SUB / PH; ++p) {
+      const int r = p * PH + rp, t = t0 + r;
+      float sv[8], dv[8];
+      if (t < t_hi) {
+        const int64_t x = (row0 + t) * D + 8 * cl;
+        const u32x4 qv = ld16(qg + x), ov = ld16(og + x);
+        const float sc = g / b.den[row0 + t], dz = b.dden[row0 + t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[2 * e] = elu_plus_one(bf16lo_to_f32(qv[e]));
+          sv[2 * e + 1] = elu_plus_one(bf16hi_to_f32(qv[e]));
+          dv[2 * e] = bf16lo_to_f32(ov[e]) * sc;
+          dv[2 * e + 1] = bf16hi_to_f32(ov[e]) * sc;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rzp[e] = fmaf(sv[e], dz, rzp[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = dv[e] = 0.f;
+      }
+      st16(sq_l + rg_index(r, 8 * cl, CPR), u32x4{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
+                                                  pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7])});
+      st16(dn_l + rg_index(r, 8 * cl, CPR), u32x4{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]),
+                                                  pack_bf16x2(dv[4], dv[5]), pack_bf16x2(dv[6], dv[7])});
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < SUB / 16; ++ks) {
+#pragma unroll
+      for (int k = 0; k < NBW; ++k) {
+        const int blk = wave * NBW + k, ib = blk / DB, jb = blk % DB;
+        const uint16_t* pa = sq_l + m_rd + ks * 128 * CPR + ib * 512;
+        const uint16_t* pb = dn_l + m_rd + ks * 128 * CPR + jb * 512;
+        const u32x2 a0 = lds_read_tr16(pa), a1 = lds_read_tr16(pa + 32);
+        const u32x2 b0 = lds_read_tr16(pb), b1 = lds_read_tr16(pb + 32);
+        acc[k] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}),
+                              __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]}), acc[k]);
+      }
+    }
+  }
+  // R block (ib, jb): register r of lane l holds R[32 ib + 8 (r / 4) + 4 hl + r % 4][32 jb + l % 32]
+  float* rpo = b.rpart + (static_cast<int64_t>(u) * b.rch + ch) * D * D;
+  const int hl = lane >> 5;
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) {
+    const int blk = wave * NBW + k, ib = blk / DB, jb = blk % DB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      rpo[(32 * ib + 8 * (r >> 2) + 4 * hl + (r & 3)) * D + 32 * jb + (lane & 31)] = acc[k][r];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rz_l[rp][8 * cl + e] = rzp[e];
+  __syncthreads();
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int p = 0; p < PH; ++p) a += rz_l[p][tid];
+    b.rzpart[(static_cast<int64_t>(u) * b.rch + ch) * D + tid] = a;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_r_mfma(const BackwardArgs& b, hipStream_t st) {
+  const WindowArgs& w = b.w;
+  const dim3 grid(static_cast<unsigned>(w.units() * b.rch)), block(kBwdThreads);
+  if (w.D == 128) hipLaunchKernelGGL((k_bwd_r_mfma<128>), grid, block, 0, st, b);
+  else if (w.D == 64) hipLaunchKernelGGL((k_bwd_r_mfma<64>), grid, block, 0, st, b);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st) {
   const WindowArgs& w = b.w;

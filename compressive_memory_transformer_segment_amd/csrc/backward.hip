@@ -316,15 +316,20 @@ __global__ __launch_bounds__(kBT) void k_bwd_r(const BackwardArgs b) {
   }
 }
 
-// ---- reverse chain of G_s = dL/dM_s over the segments, one workgroup per (batch, head) --
+// ---- reverse chain of G_s = dL/dM_s over the segments.  Columns of G evolve independently
+// under both rules ((I - Gram_s) G acts on each column alone), so one workgroup owns a block
+// of kChainCols columns of one (batch, head) and walks the segments backwards.
+constexpr int kChainCols = 16;
 template <int D>
 __global__ __launch_bounds__(kBT) void k_bwd_chain(const BackwardArgs b) {
-  constexpr int TPRW = kBT / D;          // threads per row
-  constexpr int CPT = D / TPRW;          // columns per thread
-  __shared__ float gl[D][D + 1];
+  constexpr int TPRW = kBT / D;            // threads per row
+  constexpr int CPT = kChainCols / TPRW;   // columns per thread
+  __shared__ float gl[D][kChainCols + 1];
   const WindowArgs& w = b.w;
-  const int bh = static_cast<int>(blockIdx.x), BH = w.B * w.H;
-  const int tid = threadIdx.x, i = tid / TPRW, j0 = (tid % TPRW) * CPT;
+  const int nb = D / kChainCols;
+  const int bh = static_cast<int>(blockIdx.x) / nb, BH = w.B * w.H;
+  const int cb = (static_cast<int>(blockIdx.x) % nb) * kChainCols;
+  const int tid = threadIdx.x, i = tid / TPRW, jl = (tid % TPRW) * CPT, j0 = cb + jl;
   float G[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c)
@@ -337,17 +342,17 @@ __global__ __launch_bounds__(kBT) void k_bwd_chain(const BackwardArgs b) {
     float nG[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) nG[c] = G[c];
-    if (w.delta) {   // (I - Gram_s) G, Gram_s = sum of the forward's chunk partials
+    if (w.delta) {   // (I - Gram_s) G, Gram_s = sum of the forward's chunk partials (symmetric)
       __syncthreads();
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) gl[i][j0 + c] = G[c];
+      for (int c = 0; c < CPT; ++c) gl[i][jl + c] = G[c];
       __syncthreads();
       for (int k = 0; k < D; ++k) {
         float gr = 0.f;
         for (int ch = 0; ch < w.chk; ++ch)
           gr += w.ws.g[((static_cast<int64_t>(u) * w.chk + ch) * D + i) * D + k];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) nG[c] = fmaf(-gr, gl[k][j0 + c], nG[c]);
+        for (int c = 0; c < CPT; ++c) nG[c] = fmaf(-gr, gl[k][jl + c], nG[c]);
       }
     }
     for (int ch = 0; ch < b.rch; ++ch) {
@@ -548,8 +553,13 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((k_bwd_dkv<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
   }
-  hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
-  hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH), dim3(kBT), 0, st, b);
+  if constexpr (BF16) {
+    const hipError_t e = launch_bwd_r_mfma(b, st);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
+  }
+  hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
   if constexpr (BF16) {
     const hipError_t e = launch_bwd_update_mfma(b, st);
     if (e != hipSuccess) return e;

@@ -127,6 +127,7 @@ hipError_t launch_backward(const BackwardArgs& b, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const BackwardArgs& b, hipStream_t st);    // bf16: dQ (local + retrieval)
 hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, hipStream_t st);   // bf16: dK, dV (local)
 hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st);   // bf16: memory-update part of dK, dV
+hipError_t launch_bwd_r_mfma(const BackwardArgs& b, hipStream_t st);        // bf16: sigma(Q)^T dnum, sigma(Q)^T dden
 
 hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
 hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T
