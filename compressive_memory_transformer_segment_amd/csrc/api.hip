@@ -833,15 +833,15 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   // scratch layout (256-byte aligned pieces)
   const size_t sz[] = {
       rows * D * es,                      // 0 forward output
-      rows * D * 4,                       // 1 A_mem
-      rows * D * 4,                       // 2 A_dot
+      h->bf16 ? 0 : rows * D * 4,         // 1 A_mem (the bf16 recomputation needs neither)
+      h->bf16 ? 0 : rows * D * 4,         // 2 A_dot
       rows * 4, rows * 4, rows * 4, rows * 4,   // 3-6 lse, dd, den, dden
       size_t(U) * rch * D * D * 4,        // 7 rpart
       size_t(U) * rch * D * 4,            // 8 rzpart
       size_t(U) * D * D * 4,              // 9 gm
       size_t(U) * pt * D * 4,             // 10 cpart
       size_t(U) * D * 4,                  // 11 gz
-      size_t(U) * pt * 4,                 // 12 bpart
+      rows * 4,                           // 12 per-token gate terms
       size_t(h->BH) * D * D * 4,          // 13 state copy M
       size_t(h->BH) * D * 4,              // 14 state copy z
   };
@@ -888,9 +888,17 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   a.q_loc = q;
   a.k_loc = k;
   a.out = part[0];
-  a.a_mem = static_cast<float*>(part[1]);
-  a.a_dot = static_cast<float*>(part[2]);
   a.lse = static_cast<float*>(part[3]);
+  if (h->bf16) {   // the attention writes the backward's per-token terms directly
+    a.bwd_dout = d_out;
+    a.bwd_dd = static_cast<float*>(part[4]);
+    a.bwd_den = static_cast<float*>(part[5]);
+    a.bwd_dden = static_cast<float*>(part[6]);
+    a.bwd_bq = static_cast<float*>(part[12]);
+  } else {
+    a.a_mem = static_cast<float*>(part[1]);
+    a.a_dot = static_cast<float*>(part[2]);
+  }
   a.B = h->cfg.batch;
   a.H = h->cfg.heads;
   a.D = D;
@@ -934,7 +942,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   bw.gm = static_cast<float*>(part[9]);
   bw.cpart = static_cast<float*>(part[10]);
   bw.gz = static_cast<float*>(part[11]);
-  bw.bpart = static_cast<float*>(part[12]);
+  bw.bq = static_cast<float*>(part[12]);
   bw.dm_final = dm_final;
   bw.dz_final = dz_final;
   bw.dm0 = dm0;

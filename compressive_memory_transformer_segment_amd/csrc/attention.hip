@@ -63,7 +63,11 @@ __device__ __forceinline__ void tile_of_block(int units, int nq, int& u, int& qt
   u = x + 8 * (gi * kGroup + r % g_units);
 }
 
-template <int D, bool PARTS>
+// MODE: 0 = the gated output; 1 = also A_mem, A_dot (fp32) and the log-sum-exp; 2 = the
+// backward's per-token terms instead of the output: log-sum-exp, D = dO . A_dot, the
+// retrieval denominator, its gradient -g dO . A_mem / den, and the gate term
+// g (1 - g) dO . (A_mem - A_dot) (dO given in bwd_dout).
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(const WindowArgs a) {
   constexpr int KS = D / 16;                  // k-steps over the head dimension
   constexpr int DB = D / 32;                  // 32-row blocks of the head dimension
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   uint16_t* ost = buf_at(nkv + 1 + (wave >> 2)) + (wave & 3) * 32 * D;
   const float l_tot = sum_across_halves(l_part);
   const float inv_l = 1.f / l_tot;
-  if constexpr (PARTS) {
+  if constexpr (MODE >= 1) {
     if (a.lse && hl == 0 && q < n) a.lse[row0 + q] = m_run + __log2f(l_tot);
   }
 
@@ -421,6 +425,8 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   den = sum_across_halves(den);
   const float inv_den = 1.f / (den + a.eps);
   const float g = a.gate_g[h], omg = a.gate_omg[h];
+  float ddp = 0.f, emp = 0.f;   // MODE 2: this lane's shares of dO . A_dot and dO . A_mem
+  const uint16_t* dog = MODE == 2 ? static_cast<const uint16_t*>(a.bwd_dout) + (row0 + q) * D : nullptr;
 
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       const float amem = acc_m[r] * inv_den;
       const float adot = acc_o[db][r] * inv_l;
       o[r] = g * amem + omg * adot;
-      if constexpr (PARTS) {
+      if constexpr (MODE == 1) {
         if (q < n) {
           const int dv = 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3);
           const int64_t e = (row0 + q) * D + dv;
@@ -445,10 +451,38 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
         }
       }
     }
+    if constexpr (MODE == 2) {
+      if (q < n) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      st8(ost + l32 * D + 8 * ((4 * db + r4) ^ swz(l32)) + 4 * hl,
-          u32x2{pack_bf16x2(o[4 * r4], o[4 * r4 + 1]), pack_bf16x2(o[4 * r4 + 2], o[4 * r4 + 3])});
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const u32x2 dv = ld8(dog + 32 * db + 8 * r4 + 4 * hl);
+          const float df[4] = {bf16lo_to_f32(dv[0]), bf16hi_to_f32(dv[0]), bf16lo_to_f32(dv[1]), bf16hi_to_f32(dv[1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ddp = fmaf(df[e], acc_o[db][4 * r4 + e] * inv_l, ddp);
+            emp = fmaf(df[e], acc_m[4 * r4 + e] * inv_den, emp);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        st8(ost + l32 * D + 8 * ((4 * db + r4) ^ swz(l32)) + 4 * hl,
+            u32x2{pack_bf16x2(o[4 * r4], o[4 * r4 + 1]), pack_bf16x2(o[4 * r4 + 2], o[4 * r4 + 3])});
+    }
+  }
+  if constexpr (MODE == 2) {
+    ddp = sum_across_halves(ddp);
+    emp = sum_across_halves(emp);
+    if (hl == 0 && q < n) {
+      const int64_t rq = row0 + q;
+      const float dn = den + a.eps;
+      a.bwd_dd[rq] = ddp;
+      a.bwd_den[rq] = dn;
+      a.bwd_dden[rq] = -g * emp / dn;
+      a.bwd_bq[rq] = (emp - ddp) * g * omg;
+    }
+    return;
   }
   // each wave reads back only the rows it staged
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -569,8 +603,9 @@ template <int D>
 hipError_t launch_attention_d(const WindowArgs& a, hipStream_t st) {
   if (a.bf16) {
     const dim3 grid(a.units() * ((a.N + kBMA - 1) / kBMA));
-    if (a.a_mem || a.a_dot || a.lse) hipLaunchKernelGGL((k_attn_bf16<D, true>), grid, dim3(kThreadsA), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_bf16<D, false>), grid, dim3(kThreadsA), 0, st, a);
+    if (a.bwd_dout) hipLaunchKernelGGL((k_attn_bf16<D, 2>), grid, dim3(kThreadsA), 0, st, a);
+    else if (a.a_mem || a.a_dot || a.lse) hipLaunchKernelGGL((k_attn_bf16<D, 1>), grid, dim3(kThreadsA), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_bf16<D, 0>), grid, dim3(kThreadsA), 0, st, a);
   } else {
     const dim3 grid(a.units() * ((a.N + 63) / 64));
     hipLaunchKernelGGL((k_attn_f32<D>), grid, dim3(64 * (D / 32)), 0, st, a);

@@ -82,7 +82,6 @@ __global__ __launch_bounds__(kBT) void k_bwd_prep(const BackwardArgs b) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float g = w.gate_g[p.h], omg = w.gate_omg[p.h];
   const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
-  float bsum = 0.f;
   for (int i = 0; i < kTile / 4; ++i) {
     const int t = tile * kTile + wave * (kTile / 4) + i;
     if (t >= p.n) break;
@@ -102,13 +101,9 @@ __global__ __launch_bounds__(kBT) void k_bwd_prep(const BackwardArgs b) {
       b.dd[row] = dd;
       b.den[row] = dn;
       b.dden[row] = -g * em / dn;
+      b.bq[row] = (em - dd) * g * omg;
     }
-    bsum += em - dd;
   }
-  __shared__ float red[4];
-  if (lane == 0) red[wave] = bsum;
-  __syncthreads();
-  if (threadIdx.x == 0) b.bpart[blockIdx.x] = (red[0] + red[1] + red[2] + red[3]) * g * omg;
 }
 
 // ---- dQ: local attention part (query-parallel) + retrieval part -----------------------
@@ -514,15 +509,14 @@ __global__ __launch_bounds__(kBT) void k_bwd_final(const BackwardArgs b) {
   }
 }
 
-// ---- dbeta: sum of the gate partials of the head's tiles ---------------------------------
+// ---- dbeta: the head's per-token gate terms, summed over batch and tokens ----------------
 __global__ __launch_bounds__(kBT) void k_bwd_dbeta(const BackwardArgs b) {
   const WindowArgs& w = b.w;
-  const int h = static_cast<int>(blockIdx.x), BH = w.B * w.H;
-  const int nblk = w.units() * b.pt;
+  const int h = static_cast<int>(blockIdx.x);
   float acc = 0.f;
-  for (int x = threadIdx.x; x < nblk; x += kBT) {
-    const int u = x / b.pt;
-    if ((u % BH) % w.H == h) acc += b.bpart[x];
+  for (int bb = 0; bb < w.B; ++bb) {
+    const float* x = b.bq + (static_cast<int64_t>(bb) * w.H + h) * w.T;
+    for (int64_t t = threadIdx.x; t < w.T; t += kBT) acc += x[t];
   }
   __shared__ float red[kBT / 64];
   acc = wave_sum(acc);
@@ -540,7 +534,8 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
   const WindowArgs& w = b.w;
   const unsigned tiles = static_cast<unsigned>(w.units() * b.pt);
   const unsigned BH = static_cast<unsigned>(w.B * w.H);
-  hipLaunchKernelGGL((k_bwd_prep<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
+  if constexpr (!BF16)   // (the bf16 forward recomputation writes these terms itself)
+    hipLaunchKernelGGL((k_bwd_prep<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
   if constexpr (BF16) {
     const hipError_t e = launch_bwd_dq_mfma(b, st);
     if (e != hipSuccess) return e;

@@ -27,6 +27,13 @@ struct WindowArgs {
   float* a_dot;      // optional fp32 [B,H,T,D]
   float* lse;        // optional fp32 [B,H,T]: log2 of the softmax row sum, in the scaled
                      // log2 domain (P = exp2(scale log2e q.k - lse)); written with a_mem / a_dot
+  // backward recomputation (bf16): with bwd_dout set the attention writes, instead of the
+  // output, the per-token terms of the gradient, each [B,H,T] fp32 (and lse)
+  const void* bwd_dout;
+  float* bwd_dd;     // dO . A_dot
+  float* bwd_den;    // sigma(q) z_{s-1} + eps
+  float* bwd_dden;   // -g dO . A_mem / den
+  float* bwd_bq;     // g (1 - g) dO . (A_mem - A_dot)
   int B, H, D;
   int64_t T;         // tokens in the call
   int N;             // segment length
@@ -112,7 +119,7 @@ struct BackwardArgs {
   float* gm;             // [U][D][D]      dL/dM_s (the state after segment s)
   float* cpart;          // [U][ct][D]     delta: sigma(K)^T ddenk per token tile
   float* gz;             // [U][D]         dL/dz_s
-  float* bpart;          // [U * pt]       gate partials
+  float* bq;             // [B,H,T]        per-token gate terms g (1 - g) dO . (A_mem - A_dot)
   const float* dm_final; // optional [B,H,D,D] gradient of the final M
   const float* dz_final; // optional [B,H,D]
   float* dm0;            // optional [B,H,D,D] gradient of the initial M
