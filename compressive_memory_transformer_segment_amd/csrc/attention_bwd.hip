@@ -418,8 +418,9 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
 // G_s (fp32) and, for the delta rule, M_{s-1} are staged in LDS as bf16 in both orientations
 // (16-row-group layout); sigma(K) and V come from registers; the (V - R) and dW results are
 // the B operands of the last products, with G_s and M_{s-1} read in the order their
-// registers hold.  dV, dK are updated in place (fp32); the tile's sigma(K)^T ddenk partial
-// goes to cpart.
+// registers hold.  dV, dK are updated in place (fp32); for the linear rule dK also receives
+// dL/dz_s sigma'(K) here (the z chain has run); for the delta rule the tile's
+// sigma(K)^T ddenk partial goes to cpart and the z term is added by a later pass.
 __device__ __forceinline__ int rg_index(int r, int c, int cpr) {
   return ((r >> 4) * 16 * cpr + 16 * (c >> 3) + (r & 15)) * 8 + (c & 7);
 }
@@ -489,6 +490,7 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
   const uint16_t* kr = static_cast<const uint16_t*>(w.k) + row * D;
   const uint16_t* vr = static_cast<const uint16_t*>(w.v) + row * D;
   const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
+  const float* gzb = b.gz + static_cast<int64_t>(u) * D;   // linear: computed before this kernel
 
   // sigma(k) of this lane's token as the B operand (k = i natural), and sigma(k) . z
   bf16x8 wreg[KS];
@@ -620,6 +622,7 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
         for (int e = 0; e < 4; ++e) {
           float a = S[ib][4 * r4 + e];
           if constexpr (DELTA) a = fmaf(ddk, zb[i0 + e], a);
+          else a += gzb[i0 + e];   // linear: dL/dz_s reaches every token of the segment
           o[e] += a * (kf[e] > 0.f ? 1.f : __builtin_amdgcn_exp2f(kf[e] * kLog2e));
         }
         *pk = o;

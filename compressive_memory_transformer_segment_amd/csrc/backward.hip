@@ -510,21 +510,22 @@ __global__ __launch_bounds__(kBT) void k_bwd_final(const BackwardArgs b) {
 }
 
 // ---- dbeta: the head's per-token gate terms, summed over batch and tokens ----------------
-__global__ __launch_bounds__(kBT) void k_bwd_dbeta(const BackwardArgs b) {
+constexpr int kBetaThreads = 1024;
+__global__ __launch_bounds__(kBetaThreads) void k_bwd_dbeta(const BackwardArgs b) {
   const WindowArgs& w = b.w;
   const int h = static_cast<int>(blockIdx.x);
   float acc = 0.f;
   for (int bb = 0; bb < w.B; ++bb) {
     const float* x = b.bq + (static_cast<int64_t>(bb) * w.H + h) * w.T;
-    for (int64_t t = threadIdx.x; t < w.T; t += kBT) acc += x[t];
+    for (int64_t t = threadIdx.x; t < w.T; t += kBetaThreads) acc += x[t];
   }
-  __shared__ float red[kBT / 64];
+  __shared__ float red[kBetaThreads / 64];
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) {
     float t = 0.f;
-    for (int i = 0; i < kBT / 64; ++i) t += red[i];
+    for (int i = 0; i < kBetaThreads / 64; ++i) t += red[i];
     b.dbeta[h] = t;
   }
 }
@@ -555,15 +556,23 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
     hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
   }
   hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
-  if constexpr (BF16) {
+  if (BF16 && !w.delta) {
+    // linear: g_s needs only the R pass, so the z chain runs first and the update kernel
+    // adds g_s sigma'(K) to dK itself
+    hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
     const hipError_t e = launch_bwd_update_mfma(b, st);
     if (e != hipSuccess) return e;
   } else {
-    hipLaunchKernelGGL((k_bwd_update<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
+    if constexpr (BF16) {
+      const hipError_t e = launch_bwd_update_mfma(b, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL((k_bwd_update<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
+    }
+    hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
+    hipLaunchKernelGGL((k_bwd_final<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
   }
-  hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
-  hipLaunchKernelGGL((k_bwd_final<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
-  hipLaunchKernelGGL(k_bwd_dbeta, dim3(static_cast<unsigned>(w.H)), dim3(kBT), 0, st, b);
+  hipLaunchKernelGGL(k_bwd_dbeta, dim3(static_cast<unsigned>(w.H)), dim3(kBetaThreads), 0, st, b);
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import csv
 import hashlib
+import re
 import os
 import sys
 from collections import defaultdict
@@ -86,13 +87,9 @@ def kernel_source_hash() -> str:
 
 def _short(name: str) -> str:
     """Kernel name without namespaces and argument list, template arguments kept."""
-    for key in ("k_attn_bf16", "k_attn_f32", "k_state_bf16", "k_state_f32", "k_keysum_f32",
-                "k_chain_linear", "k_chain_delta", "k_zero_f32"):
-        i = name.find(key)
-        if i >= 0:
-            rest = name[i:]
-            j = rest.find("(")
-            return rest[:j] if j >= 0 else rest
+    m = re.search(r"infini::(?:\(anonymous namespace\)::)?(k_\w+(?:<[^>]*>)?)", name)
+    if m:
+        return m.group(1)
     if "copyBuffer" in name:
         return "__amd_rocclr_copyBuffer"
     if "direct_copy_kernel" in name:
