@@ -344,12 +344,12 @@ def main_backward(args):
                    "segment_len": w.segment_len, "n_tokens": w.n_tokens, "update": w.update,
                    "step": "infini_attn_backward: forward recomputed, then all gradients", "parallelism": "none"},
         "roofline": {
-            "kernel": "gradient kernels of one backward call (fp32 SIMT)",
-            "bound": "alu",
+            "kernel": "gradient kernels of one backward call (bf16 matrix-core products, fp32 chains)",
+            "bound": "mfma",
             "achieved": achieved,
-            "peak": 157.3,
+            "peak": profiling.PEAK_BF16_FLOPS / 1e12,
             "unit": "TFLOP/s",
-            "frac": achieved / 157.3,
+            "frac": achieved / (profiling.PEAK_BF16_FLOPS / 1e12),
             "traffic": None,
             "algorithmic_flops": fl,
             "avg_launch_us": bwd_ms / bwd_n * 1e3,
