@@ -247,6 +247,193 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
   }
 }
 
+// Linear rule, bf16 inputs: a warp-specialised version of the pass above.  Waves 0-7
+// produce (two per SIMD, so that each SIMD has independent exponential chains to
+// interleave) and waves 8-11 consume.  Per 64-token stage the producers turn K into sigma(K),
+// split into bf16 hi + lo, and stage it with V in LDS, two stages deep; meanwhile the
+// consumers accumulate U^T += V^T sigma(K) on the matrix cores from the other stage, so
+// the exponentials and the products run side by side.  Producers keep their global loads
+// three stages ahead in four register sets; the stage count is rounded up to a multiple
+// of four (rows past the chunk end read as zeros and add nothing), so the loop body is
+// straight-line code and the compiler's load waits stay exact.  One barrier per stage.
+// The partial sums go out as in k_state_bf16: one slot per (unit, chunk), added in chunk
+// order by the chain.
+constexpr int kProdWaves = 8;
+constexpr int kLinThreads = 64 * (kProdWaves + 4);
+template <int D>
+__global__ __launch_bounds__(kLinThreads, 1) void k_state_lin_bf16(const WindowArgs a) {
+  constexpr int P = D + 32;              // LDS row pitch (elements): conflict-free transpose reads
+  constexpr int DQ = D / 8;              // producer threads per token row (8 features each)
+  constexpr int TQ = 64 * kProdWaves / DQ;   // producer row groups
+  constexpr int RPT = kSub / TQ;         // rows per producer thread per stage
+  constexpr int BB = D / 64;             // 32x32 output blocks per consumer wave, per dimension
+  __shared__ __align__(16) uint16_t hi_s[2][kSub][P];
+  __shared__ __align__(16) uint16_t lo_s[2][kSub][P];
+  __shared__ __align__(16) uint16_t v_s[2][kSub][P];
+  __shared__ float red[TQ][D];
+
+  const int u = blockIdx.x / a.chk;
+  const int c = blockIdx.x % a.chk;
+  const UnitPos p = unit_pos(a, u);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int t_begin = c * a.ch;
+  const int t_end = min(t_begin + a.ch, p.n);
+  const int ns = t_end > t_begin ? ((t_end - t_begin + 4 * kSub - 1) / (4 * kSub)) * 4 : 0;   // stages
+  const int64_t slot = static_cast<int64_t>(u) * a.chk + c;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+
+  if (wave < kProdWaves) {
+    // ---------------------------------------------------------------- producers
+    const int dq = tid % DQ, tq = tid / DQ;
+    // the segment's K and V rows up to the chunk end; rows past it read as zeros (V = 0
+    // there, so the padded rows add nothing to U; the key sums skip them)
+    const int64_t seg_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
+    const auto krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + seg_base, static_cast<uint32_t>(t_end) * D * 2);
+    const auto vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + seg_base, static_cast<uint32_t>(t_end) * D * 2);
+    float zacc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
+    auto load = [&](int s, u32x4 (&kd)[RPT], u32x4 (&vd)[RPT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const uint32_t off = (static_cast<uint32_t>(t_begin + s * kSub + tq * RPT + r) * D + dq * 8) * 2;
+        kd[r] = buffer_ld16(krs, off);
+        vd[r] = buffer_ld16(vrs, off);
+      }
+    };
+    // stage s: sigma(K) hi / lo and V into LDS buffer s % 2, key sums of the real rows
+    auto convert = [&](int s, const u32x4 (&kd)[RPT], const u32x4 (&vd)[RPT]) __attribute__((always_inline)) {
+      const int b = s & 1;
+      const int ts = t_begin + s * kSub;
+      const bool whole = ts + kSub <= t_end;   // wave-uniform: no padded rows in this stage
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const int tl = tq * RPT + r;
+        float sk[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sk[2 * i] = elu_plus_one(bf16lo_to_f32(kd[r][i]));
+          sk[2 * i + 1] = elu_plus_one(bf16hi_to_f32(kd[r][i]));
+        }
+        if (whole || ts + tl < t_end) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) zacc[i] += sk[i];
+        }
+        u32x4 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = pack_bf16x2(sk[2 * i], sk[2 * i + 1]);
+          lo[i] = pack_bf16x2(sk[2 * i] - bf16lo_to_f32(hi[i]), sk[2 * i + 1] - bf16hi_to_f32(hi[i]));
+        }
+        st16(&hi_s[b][tl][dq * 8], hi);
+        st16(&lo_s[b][tl][dq * 8], lo);
+        st16(&v_s[b][tl][dq * 8], vd[r]);
+      }
+    };
+    // stage s waits in register set s % 4 from its load until its conversion; step i
+    // stages i + 1 into the buffer the consumers read in step i - 1
+    u32x4 k0[RPT], v0[RPT], k1[RPT], v1[RPT], k2[RPT], v2[RPT], k3[RPT], v3[RPT];
+    if (ns > 0) {
+      load(0, k0, v0);
+      load(1, k1, v1);
+      load(2, k2, v2);
+      load(3, k3, v3);
+      convert(0, k0, v0);
+      load(4, k0, v0);
+    }
+    __syncthreads();   // stage 0 staged
+    for (int i = 0; i < ns; i += 4) {
+      convert(i + 1, k1, v1);
+      load(i + 5, k1, v1);
+      __syncthreads();
+      convert(i + 2, k2, v2);
+      load(i + 6, k2, v2);
+      __syncthreads();
+      convert(i + 3, k3, v3);
+      load(i + 7, k3, v3);
+      __syncthreads();
+      convert(i + 4, k0, v0);
+      load(i + 8, k0, v0);
+      __syncthreads();
+    }
+    // key sums: reduce the per-thread partials over the row groups (in group order)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
+  } else {
+    // ---------------------------------------------------------------- consumers
+    // consumer wave cw owns the BB x BB blocks (ib0 + bi, jb0 + bj) of U^T
+    const int cw = wave - kProdWaves;
+    const int ib0 = BB * (cw >> 1), jb0 = BB * (cw & 1);
+    f32x16 acc[BB][BB];
+#pragma unroll
+    for (int bi = 0; bi < BB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BB; ++bj) acc[bi][bj] = zero16();
+    __syncthreads();   // stage 0 staged
+    // operands of one 16-token k-step: V^T rows (av), sigma(K) hi and lo columns
+    struct Ops {
+      bf16x8 av[BB], bh[BB], bl[BB];
+    };
+    auto fetch = [&](int b, int ks, Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bi = 0; bi < BB; ++bi) o.av[bi] = lds_operand_tr(&v_s[b][0][0], P, 16 * ks, 32 * (ib0 + bi), lane);
+#pragma unroll
+      for (int bj = 0; bj < BB; ++bj) {
+        o.bh[bj] = lds_operand_tr(&hi_s[b][0][0], P, 16 * ks, 32 * (jb0 + bj), lane);
+        o.bl[bj] = lds_operand_tr(&lo_s[b][0][0], P, 16 * ks, 32 * (jb0 + bj), lane);
+      }
+    };
+    auto multiply = [&](const Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bi = 0; bi < BB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BB; ++bj) {
+          acc[bi][bj] = mfma32x32x16(o.av[bi], o.bh[bj], acc[bi][bj]);
+          acc[bi][bj] = mfma32x32x16(o.av[bi], o.bl[bj], acc[bi][bj]);
+        }
+    };
+    static_assert(kSub == 64, "four k-steps per stage");
+    for (int i = 0; i < ns; ++i) {
+      // the operands of k-step ks + 2 are read while k-step ks multiplies
+      const int b = i & 1;
+      Ops o0, o1;
+      fetch(b, 0, o0);
+      fetch(b, 1, o1);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(o0);
+      fetch(b, 2, o0);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(o1);
+      fetch(b, 3, o1);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(o0);
+      multiply(o1);
+      __syncthreads();
+    }
+    // U^T partial: register r of block (ib, jb) holds row 32 ib + 8 (r / 4) + 4 (lane / 32)
+    // + r % 4, column 32 jb + lane % 32
+    float* u_dst = a.ws.u + slot * DD;
+    const int hl = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int bi = 0; bi < BB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BB; ++bj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * (ib0 + bi) + 8 * (r >> 2) + 4 * hl + (r & 3);
+          u_dst[row * D + 32 * (jb0 + bj) + l32] = acc[bi][bj][r];
+        }
+  }
+  __syncthreads();   // the producers' key-sum partials are in red
+  for (int d = tid; d < D; d += kLinThreads) {
+    float sum = 0.f;
+    for (int g = 0; g < TQ; ++g) sum += red[g][d];
+    a.ws.dz[slot * D + d] = sum;
+  }
+}
+
 // ------------------------------------------------------------------ float32 I/O path
 // One workgroup per unit (no chunking).  Thread (bi, bj) owns a TB x TB block of U (and
 // G); tokens are staged in LDS 32 at a time.
@@ -335,7 +522,7 @@ hipError_t launch_state_d(const WindowArgs& a, hipStream_t st, int mode) {
   if (a.bf16) {
     const dim3 grid(a.units() * a.chk);
     if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_state_bf16<D, MODE_KEYSUM>), grid, dim3(kThreads), 0, st, a);
-    else if (mode == MODE_LINEAR) hipLaunchKernelGGL((k_state_bf16<D, MODE_LINEAR>), grid, dim3(kThreads), 0, st, a);
+    else if (mode == MODE_LINEAR) hipLaunchKernelGGL((k_state_lin_bf16<D>), grid, dim3(kLinThreads), 0, st, a);
     else hipLaunchKernelGGL((k_state_bf16<D, MODE_DELTA>), grid, dim3(kThreads), 0, st, a);
   } else {
     const dim3 grid(a.units());
