@@ -60,7 +60,9 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
 #pragma unroll
           for (int e = 0; e < EPT; ++e) ut[sb][c][e] = src[e];
         }
-        dzv[sb][c] = zown ? a.ws.dz[slot * D + tid] : 0.f;
+        // every thread loads (threads past D re-read the first D; only owners use them):
+        // a load under the owner test made the compiler wait for each one before the next
+        dzv[sb][c] = a.ws.dz[slot * D + (tid & (D - 1))];
       }
     }
 #pragma unroll
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
       for (int e = 0; e < EPT; ++e) up[e][c] = a.ws.u[(u * CHK + c) * DD + static_cast<int64_t>(dv) * D + cg + CG * e];
     float dzp[CHK];
 #pragma unroll
-    for (int c = 0; c < CHK; ++c) dzp[c] = zown ? a.ws.dz[(u * CHK + c) * D + tid] : 0.f;
+    for (int c = 0; c < CHK; ++c) dzp[c] = a.ws.dz[(u * CHK + c) * D + (tid & (D - 1))];   // used by owners only
     // record the state this segment reads
     if constexpr (BF16) {
       uint16_t* mt = static_cast<uint16_t*>(a.ws.mt) + off;
