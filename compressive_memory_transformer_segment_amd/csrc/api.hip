@@ -110,6 +110,7 @@ size_t unit_bytes(const infini_attn& h) {
   size_t b = 0;
   b += DD * (h.bf16 ? 2 : 4);        // mt
   b += D * 4;                        // zb
+  if (h.delta) b += DD * 4;          // gs
   return b + part_bytes(h);          // at least one chunk slot per unit
 }
 int chunks_for(const infini_attn& h, int w_call) {
@@ -134,6 +135,7 @@ void layout(const infini_attn& h, F&& take) {
   take(0, P * D * 4);                                // dz
   take(1, P * DD * 4);                               // u
   take(2, h.delta ? P * DD * 4 : 0);                 // g
+  take(3, h.delta ? U * DD * 4 : 0);                 // gs
   take(4, U * DD * (h.bf16 ? 2 : 4));                // mt
   take(5, U * D * 4);                                // zb
 }
@@ -154,6 +156,7 @@ void carve(infini_attn& h) {
   h.ws.dz = static_cast<float*>(ptrs[0]);
   h.ws.u = static_cast<float*>(ptrs[1]);
   h.ws.g = static_cast<float*>(ptrs[2]);
+  h.ws.gs = static_cast<float*>(ptrs[3]);
   h.ws.mt = ptrs[4];
   h.ws.zb = static_cast<float*>(ptrs[5]);
   h.ws_bytes = static_cast<size_t>(p - static_cast<char*>(h.ws_base));

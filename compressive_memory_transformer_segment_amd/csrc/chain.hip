@@ -105,128 +105,151 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
   if (zown) a.z[static_cast<int64_t>(bh) * D + tid] = z;
 }
 
-// Delta rule: each step needs the workgroup's rows of M^T in full and all of G_s.
-// Thread (r, cg) owns row rb + r and columns cg + CG*e (strided, so that lanes read
-// consecutive rows of G in LDS).  All loads of a step that do not depend on the chain (the
-// U^T, dz and G partials) are issued in batches before they are used.
-template <int D, int EPT, int CHK, bool BF16>
-__global__ __launch_bounds__(kThreads) void k_chain_delta(const WindowArgs a) {
-  constexpr int CG = D / EPT;
-  constexpr int RB = kThreads / CG;
-  constexpr int GP = D + 4;               // LDS row pitch of G (floats)
-  constexpr int MP = D + 4;               // LDS row pitch of the M^T rows
-  constexpr int IT = D * D / 4 / kThreads;   // float4 elements of G per thread
-  constexpr int NB4 = CHK >= 8 ? 2 : 4;      // float4 elements per load batch
-  static_assert(IT % NB4 == 0, "whole batches");
-  __shared__ __align__(16) float g_lds[D][GP];
-  __shared__ __align__(16) float m_lds[RB][MP];
+// Delta rule, G_s summed over the chunks beforehand (k_gsum).  A workgroup owns four
+// rows of M^T of one (b,h); thread (r, i) owns row rb + r, column i (the row is the same
+// for the whole wave, so the reads of M^T rows are broadcasts; thread i reads row i of
+// G_s).  Nothing but M^T itself depends on the chain, so step s + 1's G and U^T / key-sum
+// partials are loaded into registers while step s multiplies, and G_{s+1} is staged into
+// the other of two LDS buffers at the end of step s.  One barrier per step.  Two waves
+// per SIMD, so that one wave's LDS latency is covered by the other's FMAs.  Rows of M^T
+// evolve independently, so workgroups never wait on each other.
+template <int D, int CHK, bool BF16>
+__global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, const float* __restrict__ gsum) {
+  constexpr int NT = 4 * D;
+  constexpr int GP = D + 4;               // LDS row pitch of G and of the M^T rows (floats)
+  constexpr int GV = D * D / 4 / NT;      // float4 elements of G_s per thread
+  __shared__ __align__(16) float g_lds[2][D][GP];
+  __shared__ __align__(16) float m_lds[2][4][GP];
 
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x / (D / RB);
-  const int rb = (blockIdx.x % (D / RB)) * RB;
+  const int W = a.W;
+  const int bh = blockIdx.x / (D / 4);
+  const int rb = (blockIdx.x % (D / 4)) * 4;
   const int tid = threadIdx.x;
-  const int r = tid / CG, cg = tid % CG;
-  const int dv = rb + r;
+  const int r = tid / D, i = tid % D;     // r is wave-uniform (D is a multiple of 64)
+  const int row = rb + r;                 // this thread's row of M^T
   const int64_t DD = static_cast<int64_t>(D) * D;
 
-  float m[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) m[e] = a.zero_state ? 0.f : a.M[bh * DD + static_cast<int64_t>(cg + CG * e) * D + dv];
+  // M^T[row][i] = M[i][row]
+  float m = a.zero_state ? 0.f : a.M[bh * DD + static_cast<int64_t>(i) * D + row];
   const bool zown = rb == 0 && tid < D;
   float z = zown && !a.zero_state ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
 
-  for (int s = 0; s < a.W; ++s) {
-    const int64_t u = static_cast<int64_t>(s) * BH + bh;
-    const int64_t off = u * DD + static_cast<int64_t>(dv) * D;
-    // this step's U^T and dz partials
-    float up[EPT][CHK];
+  // what one step loads ahead of the chain
+  struct Pre {
+    f32x4 g[GV];
+    float up[CHK];
+    float dz[CHK];
+  };
+  auto fetch = [&](int s, Pre& p) __attribute__((always_inline)) {
+    const int64_t u = static_cast<int64_t>(min(s, W - 1)) * BH + bh;
+    const float* src = gsum + u * DD;
 #pragma unroll
-    for (int c = 0; c < CHK; ++c)
+    for (int v = 0; v < GV; ++v) p.g[v] = *reinterpret_cast<const f32x4*>(src + 4 * (tid + v * NT));
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) up[e][c] = a.ws.u[(u * CHK + c) * DD + static_cast<int64_t>(dv) * D + cg + CG * e];
-    float dzp[CHK];
-#pragma unroll
-    for (int c = 0; c < CHK; ++c) dzp[c] = a.ws.dz[(u * CHK + c) * D + (tid & (D - 1))];   // used by owners only
-    // record the state this segment reads
-    if constexpr (BF16) {
-      uint16_t* mt = static_cast<uint16_t*>(a.ws.mt) + off;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) mt[cg + CG * e] = f32_to_bf16(m[e]);
-    } else {
-      float* mt = static_cast<float*>(a.ws.mt) + off;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) mt[cg + CG * e] = m[e];
+    for (int c = 0; c < CHK; ++c) {
+      p.up[c] = a.ws.u[(u * CHK + c) * DD + static_cast<int64_t>(row) * D + i];
+      p.dz[c] = a.ws.dz[(u * CHK + c) * D + i];   // used by owners only
     }
+  };
+  auto stage = [&](int b, const Pre& p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < GV; ++v) {
+      const int e = 4 * (tid + v * NT);
+      *reinterpret_cast<f32x4*>(&g_lds[b][e / D][e % D]) = p.g[v];
+    }
+  };
+  // step s of the chain: p holds step s's partials, G_s is in LDS buffer s % 2, and nx
+  // holds step s + 1's loads (its G is staged at the end)
+  auto step = [&](int s, const Pre& p, const Pre& nx) __attribute__((always_inline)) {
+    const int b = s & 1;
+    const int64_t u = static_cast<int64_t>(s) * BH + bh;
+    // record the state this segment reads
+    const int64_t off = u * DD + static_cast<int64_t>(row) * D + i;
+    if constexpr (BF16) static_cast<uint16_t*>(a.ws.mt)[off] = f32_to_bf16(m);
+    else static_cast<float*>(a.ws.mt)[off] = m;
     if (zown) {
       a.ws.zb[u * D + tid] = z;
       float dz = 0.f;
 #pragma unroll
-      for (int c = 0; c < CHK; ++c) dz += dzp[c];
+      for (int c = 0; c < CHK; ++c) dz += p.dz[c];
       z += dz;
     }
-    // stage G_s (sum of the chunk partials, in chunk order) and the rows of M^T
-#pragma unroll
-    for (int b = 0; b < IT; b += NB4) {
-      f32x4 gp[NB4][CHK];
-#pragma unroll
-      for (int i = 0; i < NB4; ++i) {
-        const int e4 = tid + (b + i) * kThreads;
-        const int row = (e4 * 4) / D, col = (e4 * 4) % D;
-#pragma unroll
-        for (int c = 0; c < CHK; ++c)
-          gp[i][c] = *reinterpret_cast<const f32x4*>(a.ws.g + (u * CHK + c) * DD + row * D + col);
-      }
-#pragma unroll
-      for (int i = 0; i < NB4; ++i) {
-        const int e4 = tid + (b + i) * kThreads;
-        const int row = (e4 * 4) / D, col = (e4 * 4) % D;
-        f32x4 gs = gp[i][0];
-#pragma unroll
-        for (int c = 1; c < CHK; ++c) gs += gp[i][c];
-        *reinterpret_cast<f32x4*>(&g_lds[row][col]) = gs;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) m_lds[r][cg + CG * e] = m[e];
-    __syncthreads();
-    // (M^T G^T)[dv][i] = sum_k M^T[dv][k] G[i][k]
-    float acc[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+    m_lds[b][r][i] = m;
+    __syncthreads();   // G_s and this step's rows of M^T are in LDS
+    // (M^T G^T)[row][i] = sum_k M^T[row][k] G[i][k], as four interleaved partial sums
+    // (k mod 4); k in blocks of 16 whose 8 LDS reads are issued together
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
-    for (int k = 0; k < D; k += 4) {
-      const f32x4 mk = *reinterpret_cast<const f32x4*>(&m_lds[r][k]);
+    for (int kk = 0; kk < D; kk += 16) {
+      f32x4 gk[4], mk[4];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const f32x4 gk = *reinterpret_cast<const f32x4*>(&g_lds[cg + CG * e][k]);
-        acc[e] += mk[0] * gk[0] + mk[1] * gk[1] + mk[2] * gk[2] + mk[3] * gk[3];
+      for (int j = 0; j < 4; ++j) {
+        gk[j] = *reinterpret_cast<const f32x4*>(&g_lds[b][i][kk + 4 * j]);
+        mk[j] = *reinterpret_cast<const f32x4*>(&m_lds[b][r][kk + 4 * j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(mk[j][e], gk[j][e], acc[e]);
+    }
+    float ut = 0.f;
+#pragma unroll
+    for (int c = 0; c < CHK; ++c) ut += p.up[c];
+    m = (m - ((acc[0] + acc[1]) + (acc[2] + acc[3]))) + ut;
+    // G_{s+1} into the buffer step s - 1 read (every thread is past this step's barrier)
+    stage(b ^ 1, nx);
+  };
+
+  // two register sets: step s's partials in one, step s + 1's loads in the other
+  if (W > 0) {
+    Pre pa, pb;
+    fetch(0, pa);
+    stage(0, pa);
+    for (int s = 0; s < W; s += 2) {
+      fetch(s + 1, pb);
+      step(s, pa, pb);
+      if (s + 1 < W) {
+        fetch(s + 2, pa);
+        step(s + 1, pb, pa);
       }
     }
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      float ut = 0.f;
-#pragma unroll
-      for (int c = 0; c < CHK; ++c) ut += up[e][c];
-      m[e] = (m[e] - acc[e]) + ut;
-    }
-    __syncthreads();
   }
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) a.M[bh * DD + static_cast<int64_t>(cg + CG * e) * D + dv] = m[e];
+  a.M[bh * DD + static_cast<int64_t>(i) * D + row] = m;
   if (zown) a.z[static_cast<int64_t>(bh) * D + tid] = z;
+}
+
+// G_s = sum of its chunk partials, in chunk order (the order the state pass's partials were
+// always added in), for every unit of the window.
+template <int D>
+__global__ __launch_bounds__(256) void k_gsum(const WindowArgs a) {
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t e4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // float4 index
+  if (e4 >= static_cast<int64_t>(a.W) * a.B * a.H * (DD / 4)) return;
+  const int64_t u = e4 / (DD / 4), w = 4 * (e4 % (DD / 4));
+  f32x4 sum = *reinterpret_cast<const f32x4*>(a.ws.g + u * a.chk * DD + w);
+  for (int c = 1; c < a.chk; ++c) sum += *reinterpret_cast<const f32x4*>(a.ws.g + (u * a.chk + c) * DD + w);
+  *reinterpret_cast<f32x4*>(a.ws.gs + u * DD + w) = sum;
 }
 
 template <int D>
 hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   if (a.delta) {
-    constexpr int EPT = 16 * D / kThreads;        // 16 rows of M^T per workgroup
-    const dim3 grid(BH * (D / 16));
-    if (!a.bf16) hipLaunchKernelGGL((k_chain_delta<D, EPT, 1, false>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_delta<D, EPT, 1, true>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_delta<D, EPT, 2, true>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_delta<D, EPT, 4, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_chain_delta<D, EPT, 8, true>), grid, dim3(kThreads), 0, st, a);
+    // with several chunks, sum the Gram partials once instead of in every workgroup
+    const float* gsum = a.ws.g;
+    if (a.chk > 1) {
+      const int64_t n4 = static_cast<int64_t>(a.W) * BH * D * D / 4;
+      hipLaunchKernelGGL((k_gsum<D>), dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, a);
+      gsum = a.ws.gs;
+    }
+    const dim3 grid(BH * (D / 4));
+    const dim3 block(4 * D);
+    if (!a.bf16) hipLaunchKernelGGL((k_chain_delta<D, 1, false>), grid, block, 0, st, a, gsum);
+    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_delta<D, 1, true>), grid, block, 0, st, a, gsum);
+    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_delta<D, 2, true>), grid, block, 0, st, a, gsum);
+    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_delta<D, 4, true>), grid, block, 0, st, a, gsum);
+    else hipLaunchKernelGGL((k_chain_delta<D, 8, true>), grid, block, 0, st, a, gsum);
   } else {
     constexpr int EPT = 2;
     constexpr int RB = kThreads / (D / EPT);

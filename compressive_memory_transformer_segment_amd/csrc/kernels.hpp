@@ -12,6 +12,7 @@ struct Workspace {
   float* dz;        // [U][CHK][D]    per-chunk key sums  sum_t sigma(k_t)
   float* u;         // [U][CHK][D][D] per-chunk (sigma(K)^T V)^T: [d_value][d_key]
   float* g;         // [U][CHK][D][D] per-chunk sigma(K)^T diag(1/den) sigma(K) (delta): [d_key][d_key]
+  float* gs;        // [U][D][D]      the same summed over the chunks (delta, bf16, CHK > 1)
   void* mt;         // [U][D][D]      M_{s-1} transposed ([d_value][d_key]); bf16 or f32
   float* zb;        // [U][D]         z_{s-1}
 };
