@@ -78,10 +78,9 @@ bool live(const infini_attn* h) {
 
 constexpr size_t kDefaultWorkspaceBudget = size_t(512) << 20;   // bytes
 constexpr int kMaxWindow = 64;
-// Workgroups the state pass aims for (segments x chunks): the delta rule's pass runs two
-// 4-wave workgroups per compute unit; the linear rule's bf16 pass one 12-wave workgroup.
-constexpr int kStateTargetWorkgroups = 512;
-constexpr int kStateTargetWorkgroupsLinear = 256;
+// Workgroups the bf16 state pass aims for (segments x chunks): one warp-specialised
+// workgroup per compute unit.
+constexpr int kStateTargetWorkgroups = 256;
 
 struct DeviceGuard {
   int prev = -1;
@@ -118,8 +117,7 @@ int chunks_for(const infini_attn& h, int w_call) {
   const int units = w_call * h.BH;
   // a power of two (the chain kernel is specialised on it), at most 8, and no more chunks
   // than 64-token sub-tiles
-  const int target = h.delta ? kStateTargetWorkgroups : kStateTargetWorkgroupsLinear;
-  const int want = (target + units - 1) / units;
+  const int want = (kStateTargetWorkgroups + units - 1) / units;
   int chk = 1;
   while (chk * 2 <= want && chk * 2 <= 8 && chk * 2 <= std::max(1, h.NP / 64) && w_call * chk * 2 <= h.part_cap)
     chk *= 2;

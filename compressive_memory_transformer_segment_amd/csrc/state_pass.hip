@@ -434,6 +434,203 @@ __global__ __launch_bounds__(kLinThreads, 1) void k_state_lin_bf16(const WindowA
   }
 }
 
+// Delta rule, bf16 inputs: the warp-specialised layout of k_state_lin_bf16 with the Gram
+// term.  Waves 0-3 produce: per 32-token stage they form sigma(K), the row weights
+// 1 / (sigma(k_t) . z_{s-1} + eps) and sigma(K) scaled by them, split both into bf16 hi + lo,
+// and stage them with V in LDS, two stages deep (their global loads run three stages
+// ahead in registers).  Waves 4-7 consume: each owns a 2 x 2 group of 32 x 32 blocks of U^T
+// (hi and lo MFMAs) and of G (hi*hi + hi*lo + lo*hi).  One barrier per stage; the stage
+// count is rounded up to a multiple of four as in the linear kernel.
+constexpr int kSubD = 32;                 // tokens per stage
+template <int D>
+__global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a) {
+  constexpr int P = D + 32;              // LDS row pitch (elements): conflict-free transpose reads
+  constexpr int DQ = D / 8;              // producer threads per token row (8 features each)
+  constexpr int TQ = 256 / DQ;           // producer row groups
+  constexpr int RPT = kSubD / TQ;        // rows per producer thread per stage
+  constexpr int BB = D / 64;             // 32x32 blocks per consumer wave, per dimension
+  static_assert(RPT >= 1, "a producer thread owns at least one row");
+  __shared__ __align__(16) uint16_t hi_s[2][kSubD][P];
+  __shared__ __align__(16) uint16_t lo_s[2][kSubD][P];
+  __shared__ __align__(16) uint16_t dh_s[2][kSubD][P];
+  __shared__ __align__(16) uint16_t dl_s[2][kSubD][P];
+  __shared__ __align__(16) uint16_t v_s[2][kSubD][P];
+  __shared__ float zprev[D];
+  __shared__ float red[TQ][D];
+
+  const int u = blockIdx.x / a.chk;
+  const int c = blockIdx.x % a.chk;
+  const UnitPos p = unit_pos(a, u);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int t_begin = c * a.ch;
+  const int t_end = min(t_begin + a.ch, p.n);
+  const int ns = t_end > t_begin ? ((t_end - t_begin + 4 * kSubD - 1) / (4 * kSubD)) * 4 : 0;   // stages
+  const int64_t slot = static_cast<int64_t>(u) * a.chk + c;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+
+  z_before<D>(a, p, zprev);
+  __syncthreads();
+
+  if (wave < 4) {
+    // ---------------------------------------------------------------- producers
+    const int dq = tid % DQ, tq = tid / DQ;
+    const int64_t seg_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
+    const auto krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + seg_base, static_cast<uint32_t>(t_end) * D * 2);
+    const auto vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + seg_base, static_cast<uint32_t>(t_end) * D * 2);
+    float zp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zp[i] = zprev[dq * 8 + i];
+    float zacc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
+    auto load = [&](int s, u32x4 (&kd)[RPT], u32x4 (&vd)[RPT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const uint32_t off = (static_cast<uint32_t>(t_begin + s * kSubD + tq * RPT + r) * D + dq * 8) * 2;
+        kd[r] = buffer_ld16(krs, off);
+        vd[r] = buffer_ld16(vrs, off);
+      }
+    };
+    auto split = [&](const float (&x)[8], u32x4& hi, u32x4& lo) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        lo[i] = pack_bf16x2(x[2 * i] - bf16lo_to_f32(hi[i]), x[2 * i + 1] - bf16hi_to_f32(hi[i]));
+      }
+    };
+    auto convert = [&](int s, const u32x4 (&kd)[RPT], const u32x4 (&vd)[RPT]) __attribute__((always_inline)) {
+      const int b = s & 1;
+      const int ts = t_begin + s * kSubD;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const int tl = tq * RPT + r;
+        const bool real = ts + tl < t_end;
+        float sk[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sk[2 * i] = elu_plus_one(bf16lo_to_f32(kd[r][i]));
+          sk[2 * i + 1] = elu_plus_one(bf16hi_to_f32(kd[r][i]));
+        }
+        // den_t = sigma(k_t) . z_{s-1} + eps; the row is spread over DQ consecutive lanes
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part += sk[i] * zp[i];
+#pragma unroll
+        for (int off = DQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        const float dsc = real ? 1.f / (part + a.eps) : 0.f;
+        float dk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dk[i] = sk[i] * dsc;
+          if (real) zacc[i] += sk[i];
+        }
+        u32x4 hi, lo, dh, dl;
+        split(sk, hi, lo);
+        split(dk, dh, dl);
+        st16(&hi_s[b][tl][dq * 8], hi);
+        st16(&lo_s[b][tl][dq * 8], lo);
+        st16(&dh_s[b][tl][dq * 8], dh);
+        st16(&dl_s[b][tl][dq * 8], dl);
+        st16(&v_s[b][tl][dq * 8], vd[r]);
+      }
+    };
+    u32x4 k0[RPT], v0[RPT], k1[RPT], v1[RPT], k2[RPT], v2[RPT], k3[RPT], v3[RPT];
+    if (ns > 0) {
+      load(0, k0, v0);
+      load(1, k1, v1);
+      load(2, k2, v2);
+      load(3, k3, v3);
+      convert(0, k0, v0);
+      load(4, k0, v0);
+    }
+    __syncthreads();   // stage 0 staged
+    for (int i = 0; i < ns; i += 4) {
+      convert(i + 1, k1, v1);
+      load(i + 5, k1, v1);
+      __syncthreads();
+      convert(i + 2, k2, v2);
+      load(i + 6, k2, v2);
+      __syncthreads();
+      convert(i + 3, k3, v3);
+      load(i + 7, k3, v3);
+      __syncthreads();
+      convert(i + 4, k0, v0);
+      load(i + 8, k0, v0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
+  } else {
+    // ---------------------------------------------------------------- consumers
+    const int cw = wave - 4;
+    const int ib0 = BB * (cw >> 1), jb0 = BB * (cw & 1);
+    f32x16 acc_u[BB][BB], acc_g[BB][BB];
+#pragma unroll
+    for (int bi = 0; bi < BB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BB; ++bj) {
+        acc_u[bi][bj] = zero16();
+        acc_g[bi][bj] = zero16();
+      }
+    __syncthreads();   // stage 0 staged
+    for (int i = 0; i < ns; ++i) {
+      const int b = i & 1;
+#pragma unroll
+      for (int ks = 0; ks < kSubD / 16; ++ks) {
+        bf16x8 av[BB], ah[BB], al[BB], bh[BB], bl[BB], eh[BB], el[BB];
+#pragma unroll
+        for (int bi = 0; bi < BB; ++bi) {
+          av[bi] = lds_operand_tr(&v_s[b][0][0], P, 16 * ks, 32 * (ib0 + bi), lane);
+          ah[bi] = lds_operand_tr(&hi_s[b][0][0], P, 16 * ks, 32 * (ib0 + bi), lane);
+          al[bi] = lds_operand_tr(&lo_s[b][0][0], P, 16 * ks, 32 * (ib0 + bi), lane);
+        }
+#pragma unroll
+        for (int bj = 0; bj < BB; ++bj) {
+          bh[bj] = lds_operand_tr(&hi_s[b][0][0], P, 16 * ks, 32 * (jb0 + bj), lane);
+          bl[bj] = lds_operand_tr(&lo_s[b][0][0], P, 16 * ks, 32 * (jb0 + bj), lane);
+          eh[bj] = lds_operand_tr(&dh_s[b][0][0], P, 16 * ks, 32 * (jb0 + bj), lane);
+          el[bj] = lds_operand_tr(&dl_s[b][0][0], P, 16 * ks, 32 * (jb0 + bj), lane);
+        }
+#pragma unroll
+        for (int bi = 0; bi < BB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < BB; ++bj) {
+            // U^T block: rows = value features, columns = key features
+            acc_u[bi][bj] = mfma32x32x16(av[bi], bh[bj], acc_u[bi][bj]);
+            acc_u[bi][bj] = mfma32x32x16(av[bi], bl[bj], acc_u[bi][bj]);
+            // G block: rows = key features (sigma(K)), columns = key features (scaled)
+            acc_g[bi][bj] = mfma32x32x16(ah[bi], eh[bj], acc_g[bi][bj]);
+            acc_g[bi][bj] = mfma32x32x16(ah[bi], el[bj], acc_g[bi][bj]);
+            acc_g[bi][bj] = mfma32x32x16(al[bi], eh[bj], acc_g[bi][bj]);
+          }
+      }
+      __syncthreads();
+    }
+    float* u_dst = a.ws.u + slot * DD;
+    float* g_dst = a.ws.g + slot * DD;
+    const int hl = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int bi = 0; bi < BB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BB; ++bj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * (ib0 + bi) + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const int col = 32 * (jb0 + bj) + l32;
+          u_dst[row * D + col] = acc_u[bi][bj][r];
+          g_dst[row * D + col] = acc_g[bi][bj][r];
+        }
+  }
+  __syncthreads();   // the producers' key-sum partials are in red
+  for (int d = tid; d < D; d += 512) {
+    float sum = 0.f;
+    for (int g = 0; g < TQ; ++g) sum += red[g][d];
+    a.ws.dz[slot * D + d] = sum;
+  }
+}
+
 // ------------------------------------------------------------------ float32 I/O path
 // One workgroup per unit (no chunking).  Thread (bi, bj) owns a TB x TB block of U (and
 // G); tokens are staged in LDS 32 at a time.
@@ -523,7 +720,7 @@ hipError_t launch_state_d(const WindowArgs& a, hipStream_t st, int mode) {
     const dim3 grid(a.units() * a.chk);
     if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_state_bf16<D, MODE_KEYSUM>), grid, dim3(kThreads), 0, st, a);
     else if (mode == MODE_LINEAR) hipLaunchKernelGGL((k_state_lin_bf16<D>), grid, dim3(kLinThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_state_bf16<D, MODE_DELTA>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_state_delta_bf16<D>), grid, dim3(512), 0, st, a);
   } else {
     const dim3 grid(a.units());
     if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_keysum_f32<D>), grid, dim3(kThreads), 0, st, a);
