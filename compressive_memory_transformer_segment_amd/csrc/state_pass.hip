@@ -64,24 +64,15 @@ __device__ void z_before(const WindowArgs& a, const UnitPos& p, float* zs) {
   }
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
+// Key sums only (the delta rule needs z_{s-1} before its state pass): one workgroup per
+// (unit, chunk), 64-token sub-tiles of K loaded one ahead of the one being summed; each
+// thread sums sigma(K) over its rows and 8 features, then the row groups are reduced in
+// group order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_keysum_bf16(const WindowArgs a) {
   constexpr int DQ = D / 8;              // threads per token row (8 features each)
   constexpr int TQ = kThreads / DQ;      // row groups
-  constexpr int RPT = kSub / TQ;         // rows per thread per sub-tile (D/32)
-  constexpr int NBLK = (D / 32) * (D / 32);
-  constexpr int NB = NBLK / 4;           // 32x32 output blocks per wave
-  constexpr int P = D + 32;              // LDS row pitch (elements): conflict-free transpose reads
-  constexpr bool kMat = MODE != MODE_KEYSUM;
-  constexpr bool kDelta = MODE == MODE_DELTA;
-
-  // Row-major [token][feature] tiles; MFMA operands are read with LDS transpose reads.
-  __shared__ __align__(16) uint16_t sk_hi[kMat ? kSub : 1][P];
-  __shared__ __align__(16) uint16_t sk_lo[kMat ? kSub : 1][P];
-  __shared__ __align__(16) uint16_t v_s[kMat ? kSub : 1][P];
-  __shared__ __align__(16) uint16_t dk_hi[kDelta ? kSub : 1][P];
-  __shared__ __align__(16) uint16_t dk_lo[kDelta ? kSub : 1][P];
-  __shared__ float zprev[kDelta ? D : 1];
+  constexpr int RPT = kSub / TQ;         // rows per thread per sub-tile
   __shared__ float red[TQ][D];
 
   const int u = blockIdx.x / a.chk;
@@ -89,165 +80,50 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
   const UnitPos p = unit_pos(a, u);
   const int tid = threadIdx.x;
   const int dq = tid % DQ, tq = tid / DQ;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int hl = lane >> 5;
-  const int l32 = lane & 31;
-
-  if constexpr (kDelta) {
-    z_before<D>(a, p, zprev);
-    __syncthreads();
-  }
-
-  // the segment's K and V rows as buffer resources: rows at or past n read as zeros
   const int64_t seg_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
-  const auto krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + seg_base, static_cast<uint32_t>(p.n) * D * 2);
-  const auto vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + seg_base, static_cast<uint32_t>(p.n) * D * 2);
+  const int t_begin = c * a.ch;
+  const int t_end = min(t_begin + a.ch, p.n);
+  // rows past the chunk end read as zeros; they are skipped below
+  const auto krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + seg_base, static_cast<uint32_t>(max(t_end, 0)) * D * 2);
 
   float zacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
-  f32x16 acc_u[kMat ? NB : 1];
-  f32x16 acc_g[kDelta ? NB : 1];
+  u32x4 kcur[RPT];
+  auto load = [&](int ts, u32x4 (&kd)[RPT]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 0; k < (kMat ? NB : 1); ++k) acc_u[k] = zero16();
-#pragma unroll
-  for (int k = 0; k < (kDelta ? NB : 1); ++k) acc_g[k] = zero16();
-
-  // sub-tile loads, one sub-tile ahead of the one being processed
-  u32x4 kcur[RPT], vcur[RPT];
-  auto load = [&](int ts, u32x4 (&kd)[RPT], u32x4 (&vd)[RPT]) {
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const uint32_t off = (static_cast<uint32_t>(ts + tq * RPT + r) * D + dq * 8) * 2;
-      kd[r] = buffer_ld16(krs, off);
-      if constexpr (kMat) vd[r] = buffer_ld16(vrs, off);
-    }
+    for (int r = 0; r < RPT; ++r)
+      kd[r] = buffer_ld16(krs, (static_cast<uint32_t>(ts + tq * RPT + r) * D + dq * 8) * 2);
   };
-  const int t_begin = c * a.ch;
-  const int t_end = min(t_begin + a.ch, p.n);
-  if (t_begin < t_end) load(t_begin, kcur, vcur);
+  if (t_begin < t_end) load(t_begin, kcur);
   for (int ts = t_begin; ts < t_end; ts += kSub) {
-    u32x4 knext[RPT], vnext[RPT];
-    if (ts + kSub < t_end) load(ts + kSub, knext, vnext);
-    // ---- sigma(K) in fp32 for this thread's RPT rows x 8 features
-    float sk[RPT][8];
+    u32x4 knext[RPT];
+    if (ts + kSub < t_end) load(ts + kSub, knext);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const int tl = tq * RPT + r;
-      const int t = ts + tl;
-      if constexpr (kMat) st16(&v_s[tl][dq * 8], vcur[r]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = bf16lo_to_f32(kcur[r][i]), x1 = bf16hi_to_f32(kcur[r][i]);
-        sk[r][2 * i] = (t < p.n) ? elu_plus_one(x0) : 0.f;
-        sk[r][2 * i + 1] = (t < p.n) ? elu_plus_one(x1) : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zacc[i] += sk[r][i];
-    }
-    if constexpr (kMat) {
-      // ---- hi/lo bf16 split of sigma(K) (and of diag(1/den) sigma(K) for the delta rule)
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const int tl = tq * RPT + r;
-        float dsc = 0.f;
-        if constexpr (kDelta) {
-          // den_t = sigma(k_t) . z_{s-1} + eps; the row is spread over DQ consecutive lanes
-          float part = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) part += sk[r][i] * zprev[dq * 8 + i];
-#pragma unroll
-          for (int off = DQ / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-          dsc = (ts + tl < p.n) ? 1.f / (part + a.eps) : 0.f;
-        }
-        u32x4 hi, lo, dh, dl;
+      if (ts + tq * RPT + r < t_end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float s0 = sk[r][2 * i], s1 = sk[r][2 * i + 1];
-          hi[i] = pack_bf16x2(s0, s1);
-          lo[i] = pack_bf16x2(s0 - bf16lo_to_f32(hi[i]), s1 - bf16hi_to_f32(hi[i]));
-          if constexpr (kDelta) {
-            const float d0 = s0 * dsc, d1 = s1 * dsc;
-            dh[i] = pack_bf16x2(d0, d1);
-            dl[i] = pack_bf16x2(d0 - bf16lo_to_f32(dh[i]), d1 - bf16hi_to_f32(dh[i]));
-          }
-        }
-        st16(&sk_hi[tl][dq * 8], hi);
-        st16(&sk_lo[tl][dq * 8], lo);
-        if constexpr (kDelta) {
-          st16(&dk_hi[tl][dq * 8], dh);
-          st16(&dk_lo[tl][dq * 8], dl);
+          zacc[2 * i] += elu_plus_one(bf16lo_to_f32(kcur[r][i]));
+          zacc[2 * i + 1] += elu_plus_one(bf16hi_to_f32(kcur[r][i]));
         }
       }
-      __syncthreads();
-
-      // ---- MFMA: each wave owns NB 32x32 blocks of the d x d outputs; operands come
-      // from the row-major tiles through transpose reads (k = token).
-#pragma unroll
-      for (int ks = 0; ks < kSub / 16; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-          const int blk = wave * NB + kb;
-          const int ib = blk / (D / 32), jb = blk % (D / 32);
-          // U^T block (rows = value features ib, columns = key features jb)
-          const bf16x8 av = lds_operand_tr(&v_s[0][0], P, 16 * ks, 32 * ib, lane);
-          const bf16x8 bkh = lds_operand_tr(&sk_hi[0][0], P, 16 * ks, 32 * jb, lane);
-          const bf16x8 bkl = lds_operand_tr(&sk_lo[0][0], P, 16 * ks, 32 * jb, lane);
-          acc_u[kb] = mfma32x32x16(av, bkh, acc_u[kb]);
-          acc_u[kb] = mfma32x32x16(av, bkl, acc_u[kb]);
-          if constexpr (kDelta) {
-            // G block (rows = key features ib, columns = key features jb)
-            const bf16x8 ah = lds_operand_tr(&sk_hi[0][0], P, 16 * ks, 32 * ib, lane);
-            const bf16x8 al = lds_operand_tr(&sk_lo[0][0], P, 16 * ks, 32 * ib, lane);
-            const bf16x8 bh = lds_operand_tr(&dk_hi[0][0], P, 16 * ks, 32 * jb, lane);
-            const bf16x8 bl = lds_operand_tr(&dk_lo[0][0], P, 16 * ks, 32 * jb, lane);
-            acc_g[kb] = mfma32x32x16(ah, bh, acc_g[kb]);
-            acc_g[kb] = mfma32x32x16(ah, bl, acc_g[kb]);
-            acc_g[kb] = mfma32x32x16(al, bh, acc_g[kb]);
-          }
-        }
-      }
-      __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      kcur[r] = knext[r];
-      if constexpr (kMat) vcur[r] = vnext[r];
-    }
+    for (int r = 0; r < RPT; ++r) kcur[r] = knext[r];
   }
-
-  // ---- key sums: reduce the per-thread partials over the row groups (in group order)
   const int64_t slot = static_cast<int64_t>(u) * a.chk + c;
-  const int64_t DD = static_cast<int64_t>(D) * D;
-  if constexpr (MODE != MODE_DELTA) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
-    __syncthreads();
-    for (int d = tid; d < D; d += kThreads) {
-      float sum = 0.f;
-      for (int g = 0; g < TQ; ++g) sum += red[g][d];
-      a.ws.dz[slot * D + d] = sum;
-    }
-  }
-  if constexpr (kMat) {
-    float* u_dst = a.ws.u + slot * DD;
-    float* g_dst = kDelta ? a.ws.g + slot * DD : nullptr;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      const int blk = wave * NB + kb;
-      const int ib = blk / (D / 32), jb = blk % (D / 32);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * ib + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int col = 32 * jb + l32;
-        u_dst[row * D + col] = acc_u[kb][r];
-        if constexpr (kDelta) g_dst[row * D + col] = acc_g[kb][r];
-      }
-    }
+  for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
+  __syncthreads();
+  for (int d = tid; d < D; d += kThreads) {
+    float sum = 0.f;
+    for (int g = 0; g < TQ; ++g) sum += red[g][d];
+    a.ws.dz[slot * D + d] = sum;
   }
 }
 
-// Linear rule, bf16 inputs: a warp-specialised version of the pass above.  Waves 0-7
+// Linear rule, bf16 inputs: a warp-specialised pass.  Waves 0-7
 // produce (two per SIMD, so that each SIMD has independent exponential chains to
 // interleave) and waves 8-11 consume.  Per 64-token stage the producers turn K into sigma(K),
 // split into bf16 hi + lo, and stage it with V in LDS, two stages deep; meanwhile the
@@ -256,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_state_bf16(const WindowArgs a) {
 // three stages ahead in four register sets; the stage count is rounded up to a multiple
 // of four (rows past the chunk end read as zeros and add nothing), so the loop body is
 // straight-line code and the compiler's load waits stay exact.  One barrier per stage.
-// The partial sums go out as in k_state_bf16: one slot per (unit, chunk), added in chunk
+// Every workgroup writes its own partial sums, one slot per (unit, chunk), added in chunk
 // order by the chain.
 constexpr int kProdWaves = 8;
 constexpr int kLinThreads = 64 * (kProdWaves + 4);
@@ -440,7 +316,9 @@ __global__ __launch_bounds__(kLinThreads, 1) void k_state_lin_bf16(const WindowA
 // and stage them with V in LDS, two stages deep (their global loads run three stages
 // ahead in registers).  Waves 4-7 consume: each owns a 2 x 2 group of 32 x 32 blocks of U^T
 // (hi and lo MFMAs) and of G (hi*hi + hi*lo + lo*hi).  One barrier per stage; the stage
-// count is rounded up to a multiple of four as in the linear kernel.
+// count is rounded up to a multiple of four as in the linear kernel.  The key sums are the
+// key-sum pass's: this kernel reads them (z_{s-1}) and must not rewrite them, since other
+// workgroups read them concurrently.
 constexpr int kSubD = 32;                 // tokens per stage
 template <int D>
 __global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a) {
@@ -456,7 +334,6 @@ __global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a)
   __shared__ __align__(16) uint16_t dl_s[2][kSubD][P];
   __shared__ __align__(16) uint16_t v_s[2][kSubD][P];
   __shared__ float zprev[D];
-  __shared__ float red[TQ][D];
 
   const int u = blockIdx.x / a.chk;
   const int c = blockIdx.x % a.chk;
@@ -482,9 +359,6 @@ __global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a)
     float zp[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) zp[i] = zprev[dq * 8 + i];
-    float zacc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
     auto load = [&](int s, u32x4 (&kd)[RPT], u32x4 (&vd)[RPT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < RPT; ++r) {
@@ -522,10 +396,7 @@ __global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a)
         const float dsc = real ? 1.f / (part + a.eps) : 0.f;
         float dk[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dk[i] = sk[i] * dsc;
-          if (real) zacc[i] += sk[i];
-        }
+        for (int i = 0; i < 8; ++i) dk[i] = sk[i] * dsc;
         u32x4 hi, lo, dh, dl;
         split(sk, hi, lo);
         split(dk, dh, dl);
@@ -560,8 +431,6 @@ __global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a)
       load(i + 8, k0, v0);
       __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[tq][dq * 8 + i] = zacc[i];
   } else {
     // ---------------------------------------------------------------- consumers
     const int cw = wave - 4;
@@ -622,12 +491,6 @@ __global__ __launch_bounds__(512, 1) void k_state_delta_bf16(const WindowArgs a)
           u_dst[row * D + col] = acc_u[bi][bj][r];
           g_dst[row * D + col] = acc_g[bi][bj][r];
         }
-  }
-  __syncthreads();   // the producers' key-sum partials are in red
-  for (int d = tid; d < D; d += 512) {
-    float sum = 0.f;
-    for (int g = 0; g < TQ; ++g) sum += red[g][d];
-    a.ws.dz[slot * D + d] = sum;
   }
 }
 
@@ -718,7 +581,7 @@ template <int D>
 hipError_t launch_state_d(const WindowArgs& a, hipStream_t st, int mode) {
   if (a.bf16) {
     const dim3 grid(a.units() * a.chk);
-    if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_state_bf16<D, MODE_KEYSUM>), grid, dim3(kThreads), 0, st, a);
+    if (mode == MODE_KEYSUM) hipLaunchKernelGGL((k_keysum_bf16<D>), grid, dim3(kThreads), 0, st, a);
     else if (mode == MODE_LINEAR) hipLaunchKernelGGL((k_state_lin_bf16<D>), grid, dim3(kLinThreads), 0, st, a);
     else hipLaunchKernelGGL((k_state_delta_bf16<D>), grid, dim3(512), 0, st, a);
   } else {
