@@ -382,7 +382,7 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   if (!(c.eps >= 0.f) || !std::isfinite(c.eps)) return INFINI_ERR_INVALID_ARG;
   if (std::isnan(c.softmax_scale) || std::isinf(c.softmax_scale)) return INFINI_ERR_INVALID_ARG;
   if (c.head_dim != 64 && c.head_dim != 128) return INFINI_ERR_UNSUPPORTED;
-  if (int64_t(c.batch) * c.heads > (int64_t(1) << 20) || c.segment_len > (1 << 24)) return INFINI_ERR_UNSUPPORTED;
+  if (int64_t(c.batch) * c.heads > (int64_t(1) << 20) || c.segment_len > (1 << 22)) return INFINI_ERR_UNSUPPORTED;
 
   infini_attn* h = new (std::nothrow) infini_attn{};
   if (!h) return INFINI_ERR_OOM;
@@ -849,6 +849,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
       rows * 4,                           // 12 per-token gate terms
       size_t(h->BH) * D * D * 4,          // 13 state copy M
       size_t(h->BH) * D * 4,              // 14 state copy z
+      h->bf16 && !h->delta ? size_t(U) * D * D * 4 : 0,   // 15 G_s packed in bf16, two orientations
   };
   constexpr int NP = sizeof(sz) / sizeof(sz[0]);
   size_t total = 0;
@@ -947,6 +948,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   bw.gm = static_cast<float*>(part[9]);
   bw.cpart = static_cast<float*>(part[10]);
   bw.gz = static_cast<float*>(part[11]);
+  bw.gpk = sz[15] ? static_cast<uint16_t*>(part[15]) : nullptr;
   bw.bq = static_cast<float*>(part[12]);
   bw.dm_final = dm_final;
   bw.dz_final = dz_final;

@@ -222,6 +222,48 @@ __global__ __launch_bounds__(kBwdThreads, 2) void k_bwd_dq_mfma(const BackwardAr
   }
 }
 
+// Element (r, c) of a [D][D] bf16 matrix in the 16-row-group layout: chunk c / 8 of row r
+// in slot (r / 16) * 16 CPR + 16 (c / 8) + r % 16 (CPR = D / 8 chunks of 8 per row), so the 32
+// rows of an MFMA A operand read 16-byte chunks at consecutive addresses.
+__device__ __forceinline__ int rg_index(int r, int c, int cpr) {
+  return ((r >> 4) * 16 * cpr + 16 * (c >> 3) + (r & 15)) * 8 + (c & 7);
+}
+
+// G_s (fp32, row-major [i][j]) -> bf16 in the 16-row-group layout in both orientations:
+// gr holds rows i (G_s), gt rows j (G_s^T).  gr / gt may be LDS or global memory; the
+// `threads` threads of the caller split the D * D / 8 chunks.
+template <int D>
+__device__ __forceinline__ void pack_g(const float* gm, uint16_t* gr, uint16_t* gt, int tid, int threads) {
+  constexpr int CPR = D / 8;
+#pragma unroll 4
+  for (int e = tid; e < D * CPR; e += threads) {
+    {  // G rows: chunk (i, cj)
+      const int i = e / CPR, cj = e % CPR;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(gm + i * D + 8 * cj);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(gm + i * D + 8 * cj + 4);
+      st16(gr + rg_index(i, 8 * cj, CPR), u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
+                                               pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])});
+    }
+    {  // G^T rows: chunk (j, ci) = G[8 ci .. + 7][j]
+      const int j = e % D, ci = e / D;
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = gm[(8 * ci + k) * D + j];
+      st16(gt + rg_index(j, 8 * ci, CPR), u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                               pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
+    }
+  }
+}
+
+// Packed G_s of every segment for the linear rule's fused dK, dV epilogue (one workgroup per
+// segment and head).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_gpack(const BackwardArgs b) {
+  const int64_t u = blockIdx.x;
+  uint16_t* dst = b.gpk + u * 2 * D * D;
+  pack_g<D>(b.gm + u * D * D, dst, dst + D * D, static_cast<int>(threadIdx.x), kBwdThreads);
+}
+
 // dK, dV (k_bwd_dkv_mfma): one workgroup = 4 waves = 128 keys; every wave owns 32 keys and
 // works in the mirror frame, keys on lanes: S = Q K^T and dP = dO V^T (this wave's K and V
 // rows are the B operands, held in registers), P and dS = P o (dP - D) per query row, then
@@ -230,16 +272,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void k_bwd_dq_mfma(const BackwardAr
 // 64 (Q, dO, lse, D) go HBM -> LDS by buffer -> LDS copies, double buffered.
 // (d = 128: the K, V operands and the dK, dV accumulators need more than 256 registers, so
 // one workgroup per CU with the accumulators in AGPRs.)
-template <int D>
+// FUSE (linear rule): the memory-update part of dK, dV is added in the epilogue, in the
+// accumulators' frame, before the one store: dV += sigma(K) G_s and
+// dK += (V G_s^T + g_s) o sigma'(K) (Eq. 8 differentiated; G_s = dL/dM_s, g_s = dL/dz_s,
+// both known: the reverse chains run before this kernel).  G_s arrives packed in bf16
+// (k_bwd_gpack) and is copied to LDS while the query tiles stream.  Requires k_loc == k.
+template <int D, bool FUSE>
 __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(const BackwardArgs b) {
-  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, DD = D * D;
   constexpr int TILE = kBwdK * D;            // elements of a Q (or dO) tile
   constexpr int CPT = kBwdK * D * 2 / 1024;  // 1 KB copies per tensor tile
   constexpr int CPW = CPT / 4;
+  constexpr int GCW = FUSE ? 2 * DD * 2 / 1024 / 4 : 0;   // 1 KB copies of packed G_s per wave
   __shared__ __align__(16) uint16_t buf0[2 * TILE];
   __shared__ __align__(16) uint16_t buf1[2 * TILE];
   __shared__ __align__(16) float st0[2][256];   // lse, D of the tile in buffer 0 (first 64 used)
   __shared__ __align__(16) float st1[2][256];
+  __shared__ __align__(16) uint16_t gl[FUSE ? 2 * DD : 8];   // G_s rows i, then rows j
 
   const WindowArgs& w = b.w;
   const int units = w.units();
@@ -292,7 +341,6 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
       copy_to_lds(src, bytes, reinterpret_cast<const uint16_t*>(stats[wave]), static_cast<uint32_t>(lane) * 16);
     }
   };
-  const int cnt = 2 * CPW + (wave < 2 ? 1 : 0);   // copies per tile issued by this wave
 
   const int g_rd = ((l32 >> 4) * 16 * CPR + 16 * hl + (l32 & 15)) * 8;
   const int G = lane >> 4, jl = lane & 15;
@@ -372,25 +420,121 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
 
   issue(0, buf0, st0);
   issue(1, buf1, st1);
+  if constexpr (FUSE) {   // after tiles 0 and 1: the first pass of the loop lets these be in flight
+    const uint16_t* gsrc = b.gpk + static_cast<int64_t>(u) * 2 * DD;
+#pragma unroll
+    for (int c = 0; c < GCW; ++c) {
+      const int idx = wave * GCW + c;
+      copy_to_lds(gsrc + 512 * idx, 1024u, gl + 512 * idx, static_cast<uint32_t>(lane) * 16);
+    }
+  }
+  // vmcnt of the tile waits, as immediates: the copies younger than the tile waited for are
+  // this wave's copies of one tile, plus those of G_s during the first pair of tiles
+  auto wait_tiles = [&](bool first) __attribute__((always_inline)) {
+    constexpr int C = 2 * CPW;
+    if (wave < 2) {
+      if (first) wait_vm_lgkm0<C + 1 + GCW>();
+      else wait_vm_lgkm0<C + 1>();
+    } else {
+      if (first) wait_vm_lgkm0<C + GCW>();
+      else wait_vm_lgkm0<C>();
+    }
+  };
   for (int i = 0; i < nqt; i += 2) {
-    wait_vm_le(cnt);   // tile i (tile i + 1 may still be in flight)
+    const bool first = i == 0;
+    wait_tiles(first);   // tile i (tile i + 1 may still be in flight)
     __builtin_amdgcn_s_barrier();
     compute(buf0, st0, i);
-    wait_vm_le(cnt);   // this wave's LDS reads of buffer 0 are done
+    wait_tiles(first);   // this wave's LDS reads of buffer 0 are done
     __builtin_amdgcn_s_barrier();
     issue(i + 2, buf0, st0);
     if (i + 1 < nqt) {
-      wait_vm_le(cnt);
+      wait_tiles(first);
       __builtin_amdgcn_s_barrier();
       compute(buf1, st1, i + 1);
-      wait_vm_le(cnt);
+      wait_tiles(first);
       __builtin_amdgcn_s_barrier();
       issue(i + 3, buf1, st1);
     }
   }
   wait_vm_le(0);   // no copy may land in LDS after the workgroup ends
-  if (!live) return;
   const float omg = w.gate_omg[h], sc = w.scale * omg;
+  if constexpr (FUSE) {
+    __syncthreads();   // every wave's copies of G_s have landed
+    const uint16_t* gr_l = gl;        // G_s, rows i
+    const uint16_t* gt_l = gl + DD;   // G_s^T, rows j
+    // sigma(k) of this lane's key as the B operand (zero past the segment's end)
+    bf16x8 wreg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float wf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = elu_plus_one(bf16lo_to_f32(kreg[ks][e])), hi = elu_plus_one(bf16hi_to_f32(kreg[ks][e]));
+        wf[2 * e] = live ? lo : 0.f;
+        wf[2 * e + 1] = live ? hi : 0.f;
+      }
+      wreg[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(wf[0], wf[1]), pack_bf16x2(wf[2], wf[3]),
+                                                 pack_bf16x2(wf[4], wf[5]), pack_bf16x2(wf[6], wf[7])});
+    }
+    // rows of dK, dV end at the segment's last key: stores of lanes past it are dropped
+    const uint32_t nb = static_cast<uint32_t>(n) * D;
+    const auto dvrs = buffer_rsrc(b.dv + row0 * D, nb * 4);
+    const auto dkrs = buffer_rsrc(b.dk + row0 * D, nb * 4);
+    const uint32_t e0 = static_cast<uint32_t>(key) * D;
+    // dV^T = (1 - g) (local) + G_s^T sigma(K)^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) adv[db][r] *= omg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        adv[db] = mfma32x32x16(as_bf16x8(ld16(gt_l + g_rd + db * 256 * CPR + 256 * ks)), wreg[ks], adv[db]);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        buffer_st16(dvrs, 4 * (e0 + 32 * db + 8 * r4 + 4 * hl),
+                    u32x4{__float_as_uint(adv[db][4 * r4]), __float_as_uint(adv[db][4 * r4 + 1]),
+                          __float_as_uint(adv[db][4 * r4 + 2]), __float_as_uint(adv[db][4 * r4 + 3])});
+    }
+    // dK^T = (1 - g) scale (local) + (G_s V^T + g_s) o sigma'(K)^T.  Register 4 q + e of block
+    // ib is feature 32 ib + 8 q + 4 hl + e; kreg[ks] holds features 16 ks + 8 hl .. + 7, so
+    // the key values of a block come from this lane and its partner lane ^ 32.
+    const float* gzb = b.gz + static_cast<int64_t>(u) * D;
+#pragma unroll
+    for (int ib = 0; ib < DB; ++ib) {
+      f32x16 sg = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sg = mfma32x32x16(as_bf16x8(ld16(gr_l + g_rd + ib * 256 * CPR + 256 * ks)), as_bf16x8(vreg[ks]), sg);
+      u32x4 kh[2][2];   // [x][half]: kreg[2 ib + x] as held by the lane with hl = half
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t own = kreg[2 * ib + x][d];
+          const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(own), 32));
+          kh[x][0][d] = hl ? other : own;
+          kh[x][1][d] = hl ? own : other;
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i0 = 32 * ib + 8 * q + 4 * hl;
+        const f32x4 gz4 = *reinterpret_cast<const f32x4*>(gzb + i0);
+        const u32x4 src = kh[q >> 1][q & 1];   // features 32 ib + 16 (q >> 1) + 8 (q & 1) .. + 7
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t dw = hl ? src[2 + (e >> 1)] : src[e >> 1];
+          const float kf = (e & 1) ? bf16hi_to_f32(dw) : bf16lo_to_f32(dw);
+          const float dsig = kf > 0.f ? 1.f : __builtin_amdgcn_exp2f(kf * kLog2e);
+          o[e] = __float_as_uint(fmaf(adk[ib][4 * q + e], sc, (sg[4 * q + e] + gz4[e]) * dsig));
+        }
+        buffer_st16(dkrs, 4 * (e0 + i0), o);
+      }
+    }
+    return;
+  }
+  if (!live) return;
   const int64_t krow = row0 + key;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -421,10 +565,6 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
 // registers hold.  dV, dK are updated in place (fp32); for the linear rule dK also receives
 // dL/dz_s sigma'(K) here (the z chain has run); for the delta rule the tile's
 // sigma(K)^T ddenk partial goes to cpart and the z term is added by a later pass.
-__device__ __forceinline__ int rg_index(int r, int c, int cpr) {
-  return ((r >> 4) * 16 * cpr + 16 * (c >> 3) + (r & 15)) * 8 + (c & 7);
-}
-
 template <int D, bool DELTA>
 __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(const BackwardArgs b) {
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, DD = D * D;
@@ -447,24 +587,9 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
   const int l32 = lane & 31, hl = lane >> 5;
 
   // ---- stage G_s (and M_{s-1}) as bf16 in both orientations
-  const float* gm = b.gm + static_cast<int64_t>(u) * DD;
-  for (int e = tid; e < D * CPR; e += kBwdThreads) {
-    {  // G rows: chunk (i, cj)
-      const int i = e / CPR, cj = e % CPR;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(gm + i * D + 8 * cj);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(gm + i * D + 8 * cj + 4);
-      st16(gr_l + rg_index(i, 8 * cj, CPR), u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
-                                                 pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])});
-    }
-    {  // G^T rows: chunk (j, ci) = G[8 ci .. + 7][j]
-      const int j = e % D, ci = e / D;
-      float x[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = gm[(8 * ci + k) * D + j];
-      st16(gt_l + rg_index(j, 8 * ci, CPR), u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                                 pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
-    }
-    if constexpr (DELTA) {
+  pack_g<D>(b.gm + static_cast<int64_t>(u) * DD, gr_l, gt_l, tid, kBwdThreads);
+  if constexpr (DELTA) {
+    for (int e = tid; e < D * CPR; e += kBwdThreads) {
       const uint16_t* mt = static_cast<const uint16_t*>(w.ws.mt) + static_cast<int64_t>(u) * DD;
       {  // M^T rows (as recorded): chunk (j, ci)
         const int j = e / CPR, ci = e % CPR;
@@ -484,25 +609,34 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
   if (tid < D) cacc[tid] = 0.f;
   __syncthreads();
 
+  // Token rows are read and written through buffer resources that end at the segment's
+  // last token: lanes past it load zeros and their stores are dropped, so no load sits
+  // behind a per-lane branch (which would serialise them).
   const int t = t0 + 32 * wave + l32;
   const bool live = t < n;
-  const int64_t row = row0 + t;
-  const uint16_t* kr = static_cast<const uint16_t*>(w.k) + row * D;
-  const uint16_t* vr = static_cast<const uint16_t*>(w.v) + row * D;
+  const uint32_t nb = static_cast<uint32_t>(n) * D;   // elements of the segment
+  const auto krs = buffer_rsrc(static_cast<const uint16_t*>(w.k) + row0 * D, nb * 2);
+  const auto vrs = buffer_rsrc(static_cast<const uint16_t*>(w.v) + row0 * D, nb * 2);
+  const auto dvrs = buffer_rsrc(b.dv + row0 * D, nb * 4);
+  const auto dkrs = buffer_rsrc(b.dk + row0 * D, nb * 4);
+  const uint32_t e0 = static_cast<uint32_t>(t) * D;   // this lane's first element
   const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
   const float* gzb = b.gz + static_cast<int64_t>(u) * D;   // linear: computed before this kernel
 
   // sigma(k) of this lane's token as the B operand (k = i natural), and sigma(k) . z
+  u32x4 kraw[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kraw[ks] = buffer_ld16(krs, 2 * (e0 + 16 * ks + 8 * hl));
   bf16x8 wreg[KS];
   float wf[KS][8];
   float zs = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const u32x4 kv = live ? ld16(kr + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      wf[ks][2 * e] = live ? elu_plus_one(bf16lo_to_f32(kv[e])) : 0.f;
-      wf[ks][2 * e + 1] = live ? elu_plus_one(bf16hi_to_f32(kv[e])) : 0.f;
+      const float lo = elu_plus_one(bf16lo_to_f32(kraw[ks][e])), hi = elu_plus_one(bf16hi_to_f32(kraw[ks][e]));
+      wf[ks][2 * e] = live ? lo : 0.f;
+      wf[ks][2 * e + 1] = live ? hi : 0.f;
     }
     wreg[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(wf[ks][0], wf[ks][1]), pack_bf16x2(wf[ks][2], wf[ks][3]),
                                                pack_bf16x2(wf[ks][4], wf[ks][5]), pack_bf16x2(wf[ks][6], wf[ks][7])});
@@ -526,7 +660,7 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
   if constexpr (!DELTA) {
     u32x4 vreg[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) vreg[ks] = live ? ld16(vr + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks) vreg[ks] = buffer_ld16(vrs, 2 * (e0 + 16 * ks + 8 * hl));
 #pragma unroll
     for (int ib = 0; ib < DB; ++ib) {
       S[ib] = zero16();
@@ -546,6 +680,11 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
         R[jb] = mfma32x32x16(as_bf16x8(ld16(mt_l + g_rd + jb * 256 * CPR + 256 * ks)), wreg[ks], R[jb]);
     }
     // register r of block jb holds feature j = 32 jb + 8 (r / 4) + 4 hl + r % 4 of this token
+    u32x2 vraw[DB][4];
+#pragma unroll
+    for (int jb = 0; jb < DB; ++jb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) vraw[jb][r4] = buffer_ld8(vrs, 2 * (e0 + 32 * jb + 8 * r4 + 4 * hl));
     float yr = 0.f;
     bf16x8 vrb[KS], dwb[KS];
 #pragma unroll
@@ -553,7 +692,7 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
       float vmr[16], dw[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const u32x2 vv = live ? ld8(vr + 32 * jb + 8 * r4 + 4 * hl) : u32x2{0, 0};
+        const u32x2 vv = vraw[jb][r4];
         const float vf[4] = {bf16lo_to_f32(vv[0]), bf16hi_to_f32(vv[0]), bf16lo_to_f32(vv[1]), bf16hi_to_f32(vv[1])};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -589,44 +728,52 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
         S[ib] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), dwb[j4], S[ib]);
       }
     }
-    // this tile's share of sigma(K)^T ddenk
-    if (live) {
+    // this tile's share of sigma(K)^T ddenk (wf and ddk are zero past the segment's end)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) atomicAdd(&cacc[16 * ks + 8 * hl + e], wf[ks][e] * ddk);
+      for (int e = 0; e < 8; ++e) atomicAdd(&cacc[16 * ks + 8 * hl + e], wf[ks][e] * ddk);
+  }
+  // dV += Y (all loads of a block first, then the stores)
+#pragma unroll
+  for (int jb = 0; jb < DB; ++jb) {
+    u32x4 old[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) old[r4] = buffer_ld16(dvrs, 4 * (e0 + 32 * jb + 8 * r4 + 4 * hl));
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(__uint_as_float(old[r4][e]) + Y[jb][4 * r4 + e]);
+      buffer_st16(dvrs, 4 * (e0 + 32 * jb + 8 * r4 + 4 * hl), o);
     }
   }
-  if (live) {
+  // dK += dsigma(K) o sigma'(K)
 #pragma unroll
-    for (int jb = 0; jb < DB; ++jb)
+  for (int ib = 0; ib < DB; ++ib) {
+    u32x4 old[4];
+    u32x2 kv[4];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int j0 = 32 * jb + 8 * r4 + 4 * hl;
-        f32x4* pv = reinterpret_cast<f32x4*>(b.dv + row * D + j0);
-        f32x4 o = *pv;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      old[r4] = buffer_ld16(dkrs, 4 * (e0 + 32 * ib + 8 * r4 + 4 * hl));
+      kv[r4] = buffer_ld8(krs, 2 * (e0 + 32 * ib + 8 * r4 + 4 * hl));
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] += Y[jb][4 * r4 + e];
-        *pv = o;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int i0 = 32 * ib + 8 * r4 + 4 * hl;
+      const float kf[4] = {bf16lo_to_f32(kv[r4][0]), bf16hi_to_f32(kv[r4][0]), bf16lo_to_f32(kv[r4][1]),
+                           bf16hi_to_f32(kv[r4][1])};
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float a = S[ib][4 * r4 + e];
+        if constexpr (DELTA) a = fmaf(ddk, zb[i0 + e], a);
+        else a += gzb[i0 + e];   // linear: dL/dz_s reaches every token of the segment
+        o[e] = __float_as_uint(__uint_as_float(old[r4][e]) +
+                               a * (kf[e] > 0.f ? 1.f : __builtin_amdgcn_exp2f(kf[e] * kLog2e)));
       }
-#pragma unroll
-    for (int ib = 0; ib < DB; ++ib)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int i0 = 32 * ib + 8 * r4 + 4 * hl;
-        const u32x2 kv = ld8(kr + i0);
-        const float kf[4] = {bf16lo_to_f32(kv[0]), bf16hi_to_f32(kv[0]), bf16lo_to_f32(kv[1]), bf16hi_to_f32(kv[1])};
-        f32x4* pk = reinterpret_cast<f32x4*>(b.dk + row * D + i0);
-        f32x4 o = *pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float a = S[ib][4 * r4 + e];
-          if constexpr (DELTA) a = fmaf(ddk, zb[i0 + e], a);
-          else a += gzb[i0 + e];   // linear: dL/dz_s reaches every token of the segment
-          o[e] += a * (kf[e] > 0.f ? 1.f : __builtin_amdgcn_exp2f(kf[e] * kLog2e));
-        }
-        *pk = o;
-      }
+      buffer_st16(dkrs, 4 * (e0 + i0), o);
+    }
   }
   if constexpr (DELTA) {
     __syncthreads();
@@ -762,12 +909,30 @@ hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, hipStream_t st) {
+hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, bool fuse_update, hipStream_t st) {
   const WindowArgs& w = b.w;
+  // the fused epilogue takes sigma(K) from the local arm's keys and G_s from gpk
+  if (fuse_update && (w.delta || w.k_loc != w.k || !b.gpk)) return hipErrorInvalidValue;
   const int nk = (w.N + kBwdQ - 1) / kBwdQ;
   const dim3 grid(static_cast<unsigned>(w.units() * nk)), block(kBwdThreads);
-  if (w.D == 128) hipLaunchKernelGGL((k_bwd_dkv_mfma<128>), grid, block, 0, st, b);
-  else if (w.D == 64) hipLaunchKernelGGL((k_bwd_dkv_mfma<64>), grid, block, 0, st, b);
+  if (w.D == 128) {
+    if (fuse_update) hipLaunchKernelGGL((k_bwd_dkv_mfma<128, true>), grid, block, 0, st, b);
+    else hipLaunchKernelGGL((k_bwd_dkv_mfma<128, false>), grid, block, 0, st, b);
+  } else if (w.D == 64) {
+    if (fuse_update) hipLaunchKernelGGL((k_bwd_dkv_mfma<64, true>), grid, block, 0, st, b);
+    else hipLaunchKernelGGL((k_bwd_dkv_mfma<64, false>), grid, block, 0, st, b);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gpack(const BackwardArgs& b, hipStream_t st) {
+  const WindowArgs& w = b.w;
+  if (!b.gpk) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(w.units())), block(kBwdThreads);
+  if (w.D == 128) hipLaunchKernelGGL((k_bwd_gpack<128>), grid, block, 0, st, b);
+  else if (w.D == 64) hipLaunchKernelGGL((k_bwd_gpack<64>), grid, block, 0, st, b);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

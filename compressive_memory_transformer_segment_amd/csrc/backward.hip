@@ -543,26 +543,30 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((k_bwd_dq<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
   }
-  if constexpr (BF16) {
-    const hipError_t e = launch_bwd_dkv_mfma(b, st);
-    if (e != hipSuccess) return e;
-  } else {
-    hipLaunchKernelGGL((k_bwd_dkv<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
-  }
-  if constexpr (BF16) {
-    const hipError_t e = launch_bwd_r_mfma(b, st);
-    if (e != hipSuccess) return e;
-  } else {
-    hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
-  }
-  hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
   if (BF16 && !w.delta) {
-    // linear: g_s needs only the R pass, so the z chain runs first and the update kernel
-    // adds g_s sigma'(K) to dK itself
+    // linear: the reverse chains need only the R pass, so they run first and the dK, dV
+    // kernel adds the memory-update part (sigma(K) G_s, (V G_s^T + g_s) o sigma'(K)) itself
+    hipError_t e = launch_bwd_r_mfma(b, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
     hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
-    const hipError_t e = launch_bwd_update_mfma(b, st);
+    e = launch_bwd_gpack(b, st);
+    if (e == hipSuccess) e = launch_bwd_dkv_mfma(b, true, st);
     if (e != hipSuccess) return e;
   } else {
+    if constexpr (BF16) {
+      const hipError_t e = launch_bwd_dkv_mfma(b, false, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL((k_bwd_dkv<D, BF16>), dim3(tiles), dim3(64 * (D / 32)), 0, st, b);
+    }
+    if constexpr (BF16) {
+      const hipError_t e = launch_bwd_r_mfma(b, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
+    }
+    hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
     if constexpr (BF16) {
       const hipError_t e = launch_bwd_update_mfma(b, st);
       if (e != hipSuccess) return e;

@@ -121,6 +121,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voffset), 0, 0));
 }
+__device__ __forceinline__ u32x2 buffer_ld8(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voffset), 0, 0));
+}
+// Stores at byte offsets at or beyond the resource's `bytes` are dropped.
+__device__ __forceinline__ void buffer_st16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voffset), 0, 0);
+}
 
 // Buffer -> LDS copy of 16 bytes per lane (gfx950): lane i's bytes land at lds_base + 16 i
 // (lds_base wave-uniform); offsets past the resource end write zeros.

@@ -120,6 +120,8 @@ struct BackwardArgs {
   float* gm;             // [U][D][D]      dL/dM_s (the state after segment s)
   float* cpart;          // [U][ct][D]     delta: sigma(K)^T ddenk per token tile
   float* gz;             // [U][D]         dL/dz_s
+  uint16_t* gpk;         // [U][2][D*D]    bf16 linear: G_s packed for the fused dK, dV epilogue
+                         //                (16-row groups; rows i, then rows j)
   float* bq;             // [B,H,T]        per-token gate terms g (1 - g) dO . (A_mem - A_dot)
   const float* dm_final; // optional [B,H,D,D] gradient of the final M
   const float* dz_final; // optional [B,H,D]
@@ -133,7 +135,9 @@ struct BackwardArgs {
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const BackwardArgs& b, hipStream_t st);    // bf16: dQ (local + retrieval)
-hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, hipStream_t st);   // bf16: dK, dV (local)
+hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, bool fuse_update, hipStream_t st);   // bf16: dK, dV
+                                           // (local; + the linear memory-update part if fuse_update)
+hipError_t launch_bwd_gpack(const BackwardArgs& b, hipStream_t st);         // bf16 linear: gm -> gpk
 hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st);   // bf16: memory-update part of dK, dV
 hipError_t launch_bwd_r_mfma(const BackwardArgs& b, hipStream_t st);        // bf16: sigma(Q)^T dnum, sigma(Q)^T dden
 

@@ -68,7 +68,8 @@ typedef struct {
   int32_t batch;          /* B >= 1 */
   int32_t heads;          /* H >= 1; each head has its own M, z and beta ("Multi-Head Infini-Attention") */
   int32_t head_dim;       /* d = d_key = d_value; 64 or 128 */
-  int32_t segment_len;    /* N >= 1 */
+  int32_t segment_len;    /* 1 <= N <= 2^22 (one segment's d-wide rows stay within a 32-bit
+                             byte range); larger: INFINI_ERR_UNSUPPORTED */
   int32_t update;         /* infini_update_t */
   int32_t io_dtype;       /* infini_dtype_t */
   float eps;              /* >= 0; added to the retrieval denominator in Eq. 7 and Eq. 9.  With
