@@ -552,26 +552,25 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
     }
 }
 
-// Memory-update part of dK, dV (k_bwd_update_mfma, Eq. 8 / 9 differentiated; formulas in
-// backward.hip): one workgroup = 4 waves = 128 tokens of one segment; every wave owns 32
-// tokens on lanes, with the feature dimension in the result registers:
+// Memory-update part of dK, dV for the delta rule (k_bwd_update_mfma, Eq. 9 differentiated;
+// formulas in backward.hip; the linear rule's part runs in k_bwd_dkv_mfma's epilogue): one
+// workgroup = 4 waves = 128 tokens of one segment; every wave owns 32 tokens on lanes, with
+// the feature dimension in the result registers:
 //   Y^T = G_s^T sigma(K)^T                      (-> dV)
-//   linear: dsigma(K)^T = G_s V^T
-//   delta:  R^T = M_{s-1}^T sigma(K)^T / denk,  dsigma(K)^T = G_s (V - R)^T + M_{s-1} dW^T
-//           + z ddenk with dW = -Y / denk, ddenk = Y . R / denk (per token)
-// G_s (fp32) and, for the delta rule, M_{s-1} are staged in LDS as bf16 in both orientations
-// (16-row-group layout); sigma(K) and V come from registers; the (V - R) and dW results are
-// the B operands of the last products, with G_s and M_{s-1} read in the order their
-// registers hold.  dV, dK are updated in place (fp32); for the linear rule dK also receives
-// dL/dz_s sigma'(K) here (the z chain has run); for the delta rule the tile's
-// sigma(K)^T ddenk partial goes to cpart and the z term is added by a later pass.
-template <int D, bool DELTA>
-__global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(const BackwardArgs b) {
+//   R^T = M_{s-1}^T sigma(K)^T / denk,  dsigma(K)^T = G_s (V - R)^T + M_{s-1} dW^T + z ddenk
+//   with dW = -Y / denk, ddenk = Y . R / denk (per token)
+// G_s (fp32) and M_{s-1} are staged in LDS as bf16 in both orientations (16-row-group
+// layout); sigma(K) and V come from registers; the (V - R) and dW results are the B operands
+// of the last products, with G_s and M_{s-1} read in the order their registers hold.  dV, dK
+// are updated in place (fp32); the tile's sigma(K)^T ddenk partial goes to cpart and the z
+// term is added by a later pass.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void k_bwd_update_mfma(const BackwardArgs b) {
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, DD = D * D;
   __shared__ __align__(16) uint16_t gt_l[DD];               // G_s^T (rows j)
   __shared__ __align__(16) uint16_t gr_l[DD];               // G_s (rows i)
-  __shared__ __align__(16) uint16_t mt_l[DELTA ? DD : 8];   // M_{s-1}^T (rows j)
-  __shared__ __align__(16) uint16_t mr_l[DELTA ? DD : 8];   // M_{s-1} (rows i)
+  __shared__ __align__(16) uint16_t mt_l[DD];   // M_{s-1}^T (rows j)
+  __shared__ __align__(16) uint16_t mr_l[DD];   // M_{s-1} (rows i)
   __shared__ float cacc[D];
 
   const WindowArgs& w = b.w;
@@ -588,22 +587,20 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
 
   // ---- stage G_s (and M_{s-1}) as bf16 in both orientations
   pack_g<D>(b.gm + static_cast<int64_t>(u) * DD, gr_l, gt_l, tid, kBwdThreads);
-  if constexpr (DELTA) {
-    for (int e = tid; e < D * CPR; e += kBwdThreads) {
-      const uint16_t* mt = static_cast<const uint16_t*>(w.ws.mt) + static_cast<int64_t>(u) * DD;
-      {  // M^T rows (as recorded): chunk (j, ci)
-        const int j = e / CPR, ci = e % CPR;
-        st16(mt_l + rg_index(j, 8 * ci, CPR), ld16(mt + j * D + 8 * ci));
-      }
-      {  // M rows: chunk (i, cj) = M^T[8 cj .. + 7][i]
-        const int i = e % D, cj = e / D;
-        uint16_t x[8];
+  const uint16_t* mt = static_cast<const uint16_t*>(w.ws.mt) + static_cast<int64_t>(u) * DD;
+  for (int e = tid; e < D * CPR; e += kBwdThreads) {
+    {  // M^T rows (as recorded): chunk (j, ci)
+      const int j = e / CPR, ci = e % CPR;
+      st16(mt_l + rg_index(j, 8 * ci, CPR), ld16(mt + j * D + 8 * ci));
+    }
+    {  // M rows: chunk (i, cj) = M^T[8 cj .. + 7][i]
+      const int i = e % D, cj = e / D;
+      uint16_t x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = mt[(8 * cj + k) * D + i];
-        st16(mr_l + rg_index(i, 8 * cj, CPR),
-             u32x4{x[0] | (uint32_t(x[1]) << 16), x[2] | (uint32_t(x[3]) << 16), x[4] | (uint32_t(x[5]) << 16),
-                   x[6] | (uint32_t(x[7]) << 16)});
-      }
+      for (int k = 0; k < 8; ++k) x[k] = mt[(8 * cj + k) * D + i];
+      st16(mr_l + rg_index(i, 8 * cj, CPR),
+           u32x4{x[0] | (uint32_t(x[1]) << 16), x[2] | (uint32_t(x[3]) << 16), x[4] | (uint32_t(x[5]) << 16),
+                 x[6] | (uint32_t(x[7]) << 16)});
     }
   }
   if (tid < D) cacc[tid] = 0.f;
@@ -621,7 +618,6 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
   const auto dkrs = buffer_rsrc(b.dk + row0 * D, nb * 4);
   const uint32_t e0 = static_cast<uint32_t>(t) * D;   // this lane's first element
   const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
-  const float* gzb = b.gz + static_cast<int64_t>(u) * D;   // linear: computed before this kernel
 
   // sigma(k) of this lane's token as the B operand (k = i natural), and sigma(k) . z
   u32x4 kraw[KS];
@@ -640,10 +636,8 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
     }
     wreg[ks] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(wf[ks][0], wf[ks][1]), pack_bf16x2(wf[ks][2], wf[ks][3]),
                                                pack_bf16x2(wf[ks][4], wf[ks][5]), pack_bf16x2(wf[ks][6], wf[ks][7])});
-    if constexpr (DELTA) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) zs = fmaf(wf[ks][e], zb[16 * ks + 8 * hl + e], zs);
-    }
+    for (int e = 0; e < 8; ++e) zs = fmaf(wf[ks][e], zb[16 * ks + 8 * hl + e], zs);
   }
   const int g_rd = ((l32 >> 4) * 16 * CPR + 16 * hl + (l32 & 15)) * 8;
   const int p_rd = ((l32 >> 4) * 16 * CPR + (l32 & 15)) * 8 + 4 * hl;
@@ -656,19 +650,8 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
     for (int ks = 0; ks < KS; ++ks)
       Y[jb] = mfma32x32x16(as_bf16x8(ld16(gt_l + g_rd + jb * 256 * CPR + 256 * ks)), wreg[ks], Y[jb]);
   }
-  float ddk = 0.f;
-  if constexpr (!DELTA) {
-    u32x4 vreg[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) vreg[ks] = buffer_ld16(vrs, 2 * (e0 + 16 * ks + 8 * hl));
-#pragma unroll
-    for (int ib = 0; ib < DB; ++ib) {
-      S[ib] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        S[ib] = mfma32x32x16(as_bf16x8(ld16(gr_l + g_rd + ib * 256 * CPR + 256 * ks)), as_bf16x8(vreg[ks]), S[ib]);
-    }
-  } else {
+  float ddk;   // ddenk of this lane's token
+  {
     const float denk = sum_across_halves(zs) + w.eps;
     const float inv = 1.f / denk;
     f32x16 R[DB];
@@ -767,18 +750,15 @@ __global__ __launch_bounds__(kBwdThreads, DELTA ? 1 : 2) void k_bwd_update_mfma(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float a = S[ib][4 * r4 + e];
-        if constexpr (DELTA) a = fmaf(ddk, zb[i0 + e], a);
-        else a += gzb[i0 + e];   // linear: dL/dz_s reaches every token of the segment
+        a = fmaf(ddk, zb[i0 + e], a);
         o[e] = __float_as_uint(__uint_as_float(old[r4][e]) +
                                a * (kf[e] > 0.f ? 1.f : __builtin_amdgcn_exp2f(kf[e] * kLog2e)));
       }
       buffer_st16(dkrs, 4 * (e0 + i0), o);
     }
   }
-  if constexpr (DELTA) {
-    __syncthreads();
-    if (tid < D) b.cpart[(static_cast<int64_t>(u) * b.ct + tile) * D + tid] = cacc[tid];
-  }
+  __syncthreads();
+  if (tid < D) b.cpart[(static_cast<int64_t>(u) * b.ct + tile) * D + tid] = cacc[tid];
 }
 
 // R_s = sigma(Q)^T dnum and r_s = sigma(Q)^T dden over one chunk of a segment (dnum = g dO /
@@ -897,15 +877,10 @@ hipError_t launch_bwd_r_mfma(const BackwardArgs& b, hipStream_t st) {
 hipError_t launch_bwd_update_mfma(const BackwardArgs& b, hipStream_t st) {
   const WindowArgs& w = b.w;
   const dim3 grid(static_cast<unsigned>(w.units() * b.ct)), block(kBwdThreads);
-  if (w.D == 128) {
-    if (w.delta) hipLaunchKernelGGL((k_bwd_update_mfma<128, true>), grid, block, 0, st, b);
-    else hipLaunchKernelGGL((k_bwd_update_mfma<128, false>), grid, block, 0, st, b);
-  } else if (w.D == 64) {
-    if (w.delta) hipLaunchKernelGGL((k_bwd_update_mfma<64, true>), grid, block, 0, st, b);
-    else hipLaunchKernelGGL((k_bwd_update_mfma<64, false>), grid, block, 0, st, b);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (!w.delta) return hipErrorInvalidValue;   // (linear: fused into the dK, dV kernel)
+  if (w.D == 128) hipLaunchKernelGGL((k_bwd_update_mfma<128>), grid, block, 0, st, b);
+  else if (w.D == 64) hipLaunchKernelGGL((k_bwd_update_mfma<64>), grid, block, 0, st, b);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

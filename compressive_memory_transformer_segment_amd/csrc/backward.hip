@@ -22,8 +22,10 @@
 //               dL/dz_{s-1} += g_s + w^T ddenk
 //   dK += dw o sigma'(K).
 // The sequential parts are two reverse chains per (batch, head): G over d x d matrices and
-// g over d-vectors; everything else runs for all segments at once.  These kernels are the
-// plain fp32 SIMT formulation (correctness first); the local-attention part dominates.
+// g over d-vectors; everything else runs for all segments at once.  The kernels in this file
+// are the plain fp32 SIMT formulation (the f32 I/O path) plus the chains, which both paths
+// share; the bf16 path's products run on the matrix cores (attention_bwd.hip), and for the
+// linear rule the chains run before the dK, dV kernel, which adds the update's part itself.
 #include "common.hpp"
 #include "kernels.hpp"
 
