@@ -15,9 +15,11 @@
 // M_{s-1}: bound by HBM bandwidth.  One workgroup (4 waves) per (batch, head): d/8 lanes
 // share a key (8 values per lane, one 16-byte load for bf16), so one wave-wide load covers
 // 64/(d/8) keys and is fully coalesced; every lane group keeps its own online-softmax
-// state (exp2 domain, scale folded into q) over a strided subset of the keys, 8 rounds of
-// loads in flight, and the partial states are merged through LDS.  The retrieval reads
-// the fp32 M_{s-1} row by row with 16-byte loads, in parallel with the key loop's loads.
+// state (exp2 domain, scale folded into q) over a strided subset of the keys, and the
+// partial states are merged through LDS.  The key loop is double-buffered: the raw loads of
+// the next batch of rounds (8 keys per lane group for bf16) are in flight while a batch is
+// consumed, and the first batch is issued before the retrieval, which reads the fp32
+// M_{s-1} row by row with 16-byte loads.
 #include <type_traits>
 
 #include "common.hpp"
@@ -28,7 +30,6 @@ namespace infini {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kRounds = 8;   // rounds of key loads in flight per lane
 
 // 8 consecutive elements as float, from bf16 (one 16-byte load) or f32 (two).
 template <bool BF16>
@@ -48,6 +49,50 @@ __device__ __forceinline__ void load8(const void* p, float (&x)[8]) {
       x[4 + i] = __uint_as_float(w1[i]);
     }
   }
+}
+
+// 8 consecutive elements as loaded (bf16: one 16-byte load; f32: two), converted later.
+template <bool BF16>
+struct Raw8 {
+  u32x4 w[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const void* p) {
+  Raw8<BF16> r;
+  r.w[0] = ld16(p);
+  if constexpr (!BF16) r.w[1] = ld16(static_cast<const float*>(p) + 4);
+  return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BF16) {
+      x[2 * i] = bf16lo_to_f32(r.w[0][i]);
+      x[2 * i + 1] = bf16hi_to_f32(r.w[0][i]);
+    } else {
+      x[i] = __uint_as_float(r.w[0][i]);
+      x[4 + i] = __uint_as_float(r.w[1][i]);
+    }
+  }
+}
+
+// x + x of another lane in the same 16-lane row (DPP: no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of G = 8 or 16 lanes, left in every lane of the group: swap
+// neighbours (quad_perm 1,0,3,2), pairs (quad_perm 2,3,0,1), quads within 8 lanes
+// (row_half_mirror) and, for 16, the 8-lane halves of the row (row_mirror).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+  x = dpp_add<0xB1>(x);
+  x = dpp_add<0x4E>(x);
+  x = dpp_add<0x141>(x);
+  if constexpr (G == 16) x = dpp_add<0x140>(x);
+  return x;
 }
 
 template <int D, bool BF16>
@@ -72,6 +117,25 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   const T* vg = static_cast<const T*>(a.v) + static_cast<int64_t>(bh) * D;
   T* kc = static_cast<T*>(a.kc) + static_cast<int64_t>(bh) * a.N * D;
   T* vc = static_cast<T*>(a.vc) + static_cast<int64_t>(bh) * a.N * D;
+
+  // key loop batches: R rounds of NG keys; key t of the batch rounds is read from the cache
+  // for t < p, from the inputs for t == p (this token) and, past the end, from any valid
+  // row (the result is not used), so every load is unconditional
+  constexpr int R = BF16 ? 8 : 4;
+  constexpr int BATCH = NG * R;
+  const int nk = a.p + 1;
+  auto load_batch = [&](int r0, Raw8<BF16> (&kb)[R], Raw8<BF16> (&vb)[R]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int t = r0 + u * NG + grp;
+      const T* kr = t < a.p ? kc + static_cast<int64_t>(t) * D : kg;
+      const T* vr = t < a.p ? vc + static_cast<int64_t>(t) * D : vg;
+      kb[u] = load_raw8<BF16>(kr + 8 * e);
+      vb[u] = load_raw8<BF16>(vr + 8 * e);
+    }
+  };
+  Raw8<BF16> kA[R], vA[R], kB[R], vB[R];
+  load_batch(0, kA, vA);
 
   // append the token to the cache (read back by later launches only) and form sigma(q)
   if (tid < D) {
@@ -116,38 +180,37 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   load8<BF16>(qg + 8 * e, qv);
 #pragma unroll
   for (int i = 0; i < 8; ++i) qv[i] *= a.scale_log2;
-  const int nk = a.p + 1;
   float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int r0 = 0; r0 < nk; r0 += NG * kRounds) {
-    float kk[kRounds][8], vv[kRounds][8];
+  auto consume = [&](int r0, const Raw8<BF16> (&kb)[R], const Raw8<BF16> (&vb)[R]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kRounds; ++u) {
+    for (int u = 0; u < R; ++u) {
       const int t = r0 + u * NG + grp;
-      const T* kr = t < a.p ? kc + static_cast<int64_t>(t) * D : kg;   // past the end: any valid row
-      const T* vr = t < a.p ? vc + static_cast<int64_t>(t) * D : vg;
-      load8<BF16>(kr + 8 * e, kk[u]);
-      load8<BF16>(vr + 8 * e, vv[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kRounds; ++u) {
-      const int t = r0 + u * NG + grp;
+      float kk[8];
+      unpack8<BF16>(kb[u], kk);
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kk[u][i], s);
-#pragma unroll
-      for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kk[i], s);
+      s = group_sum<LPK>(s);
       if (t < nk) {   // uniform across the lane group
+        float vv[8];
+        unpack8<BF16>(vb[u], vv);
         const float m_new = fmaxf(m, s);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // m = -inf on the first key: 0
         const float pw = __builtin_amdgcn_exp2f(s - m_new);
         l = fmaf(l, alpha, pw);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(acc[i], alpha, pw * vv[u][i]);
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(acc[i], alpha, pw * vv[i]);
         m = m_new;
       }
     }
+  };
+  for (int r0 = 0; r0 < nk; r0 += 2 * BATCH) {
+    load_batch(r0 + BATCH, kB, vB);
+    consume(r0, kA, vA);
+    load_batch(r0 + 2 * BATCH, kA, vA);
+    consume(r0 + BATCH, kB, vB);
   }
   if (e == 0) {
     part_m[grp] = m;
