@@ -65,6 +65,8 @@ def _cfg(**kw):
     (dict(batch=0), -1), (dict(heads=0), -1), (dict(segment_len=0), -1), (dict(update=2), -1),
     (dict(io_dtype=5), -1), (dict(eps=-1.0), -1), (dict(eps=float("nan")), -1),
     (dict(softmax_scale=float("inf")), -1), (dict(head_dim=96), -2), (dict(head_dim=256), -2),
+    # one segment's fp32 rows must stay inside a 32-bit buffer range
+    (dict(segment_len=(1 << 22) + 1), -2), (dict(batch=1 << 11, heads=1 << 10), -2),
 ])
 def test_create_rejects_bad_configs_without_a_gpu(lib, kw, status):
     h = ctypes.c_void_p()
