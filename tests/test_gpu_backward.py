@@ -126,3 +126,41 @@ def test_full_size_backward_properties(update):
         torch.cuda.synchronize()
         for name in ("dq", "dk", "dv", "dbeta", "dm0", "dz0"):
             _check_grad((gs[name]).cpu().numpy(), (ga[name] + gb[name]).cpu().numpy(), 2e-2, f"linearity {name}")
+
+
+def test_full_size_linear_update_gradients_closed_form():
+    """8 heads, d=128, N=2048, 32K tokens, linear rule, gate closed (beta = -inf) and dO = 0:
+    only <dm_final, M_final> + <dz_final, z_final> carry gradient.  The retrieval then passes
+    none back (g = 0), so dL/dM_s = dm_final and dL/dz_s = dz_final for every segment (Eq. 8
+    differentiated: M_s = M_{s-1} + sigma(K_s)^T V_s, z_s = z_{s-1} + sum_t sigma(k_t)), and per
+    token dV_t = sigma(k_t) dm_final and dK_t = (dm_final v_t + dz_final) o sigma'(k_t) — the
+    part the dK, dV kernel adds in its epilogue, checked here on sampled tokens of every
+    segment against float64 on the CPU."""
+    gu.require_gpu()
+    base = wl.WORKLOADS[wl.THROUGHPUT_WORKLOAD]
+    w = wl.Workload(base.name + "-linear", 1, base.heads, base.head_dim, base.segment_len, base.n_tokens,
+                    "bf16", "linear", seed=base.seed)
+    H, d, N, L = w.heads, w.head_dim, w.segment_len, w.n_tokens
+    gu.note(f"[backward] closed-form update gradients {w.name}")
+    Q, K, V = wl.stream_inputs(w)
+    rng = np.random.default_rng(66)
+    dmf = rng.standard_normal((1, H, d, d)).astype(np.float32)
+    dzf = rng.standard_normal((1, H, d)).astype(np.float32)
+    dev = [gu.to_dev(x, "bf16") for x in (Q, K, V)]
+    d_out = gu.to_dev(np.zeros((1, H, L, d), dtype=np.float32), "bf16")
+    with binding.InfiniAttention(1, H, d, N, update="linear", eps=w.eps, beta=[-np.inf] * H) as layer:
+        g = layer.backward(*dev, d_out, dm_final=torch.from_numpy(dmf), dz_final=torch.from_numpy(dzf))
+        torch.cuda.synchronize()
+    dk, dv, dq = (g[n].cpu().numpy() for n in ("dk", "dv", "dq"))
+    assert np.all(dq == 0.0), "dQ must vanish with dO = 0 and the gate closed"
+    toks = np.concatenate([s * N + np.array([0, 1, 63, 64, 127, 128, 1000, N - 1]) for s in range(L // N)])
+    for h in (0, 5, H - 1):
+        k64 = K[0, h, toks].astype(np.float64)
+        v64 = V[0, h, toks].astype(np.float64)
+        sig = np.where(k64 > 0, k64 + 1.0, np.exp(k64))
+        dsig = np.where(k64 > 0, 1.0, np.exp(k64))
+        m = dmf[0, h].astype(np.float64)
+        ref_dv = sig @ m
+        ref_dk = (v64 @ m.T + dzf[0, h].astype(np.float64)) * dsig
+        _check_grad(dv[0, h, toks], ref_dv, 2e-2, f"dv h{h}")
+        _check_grad(dk[0, h, toks], ref_dk, 2e-2, f"dk h{h}")
