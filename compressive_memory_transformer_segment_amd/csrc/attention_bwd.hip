@@ -289,6 +289,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
   __shared__ __align__(16) float st0[2][256];   // lse, D of the tile in buffer 0 (first 64 used)
   __shared__ __align__(16) float st1[2][256];
   __shared__ __align__(16) uint16_t gl[FUSE ? 2 * DD : 8];   // G_s rows i, then rows j
+  __shared__ __align__(16) float gz_l[FUSE ? D : 4];          // g_s = dL/dz_s
 
   const WindowArgs& w = b.w;
   const int units = w.units();
@@ -307,6 +308,8 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
   const int kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
   const bool live = key < n;
+  // (FUSE) g_s, loaded now and staged in LDS for the epilogue
+  const float gz_mine = FUSE && threadIdx.x < D ? b.gz[static_cast<int64_t>(u) * D + threadIdx.x] : 0.f;
 
   const uint16_t* qg = static_cast<const uint16_t*>(w.q_loc) + row0 * D;
   const uint16_t* kg = static_cast<const uint16_t*>(w.k_loc) + row0 * D;
@@ -460,7 +463,8 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
   wait_vm_le(0);   // no copy may land in LDS after the workgroup ends
   const float omg = w.gate_omg[h], sc = w.scale * omg;
   if constexpr (FUSE) {
-    __syncthreads();   // every wave's copies of G_s have landed
+    if (threadIdx.x < D) gz_l[threadIdx.x] = gz_mine;
+    __syncthreads();   // every wave's copies of G_s have landed, g_s is staged
     const uint16_t* gr_l = gl;        // G_s, rows i
     const uint16_t* gt_l = gl + DD;   // G_s^T, rows j
     // sigma(k) of this lane's key as the B operand (zero past the segment's end)
@@ -499,7 +503,6 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
     // dK^T = (1 - g) scale (local) + (G_s V^T + g_s) o sigma'(K)^T.  Register 4 q + e of block
     // ib is feature 32 ib + 8 q + 4 hl + e; kreg[ks] holds features 16 ks + 8 hl .. + 7, so
     // the key values of a block come from this lane and its partner lane ^ 32.
-    const float* gzb = b.gz + static_cast<int64_t>(u) * D;
 #pragma unroll
     for (int ib = 0; ib < DB; ++ib) {
       f32x16 sg = zero16();
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i0 = 32 * ib + 8 * q + 4 * hl;
-        const f32x4 gz4 = *reinterpret_cast<const f32x4*>(gzb + i0);
+        const f32x4 gz4 = *reinterpret_cast<const f32x4*>(&gz_l[i0]);
         const u32x4 src = kh[q >> 1][q & 1];   // features 32 ib + 16 (q >> 1) + 8 (q & 1) .. + 7
         u32x4 o;
 #pragma unroll
