@@ -178,19 +178,35 @@ __global__ __launch_bounds__(kBwdThreads, 2) void k_bwd_dq_mfma(const BackwardAr
   __builtin_amdgcn_s_barrier();
 
   // ---- retrieval part: X^T = M dO^T (rows i, columns queries), M_{s-1}[i][j] = mt[j][i]
+  // The epilogue's own operands are loaded first, with no per-lane branch (rows past the
+  // segment end read zeros and their stores are dropped), so that their latency overlaps the
+  // copies of M^T: the PE-free Q values of this lane's query in result-register order,
+  // z_{s-1} (staged in LDS), and the per-query den, dden.
+  const uint32_t seg_el = static_cast<uint32_t>(n) * D;
+  const auto qrs = buffer_rsrc(static_cast<const uint16_t*>(w.q) + row0 * D, seg_el * 2);
+  const auto dqrs = buffer_rsrc(b.dq + row0 * D, seg_el * 4);
+  const uint32_t e0 = static_cast<uint32_t>(q) * D;
+  u32x2 qv[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) qv[db][r4] = buffer_ld8(qrs, 2 * (e0 + 32 * db + 8 * r4 + 4 * hl));
+  const int64_t srow = live ? row : row0;   // a valid row for lanes past the end
+  const float den_ld = b.den[srow], dden_ld = b.dden[srow];
+  const float z_mine = threadIdx.x < D ? w.ws.zb[static_cast<int64_t>(u) * D + threadIdx.x] : 0.f;
   const uint16_t* mt = static_cast<const uint16_t*>(w.ws.mt) + static_cast<int64_t>(u) * D * D;
 #pragma unroll
   for (int t = 0; t < D * D * 2 / 1024 / 4; ++t) copy_rows<D>(mt, D, buf0, wave * (D * D * 2 / 1024 / 4) + t, lane);
+  float* zsh = reinterpret_cast<float*>(buf1);   // buffer 1 is free: its last tile was read
+  if (threadIdx.x < D) zsh[threadIdx.x] = z_mine;
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   //  A operand M[i][16 ks + 8 hl + 0..7] = mt rows 16 ks + 8 hl + 0..7 at column i: lane j of
   //  group G addresses mt row 16 ks + 8 (G / 2) + j / 4 (+ 4), columns 32 db + 16 (G % 2) + 4 (j % 4)
   const int m_rd = (16 * (2 * (G & 1) + ((jl & 3) >> 1)) + 8 * (G >> 1) + (jl >> 2)) * 8 + 4 * (jl & 1);
   const float g = w.gate_g[h], omg = w.gate_omg[h];
-  const float den = live ? b.den[row] : 1.f, dden = live ? b.dden[row] : 0.f;
+  const float den = live ? den_ld : 1.f, dden = live ? dden_ld : 0.f;
   const float gd = g / den;
-  const float* zb = w.ws.zb + static_cast<int64_t>(u) * D;
-  const uint16_t* qm = static_cast<const uint16_t*>(w.q) + row * D;   // PE-free Q of the retrieval
   const float sc = w.scale * omg;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -202,22 +218,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void k_bwd_dq_mfma(const BackwardAr
       const u32x2 a1 = lds_read_tr16(p + 32);
       x = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]}), as_bf16x8(oreg[ks]), x);
     }
-    if (!live) continue;
     // register quad r4 holds features 32 db + 8 r4 + 4 hl + 0..3 of this lane's query
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int i0 = 32 * db + 8 * r4 + 4 * hl;
-      const u32x2 qv = ld8(qm + i0);
-      const f32x4 zv = *reinterpret_cast<const f32x4*>(zb + i0);
-      const float qf[4] = {bf16lo_to_f32(qv[0]), bf16hi_to_f32(qv[0]), bf16lo_to_f32(qv[1]), bf16hi_to_f32(qv[1])};
-      f32x4 o;
+      const f32x4 zv = *reinterpret_cast<const f32x4*>(zsh + i0);
+      const u32x2 qq = qv[db][r4];
+      const float qf[4] = {bf16lo_to_f32(qq[0]), bf16hi_to_f32(qq[0]), bf16lo_to_f32(qq[1]), bf16hi_to_f32(qq[1])};
+      u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float qe = qf[e];
         const float ds = qe > 0.f ? 1.f : __builtin_amdgcn_exp2f(qe * kLog2e);
-        o[e] = acc[db][4 * r4 + e] * sc + (gd * x[4 * r4 + e] + dden * zv[e]) * ds;
+        o[e] = __float_as_uint(acc[db][4 * r4 + e] * sc + (gd * x[4 * r4 + e] + dden * zv[e]) * ds);
       }
-      *reinterpret_cast<f32x4*>(b.dq + row * D + i0) = o;
+      buffer_st16(dqrs, 4 * (e0 + i0), o);
     }
   }
 }
