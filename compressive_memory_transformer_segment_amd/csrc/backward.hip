@@ -317,7 +317,10 @@ __global__ __launch_bounds__(kBT) void k_bwd_r(const BackwardArgs b) {
 // under both rules ((I - Gram_s) G acts on each column alone), so one workgroup owns a block
 // of kChainCols columns of one (batch, head) and walks the segments backwards.
 constexpr int kChainCols = 16;
-template <int D>
+constexpr int kPreCh = 8;   // z chain: R chunk partials per step kept in registers (segments up to 4096 tokens)
+// RCH > 0: the linear rule with exactly RCH chunk partials of R per step (their loads run one
+// step ahead); RCH == 0: any rule, any chunk count.
+template <int D, int RCH>
 __global__ __launch_bounds__(kBT) void k_bwd_chain(const BackwardArgs b) {
   constexpr int TPRW = kBT / D;            // threads per row
   constexpr int CPT = kChainCols / TPRW;   // columns per thread
@@ -331,6 +334,37 @@ __global__ __launch_bounds__(kBT) void k_bwd_chain(const BackwardArgs b) {
 #pragma unroll
   for (int c = 0; c < CPT; ++c)
     G[c] = b.dm_final ? b.dm_final[(static_cast<int64_t>(bh) * D + i) * D + j0 + c] : 0.f;
+  if constexpr (RCH > 0) {
+    // linear: G_{s-1} = G_s + R_s.  The next step's chunk partials of R are loaded while this
+    // step stores, so the loads never wait behind one another.
+    static_assert(CPT % 4 == 0, "columns per thread in float4 groups");
+    f32x4 nx[RCH][CPT / 4];
+    auto fetch = [&](int s) __attribute__((always_inline)) {
+      const int64_t u = static_cast<int64_t>(max(s, 0)) * BH + bh;
+#pragma unroll
+      for (int ch = 0; ch < RCH; ++ch) {
+        const float* rp = b.rpart + ((u * RCH + ch) * D + i) * D + j0;
+#pragma unroll
+        for (int v = 0; v < CPT / 4; ++v) nx[ch][v] = *reinterpret_cast<const f32x4*>(rp + 4 * v);
+      }
+    };
+    fetch(w.W - 1);
+    for (int s = w.W - 1; s >= 0; --s) {
+      float r[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) r[c] = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < RCH; ++ch)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) r[c] += nx[ch][c / 4][c % 4];
+      fetch(s - 1);
+      float* gm = b.gm + (static_cast<int64_t>(s) * BH + bh) * D * D;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) gm[i * D + j0 + c] = G[c];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) G[c] += r[c];
+    }
+  } else {   // delta rule, or more chunks than the registers hold
   for (int s = w.W - 1; s >= 0; --s) {
     const int u = s * BH + bh;
     float* gm = b.gm + static_cast<int64_t>(u) * D * D;
@@ -359,6 +393,7 @@ __global__ __launch_bounds__(kBT) void k_bwd_chain(const BackwardArgs b) {
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) G[c] = nG[c];
+  }
   }
   if (b.dm0) {
 #pragma unroll
@@ -486,6 +521,25 @@ __global__ __launch_bounds__(D) void k_bwd_zchain(const BackwardArgs b) {
   const WindowArgs& w = b.w;
   const int bh = static_cast<int>(blockIdx.x), BH = w.B * w.H, i = threadIdx.x;
   float gz = b.dz_final ? b.dz_final[static_cast<int64_t>(bh) * D + i] : 0.f;
+  if (!w.delta && b.rch <= kPreCh) {   // linear: next step's partials loaded one step ahead
+    float nx[kPreCh];
+    auto fetch = [&](int s) __attribute__((always_inline)) {
+      const int64_t u = static_cast<int64_t>(max(s, 0)) * BH + bh;
+#pragma unroll
+      for (int ch = 0; ch < kPreCh; ++ch) nx[ch] = b.rzpart[(u * b.rch + min(ch, b.rch - 1)) * D + i];
+    };
+    fetch(w.W - 1);
+    for (int s = w.W - 1; s >= 0; --s) {
+      float r = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < kPreCh; ++ch) r += ch < b.rch ? nx[ch] : 0.f;
+      fetch(s - 1);
+      b.gz[(static_cast<int64_t>(s) * BH + bh) * D + i] = gz;
+      gz += r;
+    }
+    if (b.dz0) b.dz0[static_cast<int64_t>(bh) * D + i] = gz;
+    return;
+  }
   for (int s = w.W - 1; s >= 0; --s) {
     const int u = s * BH + bh;
     b.gz[static_cast<int64_t>(u) * D + i] = gz;
@@ -550,7 +604,12 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
     // kernel adds the memory-update part (sigma(K) G_s, (V G_s^T + g_s) o sigma'(K)) itself
     hipError_t e = launch_bwd_r_mfma(b, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
+    const dim3 cgrid(BH * (D / kChainCols));
+    if (b.rch == 1) hipLaunchKernelGGL((k_bwd_chain<D, 1>), cgrid, dim3(kBT), 0, st, b);
+    else if (b.rch == 2) hipLaunchKernelGGL((k_bwd_chain<D, 2>), cgrid, dim3(kBT), 0, st, b);
+    else if (b.rch == 4) hipLaunchKernelGGL((k_bwd_chain<D, 4>), cgrid, dim3(kBT), 0, st, b);
+    else if (b.rch == 8) hipLaunchKernelGGL((k_bwd_chain<D, 8>), cgrid, dim3(kBT), 0, st, b);
+    else hipLaunchKernelGGL((k_bwd_chain<D, 0>), cgrid, dim3(kBT), 0, st, b);
     hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
     e = launch_bwd_gpack(b, st);
     if (e == hipSuccess) e = launch_bwd_dkv_mfma(b, true, st);
@@ -568,7 +627,7 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
     } else {
       hipLaunchKernelGGL((k_bwd_r<D, BF16>), dim3(static_cast<unsigned>(w.units() * b.rch)), dim3(kBT), 0, st, b);
     }
-    hipLaunchKernelGGL((k_bwd_chain<D>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
+    hipLaunchKernelGGL((k_bwd_chain<D, 0>), dim3(BH * (D / kChainCols)), dim3(kBT), 0, st, b);
     if constexpr (BF16) {
       const hipError_t e = launch_bwd_update_mfma(b, st);
       if (e != hipSuccess) return e;

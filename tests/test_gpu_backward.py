@@ -38,6 +38,9 @@ CASES = [
     ("bf16-delta-d64-state", 2, 1, 64, 96, 2 * 96 + 40, "bf16", "delta", True, True),
     # several 128-key tiles per segment and a ragged last tile (the linear rule's fused epilogue)
     ("bf16-linear-d128-n320-state", 1, 2, 128, 320, 2 * 320 + 77, "bf16", "linear", True, True),
+    # two and three 512-token chunks of the R pass per segment (the chains' register paths)
+    ("bf16-linear-d64-n1024-state", 1, 1, 64, 1024, 2 * 1024 + 100, "bf16", "linear", True, True),
+    ("bf16-linear-d64-n1100", 1, 1, 64, 1100, 2 * 1100 + 9, "bf16", "linear", False, True),
     ("f32-linear-d128", 1, 2, 128, 64, 2 * 64 + 17, "f32", "linear", True, True),
     ("f32-delta-d128", 1, 2, 128, 64, 2 * 64 + 17, "f32", "delta", True, True),
     ("f32-delta-d64-n1", 1, 2, 64, 1, 5, "f32", "delta", False, True),
