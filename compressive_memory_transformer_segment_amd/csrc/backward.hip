@@ -570,11 +570,21 @@ constexpr int kBetaThreads = 1024;
 __global__ __launch_bounds__(kBetaThreads) void k_bwd_dbeta(const BackwardArgs b) {
   const WindowArgs& w = b.w;
   const int h = static_cast<int>(blockIdx.x);
-  float acc = 0.f;
+  // eight independent partial sums, so that eight loads per thread are in flight at once
+  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int bb = 0; bb < w.B; ++bb) {
     const float* x = b.bq + (static_cast<int64_t>(bb) * w.H + h) * w.T;
-    for (int64_t t = threadIdx.x; t < w.T; t += kBetaThreads) acc += x[t];
+    int64_t t = threadIdx.x;
+    for (; t + 7 * kBetaThreads < w.T; t += 8 * kBetaThreads) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = x[t + k * kBetaThreads];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc8[k] += v[k];
+    }
+    for (; t < w.T; t += kBetaThreads) acc8[0] += x[t];
   }
+  float acc = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
   __shared__ float red[kBetaThreads / 64];
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
