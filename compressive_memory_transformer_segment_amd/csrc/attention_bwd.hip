@@ -817,29 +817,43 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_r_mfma(const BackwardArgs b
   const uint16_t* qg = static_cast<const uint16_t*>(w.q);
   const uint16_t* og = static_cast<const uint16_t*>(b.dout);
 
-  for (int t0 = t_lo; t0 < t_hi; t0 += SUB) {
+  // The rows of a 64-token tile: this thread's RPS rows of Q and dO (16 bytes each) and their
+  // den, dden, loaded with no per-lane branch (rows past the chunk end re-read its last row and
+  // are zeroed when used) one tile ahead of their use, so the loads never wait behind one another.
+  constexpr int RPS = SUB / PH;
+  struct RowSet {
+    u32x4 q[RPS], o[RPS];
+    float den[RPS], dz[RPS];
+  };
+  auto fetch = [&](int t0, RowSet& rs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < RPS; ++p) {
+      const int t = min(t0 + p * PH + rp, t_hi - 1);
+      const int64_t x = (row0 + t) * D + 8 * cl;
+      rs.q[p] = ld16(qg + x);
+      rs.o[p] = ld16(og + x);
+      rs.den[p] = b.den[row0 + t];
+      rs.dz[p] = b.dden[row0 + t];
+    }
+  };
+  auto consume = [&](int t0, const RowSet& rs) __attribute__((always_inline)) {
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < SUB / PH; ++p) {
-      const int r = p * PH + rp, t = t0 + r;
+    for (int p = 0; p < RPS; ++p) {
+      const int r = p * PH + rp;
+      const bool ok = t0 + r < t_hi;
+      const float sc = ok ? g / rs.den[p] : 0.f, dz = ok ? rs.dz[p] : 0.f;
       float sv[8], dv[8];
-      if (t < t_hi) {
-        const int64_t x = (row0 + t) * D + 8 * cl;
-        const u32x4 qv = ld16(qg + x), ov = ld16(og + x);
-        const float sc = g / b.den[row0 + t], dz = b.dden[row0 + t];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[2 * e] = elu_plus_one(bf16lo_to_f32(qv[e]));
-          sv[2 * e + 1] = elu_plus_one(bf16hi_to_f32(qv[e]));
-          dv[2 * e] = bf16lo_to_f32(ov[e]) * sc;
-          dv[2 * e + 1] = bf16hi_to_f32(ov[e]) * sc;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rzp[e] = fmaf(sv[e], dz, rzp[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] = dv[e] = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float s0 = elu_plus_one(bf16lo_to_f32(rs.q[p][e])), s1 = elu_plus_one(bf16hi_to_f32(rs.q[p][e]));
+        sv[2 * e] = ok ? s0 : 0.f;
+        sv[2 * e + 1] = ok ? s1 : 0.f;
+        dv[2 * e] = bf16lo_to_f32(rs.o[p][e]) * sc;
+        dv[2 * e + 1] = bf16hi_to_f32(rs.o[p][e]) * sc;
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rzp[e] = fmaf(sv[e], dz, rzp[e]);
       st16(sq_l + rg_index(r, 8 * cl, CPR), u32x4{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
                                                   pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7])});
       st16(dn_l + rg_index(r, 8 * cl, CPR), u32x4{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]),
@@ -859,6 +873,15 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_r_mfma(const BackwardArgs b
                               __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]}), acc[k]);
       }
     }
+  };
+  RowSet ra, rb;
+  fetch(t_lo, ra);
+  for (int t0 = t_lo; t0 < t_hi; t0 += 2 * SUB) {
+    fetch(t0 + SUB, rb);
+    consume(t0, ra);
+    if (t0 + SUB >= t_hi) break;
+    fetch(t0 + 2 * SUB, ra);
+    consume(t0 + SUB, rb);
   }
   // R block (ib, jb): register r of lane l holds R[32 ib + 8 (r / 4) + 4 hl + r % 4][32 jb + l % 32]
   float* rpo = b.rpart + (static_cast<int64_t>(u) * b.rch + ch) * D * D;
