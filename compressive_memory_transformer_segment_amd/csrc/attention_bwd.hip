@@ -585,11 +585,15 @@ __global__ __launch_bounds__(kBwdThreads, D == 128 ? 1 : 2) void k_bwd_dkv_mfma(
 template <int D>
 __global__ __launch_bounds__(kBwdThreads, 1) void k_bwd_update_mfma(const BackwardArgs b) {
   constexpr int KS = D / 16, DB = D / 32, CPR = D / 8, DD = D * D;
-  __shared__ __align__(16) uint16_t gt_l[DD];               // G_s^T (rows j)
-  __shared__ __align__(16) uint16_t gr_l[DD];               // G_s (rows i)
-  __shared__ __align__(16) uint16_t mt_l[DD];   // M_{s-1}^T (rows j)
-  __shared__ __align__(16) uint16_t mr_l[DD];   // M_{s-1} (rows i)
-  __shared__ float cacc[D];
+  // G_s^T (rows j), G_s (rows i), M_{s-1}^T (rows j), M_{s-1} (rows i); once the products
+  // are done, the first half holds the tile's per-token sigma(k_t) ddenk_t rows (fp32)
+  __shared__ __align__(16) uint16_t lds[4 * DD];
+  uint16_t* gt_l = lds;
+  uint16_t* gr_l = lds + DD;
+  uint16_t* mt_l = lds + 2 * DD;
+  uint16_t* mr_l = lds + 3 * DD;
+  float* crow = reinterpret_cast<float*>(lds);   // [128 tokens][D]
+  static_assert(128 * D * 4 <= 4 * DD * 2, "the per-token rows fit in the staging area");
 
   const WindowArgs& w = b.w;
   const int u = static_cast<int>(blockIdx.x) / b.ct, tile = static_cast<int>(blockIdx.x) % b.ct;
@@ -621,7 +625,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_bwd_update_mfma(const Backwa
                  x[6] | (uint32_t(x[7]) << 16)});
     }
   }
-  if (tid < D) cacc[tid] = 0.f;
   __syncthreads();
 
   // Token rows are read and written through buffer resources that end at the segment's
@@ -729,11 +732,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_bwd_update_mfma(const Backwa
         S[ib] = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), dwb[j4], S[ib]);
       }
     }
-    // this tile's share of sigma(K)^T ddenk (wf and ddk are zero past the segment's end)
+  }
+  // this tile's share of sigma(K)^T ddenk (wf and ddk are zero past the segment's end):
+  // every token's row sigma(k_t) ddenk_t goes to LDS once all waves are done with the
+  // staged G_s and M_{s-1}, and is summed over the tile's tokens in token order (no
+  // atomics: the result does not depend on the order in which the waves arrive)
+  __syncthreads();
+  {
+    float* cr = crow + (32 * wave + l32) * D + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x4 lo, hi;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) atomicAdd(&cacc[16 * ks + 8 * hl + e], wf[ks][e] * ddk);
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = wf[ks][e] * ddk;
+        hi[e] = wf[ks][4 + e] * ddk;
+      }
+      *reinterpret_cast<f32x4*>(cr + 16 * ks) = lo;
+      *reinterpret_cast<f32x4*>(cr + 16 * ks + 4) = hi;
+    }
   }
   // dV += Y (all loads of a block first, then the stores)
 #pragma unroll
@@ -776,7 +793,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_bwd_update_mfma(const Backwa
     }
   }
   __syncthreads();
-  if (tid < D) b.cpart[(static_cast<int64_t>(u) * b.ct + tile) * D + tid] = cacc[tid];
+  if (tid < D) {
+    float c = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < 128; ++r) c += crow[r * D + tid];
+    b.cpart[(static_cast<int64_t>(u) * b.ct + tile) * D + tid] = c;
+  }
 }
 
 // R_s = sigma(Q)^T dnum and r_s = sigma(Q)^T dden over one chunk of a segment (dnum = g dO /
