@@ -22,7 +22,7 @@ UPDATE = {"linear": 0, "delta": 1}
 DTYPE = {"bf16": 0, "f32": 1}
 TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OOM = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OOM, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 
 
 class Config(ctypes.Structure):
@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "infini_attn_forward_stream": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_forward_stream_ex": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_forward_stream_local": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+        "infini_attn_forward_stream_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp]),
         "infini_attn_project_qkv": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_project_out": (ctypes.c_int, [vp, vp, vp, vp, i64, i32, vp]),
         "infini_attn_forward_layer": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, i32, vp]),
@@ -201,6 +202,17 @@ class InfiniAttention:
             st = self._lib.infini_attn_forward_stream_ex(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                                          _ptr(a_mem), _ptr(a_dot), n, _stream_ptr(stream))
             _check("infini_attn_forward_stream_ex", st)
+        return out
+
+    def forward_stream_noalloc(self, q, k, v, out=None, stream=None):
+        """forward_stream with the window workspace in the library's static scratch array
+        (the call allocates no device memory; ``out`` must then be given by a caller that
+        cannot allocate)."""
+        self._check_io(q, k, v, out)
+        out = self._out_like(q, out)
+        st = self._lib.infini_attn_forward_stream_noalloc(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                          q.shape[2], _stream_ptr(stream))
+        _check("infini_attn_forward_stream_noalloc", st)
         return out
 
     def forward_stream_local(self, q, k, v, q_local=None, k_local=None, out=None, stream=None):

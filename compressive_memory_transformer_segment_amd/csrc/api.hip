@@ -19,6 +19,13 @@
 
 #define INFINI_EXPORT extern "C" __attribute__((visibility("default")))
 
+// Window workspace of infini_attn_forward_stream_noalloc, for callers that cannot allocate
+// device memory: one array per device, held from the library's first use on that device
+// until the process ends.  Host code never passes this name to a kernel or a copy: it
+// resolves the device address once per device (scratch_resolve) and uses that.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 struct infini_attn {
   infini_attn_config_t cfg;
   int device;
@@ -112,23 +119,33 @@ size_t unit_bytes(const infini_attn& h) {
   if (h.delta) b += DD * 4;          // gs
   return b + part_bytes(h);          // at least one chunk slot per unit
 }
-int chunks_for(const infini_attn& h, int w_call) {
+int chunks_for(const infini_attn& h, int w_call, int part_cap) {
   if (!h.bf16) return 1;
   const int units = w_call * h.BH;
   // a power of two (the chain kernel is specialised on it), at most 8, and no more chunks
   // than 64-token sub-tiles
   const int want = (kStateTargetWorkgroups + units - 1) / units;
   int chk = 1;
-  while (chk * 2 <= want && chk * 2 <= 8 && chk * 2 <= std::max(1, h.NP / 64) && w_call * chk * 2 <= h.part_cap)
+  while (chk * 2 <= want && chk * 2 <= 8 && chk * 2 <= std::max(1, h.NP / 64) && w_call * chk * 2 <= part_cap)
     chk *= 2;
   return chk;
 }
 
+int chunks_for(const infini_attn& h, int w_call) { return chunks_for(h, w_call, h.part_cap); }
+
+// Chunk-partial slots per (b,h) that windows of up to w segments need.
+int part_cap_for(const infini_attn& h, int w) {
+  int cap = w;
+  if (h.bf16)
+    for (int wc = 1; wc <= w; ++wc) cap = std::max(cap, wc * chunks_for(h, wc, 1 << 30));
+  return cap;
+}
+
 // Workspace layout: one window of units plus the chunk-partial slots.
 template <typename F>
-void layout(const infini_attn& h, F&& take) {
-  const size_t U = size_t(h.window) * h.BH;
-  const size_t P = size_t(h.part_cap) * h.BH;
+void layout(const infini_attn& h, int window, int part_cap, F&& take) {
+  const size_t U = size_t(window) * h.BH;
+  const size_t P = size_t(part_cap) * h.BH;
   const size_t D = h.D, DD = D * D;
   take(0, P * D * 4);                                // dz
   take(1, P * DD * 4);                               // u
@@ -138,26 +155,79 @@ void layout(const infini_attn& h, F&& take) {
   take(5, U * D * 4);                                // zb
 }
 
-size_t layout_bytes(const infini_attn& h) {
+size_t layout_bytes(const infini_attn& h, int window, int part_cap) {
   size_t b = 0;
-  layout(h, [&](int, size_t bytes) { b += align_up(bytes, 256); });
+  layout(h, window, part_cap, [&](int, size_t bytes) { b += align_up(bytes, 256); });
   return b;
 }
 
-void carve(infini_attn& h) {
-  char* p = static_cast<char*>(h.ws_base);
+// The window workspace carved from `base` (256-byte aligned); returns its size in bytes.
+size_t carve(const infini_attn& h, int window, int part_cap, void* base, infini::Workspace& ws) {
+  char* p = static_cast<char*>(base);
   void* ptrs[6] = {};
-  layout(h, [&](int i, size_t bytes) {
+  layout(h, window, part_cap, [&](int i, size_t bytes) {
     ptrs[i] = bytes ? p : nullptr;
     p += align_up(bytes, 256);
   });
-  h.ws.dz = static_cast<float*>(ptrs[0]);
-  h.ws.u = static_cast<float*>(ptrs[1]);
-  h.ws.g = static_cast<float*>(ptrs[2]);
-  h.ws.gs = static_cast<float*>(ptrs[3]);
-  h.ws.mt = ptrs[4];
-  h.ws.zb = static_cast<float*>(ptrs[5]);
-  h.ws_bytes = static_cast<size_t>(p - static_cast<char*>(h.ws_base));
+  ws.dz = static_cast<float*>(ptrs[0]);
+  ws.u = static_cast<float*>(ptrs[1]);
+  ws.g = static_cast<float*>(ptrs[2]);
+  ws.gs = static_cast<float*>(ptrs[3]);
+  ws.mt = ptrs[4];
+  ws.zb = static_cast<float*>(ptrs[5]);
+  return static_cast<size_t>(p - static_cast<char*>(base));
+}
+
+// Where a forward call's window workspace lives: segments per window, chunk-partial slots
+// per (b,h) and the carved buffers.
+struct WindowPlan {
+  infini::Workspace ws;
+  int window;
+  int part_cap;
+};
+
+WindowPlan handle_plan(const infini_attn& h) { return WindowPlan{h.ws, h.window, h.part_cap}; }
+
+// Device address of `scratch` on each device (nullptr: not resolved yet).
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;
+
+// Resolves the address of `scratch` on `device`, which must be the current device.
+hipError_t scratch_resolve(int device) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (device < 0) return hipErrorInvalidDevice;
+  if (static_cast<int>(g_scratch_ptr.size()) <= device) g_scratch_ptr.resize(size_t(device) + 1, nullptr);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return e != hipSuccess ? e : hipErrorInvalidSymbol;
+  }
+  g_scratch_ptr[device] = p;
+  return hipSuccess;
+}
+
+void* scratch_ptr(int device) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return device >= 0 && device < static_cast<int>(g_scratch_ptr.size()) ? g_scratch_ptr[device] : nullptr;
+}
+
+// The window workspace of one call of S segments carved from the scratch array at
+// `base`: the longest window (at most the handle's) whose workspace fits kScratchBytes,
+// with chunk-partial slots for exactly the windows the call runs (full ones and the
+// last), each chunked as forward_stream chunks a window of its length.
+int scratch_plan(const infini_attn& h, int64_t S, void* base, WindowPlan& plan) {
+  for (int w = static_cast<int>(std::min<int64_t>(h.window, S)); w >= 1; --w) {
+    const int w_last = static_cast<int>(S - (S - 1) / w * w);
+    const int cap = h.bf16 ? std::max(w * chunks_for(h, w, 1 << 30), w_last * chunks_for(h, w_last, 1 << 30)) : w;
+    if (layout_bytes(h, w, cap) > kScratchBytes) continue;
+    plan.window = w;
+    plan.part_cap = cap;
+    carve(h, w, cap, base, plan.ws);
+    return INFINI_OK;
+  }
+  return INFINI_ERR_SCRATCH;
 }
 
 void gate_values(const float* beta, int H, float* out) {
@@ -224,7 +294,7 @@ hipError_t timed(infini_attn* h, int kind, hipStream_t st, F&& launch) {
 
 int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void* out, float* a_mem,
                float* a_dot, int64_t n_tokens, void* hip_stream, const void* q_loc = nullptr,
-               const void* k_loc = nullptr) {
+               const void* k_loc = nullptr, const WindowPlan* plan_in = nullptr) {
   if (!live(h)) return INFINI_ERR_INVALID_ARG;
   if (h->dec_p > 0) return INFINI_ERR_INVALID_ARG;   // a decode segment is open: flush it first
   int rc = check_io(h, q, k, v, out, n_tokens);
@@ -245,6 +315,7 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   DeviceGuard dg(h->device);
   if (!dg.ok) return INFINI_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const WindowPlan plan = plan_in ? *plan_in : handle_plan(*h);
 
   infini::WindowArgs a{};
   a.q = q;
@@ -271,12 +342,12 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   a.gate_omg = h->gate + h->cfg.heads;
   a.M = h->M;
   a.z = h->z;
-  a.ws = h->ws;
+  a.ws = plan.ws;
   a.zero_state = h->state_zero;
-  for (int s0 = 0; s0 < a.S; s0 += h->window) {
+  for (int s0 = 0; s0 < a.S; s0 += plan.window) {
     a.s0 = s0;
-    a.W = std::min(h->window, a.S - s0);
-    a.chk = chunks_for(*h, a.W);
+    a.W = std::min(plan.window, a.S - s0);
+    a.chk = chunks_for(*h, a.W, plan.part_cap);
     a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));   // trailing chunks may be empty
     hipError_t e = hipSuccess;
     if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
@@ -367,6 +438,7 @@ INFINI_EXPORT const char* infini_attn_status_string(int status) {
     case INFINI_ERR_UNSUPPORTED: return "unsupported configuration";
     case INFINI_ERR_HIP: return "HIP runtime error";
     case INFINI_ERR_OOM: return "out of device memory";
+    case INFINI_ERR_SCRATCH: return "one segment's workspace exceeds the static scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -408,17 +480,12 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   if (c.max_window_segments > 0) w = std::min(w, c.max_window_segments);
   h->window = w;
   // chunk partials: enough slots for the chunking chosen at any window size
-  int cap = w;
-  if (h->bf16) {
-    h->part_cap = 1 << 30;
-    for (int wc = 1; wc <= w; ++wc) cap = std::max(cap, wc * chunks_for(*h, wc));
-  }
-  h->part_cap = cap;
+  h->part_cap = part_cap_for(*h, w);
 
   DeviceGuard dg(h->device);
   const size_t DD = size_t(h->D) * h->D;
   const size_t m_bytes = size_t(h->BH) * DD * 4, z_bytes = size_t(h->BH) * h->D * 4;
-  const size_t ws_bytes = layout_bytes(*h);
+  const size_t ws_bytes = layout_bytes(*h, h->window, h->part_cap);
   // M and z in one allocation (z follows M), so one fill resets both
   if (hipMalloc(&h->M, m_bytes + z_bytes) != hipSuccess) { (void)hipGetLastError(); delete h; return INFINI_ERR_OOM; }
   h->z = h->M + size_t(h->BH) * DD;
@@ -429,7 +496,8 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
     (void)hipGetLastError();
     return INFINI_ERR_OOM;
   }
-  carve(*h);
+  h->ws_bytes = carve(*h, h->window, h->part_cap, h->ws_base, h->ws);
+  (void)scratch_resolve(h->device);   // for forward_stream_noalloc; checked again there
   {
     std::lock_guard<std::mutex> lk(g_live_mu);
     g_live.insert(h);
@@ -481,6 +549,24 @@ INFINI_EXPORT int infini_attn_forward_stream_local(infini_attn_t h, const void* 
                                                    const void* v, const void* q_local, const void* k_local,
                                                    void* out, int64_t n_tokens, void* hip_stream) {
   return run_stream(h, q, k, v, out, nullptr, nullptr, n_tokens, hip_stream, q_local, k_local);
+}
+
+INFINI_EXPORT int infini_attn_forward_stream_noalloc(infini_attn_t h, const void* q, const void* k,
+                                                     const void* v, void* out, int64_t n_tokens,
+                                                     void* hip_stream) {
+  if (!live(h)) return INFINI_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return INFINI_ERR_HIP;
+  void* base = scratch_ptr(h->device);
+  if (!base) {
+    if (scratch_resolve(h->device) != hipSuccess) return INFINI_ERR_HIP;
+    base = scratch_ptr(h->device);
+  }
+  if (n_tokens < 1) return INFINI_ERR_INVALID_ARG;
+  WindowPlan plan{};
+  const int rc = scratch_plan(*h, (n_tokens + h->N - 1) / h->N, base, plan);
+  if (rc) return rc;
+  return run_stream(h, q, k, v, out, nullptr, nullptr, n_tokens, hip_stream, nullptr, nullptr, &plan);
 }
 
 INFINI_EXPORT int infini_attn_forward_segment(infini_attn_t h, const void* q, const void* k, const void* v,

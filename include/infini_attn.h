@@ -54,6 +54,8 @@ extern "C" {
 #define INFINI_ERR_UNSUPPORTED (-2)
 #define INFINI_ERR_HIP (-3)
 #define INFINI_ERR_OOM (-4)
+#define INFINI_ERR_SCRATCH (-5) /* forward_stream_noalloc: one segment's workspace exceeds its
+                                   static scratch array */
 
 typedef struct infini_attn* infini_attn_t;
 
@@ -112,6 +114,23 @@ int infini_attn_forward_stream_ex(infini_attn_t h, const void* q, const void* k,
 int infini_attn_forward_stream_local(infini_attn_t h, const void* q, const void* k, const void* v,
                                      const void* q_local, const void* k_local, void* out,
                                      int64_t n_tokens, void* hip_stream);
+
+/* forward_stream for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * arguments, with the window workspace (chunk partials of the state pass, the recorded
+ * M^T_{s-1} and z_{s-1} of every segment) taken from a static device array of 32 MiB that
+ * the library holds on each device from its first use there until the process ends,
+ * instead of the handle's workspace.  The call allocates nothing; the handle (state, gate
+ * values) comes from infini_attn_create as usual.  Windows are as long as the handle's
+ * window and the array allow; with a window as long as forward_stream's the results are
+ * bit-identical to it.  If the workspace of one segment (about 97 KB per (batch, head)
+ * at d = 128, linear rule; 225 KB delta) exceeds the array, returns INFINI_ERR_SCRATCH
+ * before enqueuing anything.  Every call on a device shares that device's array: calls
+ * that may overlap on one device (other streams, other threads, other handles) race and
+ * must be serialised by the caller.  Nothing in the array needs to start at zero: each
+ * window writes every part of it it reads. */
+int infini_attn_forward_stream_noalloc(infini_attn_t h, const void* q, const void* k, const void* v,
+                                       void* out, int64_t n_tokens, void* hip_stream);
 
 /* M = 0, z = 0: the memory before the first segment of a new stream (Eq. 4 with an
  * empty history).  Takes effect for every later call on the handle; enqueues no device

@@ -18,7 +18,7 @@ EXPECTED = {
     "infini_attn_profile_enable", "infini_attn_profile_read",
     "infini_attn_project_qkv", "infini_attn_project_out", "infini_attn_forward_layer",
     "infini_attn_decode_step", "infini_attn_decode_flush", "infini_attn_decode_position",
-    "infini_attn_backward",
+    "infini_attn_backward", "infini_attn_forward_stream_noalloc",
 }
 
 
@@ -51,6 +51,7 @@ def test_status_strings(lib):
     assert binding.status_string(-2) == "unsupported configuration"
     assert binding.status_string(-3) == "HIP runtime error"
     assert binding.status_string(-4) == "out of device memory"
+    assert "static scratch" in binding.status_string(-5)
     assert binding.status_string(12345) == "unknown status"
 
 
