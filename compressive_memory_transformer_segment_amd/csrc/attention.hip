@@ -13,10 +13,11 @@
 // registers (Q is the B operand of S^T) as the B operand of A_mem^T = M^T sigma(Q)^T.
 //
 // K and V tiles (64 keys x d) go from HBM straight into LDS with buffer -> LDS copies,
-// four buffers deep: the copies of tiles j + 1 .. j + 3 (after the last tile: M^T_{s-1}
-// and z_{s-1}) are in flight while tile j is consumed, and no registers hold data in
-// transit.  The scores of tile j + 1 are computed while the softmax of tile j runs.  Rows past
-// the segment end arrive as zeros (buffer range check), so ragged tails need no branches.
+// four buffers deep: the copy of tile j + 3 (after the last tile: M^T_{s-1} and z_{s-1})
+// is in flight while tile j is consumed, and no registers hold data in transit.  The
+// scores of tile j + 1 are computed while the softmax of tile j runs, and every group of
+// MFMAs finds its LDS operands already read into registers.  Rows past the segment end
+// arrive as zeros (buffer range check), so ragged tails need no branches.
 // The V^T operand of O^T += V^T P^T is read with LDS transpose reads, in the key order the
 // S^T result registers hold.  The online softmax is in the exp2 domain with the scale
 // folded in, and rescales the accumulator lazily: only when a row maximum grows by more
@@ -191,24 +192,17 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
                    4 * (lane & 1);
   auto swz = [](int row) __attribute__((always_inline)) -> int { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
 
-  // ---- prologue.  Every wave copies its own 32 rows of Q (row-group layout, rows >= n
-  // as zeros) into buffer 2 (waves 0-3) or 3 (waves 4-7) and reads them into registers
-  // itself; tiles 0 and 1 go into buffers 0 and 1.  Copy 2 of the sequence is issued once
-  // every wave is done with its Q rows.
+  // ---- prologue.  Every lane loads its query's Q row straight into the B-operand
+  // registers (rows >= n read as zeros); tiles 0, 1 and 2 go into buffers 0, 1 and 2.
   {
-    uint16_t* qs = (wave < 4 ? buf2 : buf3) + (wave & 3) * 32 * D;
-    const uint16_t* qsrc = qg + static_cast<int64_t>(qw0) * D;
-    const uint32_t qbytes = static_cast<uint32_t>(max(n - qw0, 0)) * D * 2;
+    const auto qr = buffer_rsrc(qg + static_cast<int64_t>(qw0) * D, static_cast<uint32_t>(max(n - qw0, 0)) * D * 2);
 #pragma unroll
-    for (int c = 0; c < CPR / 2; ++c) copy_group(c, qsrc, qbytes, qs);
-    const int c0 = issue(0, buf0);
-    const int c1 = issue(1, buf1);
-    wait_vm_le(c0 + c1);   // this wave's Q rows
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = ld16(qs + g_rd + 256 * ks);
-    wait_vm_le(0);   // tiles 0 and 1; Q read
-    __builtin_amdgcn_s_barrier();
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = buffer_ld16(qr, static_cast<uint32_t>(l32 * D + 16 * ks + 8 * hl) * 2);
+    issue(0, buf0);
+    issue(1, buf1);
     issue(2, buf2);
+    wait_vm_le(0);
+    __builtin_amdgcn_s_barrier();
   }
 
   const float c2 = a.scale_log2;
@@ -320,24 +314,99 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   // Unmasked tiles j < jm = q0 / 64 (a multiple of 4) run software-pipelined: iteration j
   // holds the scores of tile j (sc0 / sc1, maximum mxc) and computes those of tile j + 1
   // while it exponentiates and multiplies tile j, so a wave's own MFMAs run under its
-  // softmax arithmetic.  Buffer j % 4 holds tile j; copy j + 3 of the sequence goes into
-  // buffer (j + 3) % 4, consumed in iteration j - 1.  The closing wait leaves only this
-  // wave's copy j + 3 in flight: after the barrier tiles j + 1 and j + 2 are complete.
+  // softmax arithmetic.  Every group of MFMAs finds its LDS operands already in registers:
+  // the operands of the next group are read while a group runs.  An iteration has four
+  // phases of 8 MFMAs each:
+  //   1. S^T(j + 1), k-steps 0 .. KS/2 - 1 (both key halves) | exp of tile j, half 0 | read K, k-steps KS/2 ..
+  //   2. S^T(j + 1), k-steps KS/2 .. KS - 1                 | exp of tile j, half 1 | read V^T(j), half 0
+  //   3. O^T += V^T P^T(j), half 0                          | max of tile j + 1    | read V^T(j), half 1
+  //   4. O^T += V^T P^T(j), half 1                          |                      | read K(j + 2), k-steps 0 ..
+  // Buffer j % 4 holds tile j.  Copy j + 3 of the sequence is issued at the start of
+  // iteration j into buffer (j + 3) % 4 (tile j - 1, done with at the previous barrier) and
+  // waited for at its end, so tiles j + 1 and j + 2 are complete throughout iteration j.
   const int jm = q0 / kBN;
+  constexpr int KH = KS / 2;   // k-steps per operand group
+  typedef bf16x8 KOps[2][KH];  // [key half][k-step]
+  auto load_k = [&](const uint16_t* kt, int k0, KOps& ak) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < KH; ++i) ak[hh][i] = as_bf16x8(ld16(kt + g_rd + hh * 256 * CPR + 256 * (k0 + i)));
+  };
+  auto qk_part = [&](const KOps& ak, int k0, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KH; ++i) {
+      s0 = mfma32x32x16(ak[0][i], as_bf16x8(qreg[k0 + i]), s0);
+      s1 = mfma32x32x16(ak[1][i], as_bf16x8(qreg[k0 + i]), s1);
+    }
+  };
   f32x16 sc0, sc1;
-  qk_tile(buf0, sc0, sc1);   // tile 0
+  KOps kq;
+  load_k(buf0, 0, kq);
+  sc0 = zero16();
+  sc1 = zero16();
+  qk_part(kq, 0, sc0, sc1);
+  load_k(buf0, KH, kq);
+  qk_part(kq, KH, sc0, sc1);   // tile 0
   float mxc = tile_max(sc0, sc1);
+  if (jm > 0) load_k(buf1, 0, kq);   // tile 1, k-steps 0 .. KH - 1
   auto pstep = [&](int j, auto bufc) __attribute__((always_inline)) {
     constexpr int b = decltype(bufc)::value;
     maybe_rescale(mxc);
     issue(j + 3, bufp(IC<b + 3>{}));
-    f32x16 n0, n1;
-    qk_tile(bufp(IC<b + 1>{}), n0, n1);   // tile j + 1 (tile jm, masked later, at the end)
-    finish_tile(bufp(bufc), sc0, sc1);
-    mxc = tile_max(n0, n1);
+    const uint16_t* kt = bufp(bufc);
+    f32x16 n0 = zero16(), n1 = zero16();
+    bf16x8 p0, p1, p2, p3;
+    KOps kq2;
+    bf16x8 va[DB][2], vb[DB][2];
+    // phase 1
+    load_k(bufp(IC<b + 1>{}), KH, kq2);
+    qk_part(kq, 0, n0, n1);
+    half_exp(sc0, p0, p1);
+    // interleave: each MFMA followed by its share of the LDS reads and the VALU work
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);   // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 2
+    v_operands(kt, 0, va);
+    qk_part(kq2, KH, n0, n1);
+    half_exp(sc1, p2, p3);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB / KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 3
+    v_operands(kt, 1, vb);
+    pv(va, p0, p1);
+    const float mh0 = half_max(n0);
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 4
+    load_k(bufp(IC<b + 2>{}), 0, kq);   // tile j + 2 (read but unused past the last tile)
+    pv(vb, p2, p3);
+    mxc = max_across_halves(fmaxf(mh0, half_max(n1))) * c2;
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KS / DB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     sc0 = n0;
     sc1 = n1;
-    wait_vm_le(count(j + 3));
+    wait_vm_le(0);
     __builtin_amdgcn_s_barrier();
   };
   for (int j = 0; j < jm; j += 4) {
