@@ -15,7 +15,19 @@ With --layer a step is one ``infini_attn_forward_layer`` instead: the whole laye
 its input X [B, T, d_model] to O, the Q/K/V projection (Eq. 5) and the output projection
 (Eq. 11) included; the roofline is then that of the kernel with the most time per step.
 
+With --workload NAME the step runs another workload of the library's set (the delta-rule
+32K streams at batch 1 and 4, the 512K-token 32-head stream, the 1M-token stream); streams
+longer than 16 segments are built on the device from a pool of 16 distinct segments used
+cyclically (the values do not change the kernels' work).  With --per-segment the 1M-token
+stream is fed one ``infini_attn_forward_segment`` call per segment (the streaming path)
+and the line also carries the device-memory evidence (used bytes after 1, 64, 256 and 512
+segments).
+
+Step time = median over the K timed steps (each bracketed by HIP events on the launch
+stream); the mean is reported next to it.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer]
+       [--per-segment] [--decode] [--backward] [--local-qk]
 """
 
 from __future__ import annotations
@@ -53,6 +65,10 @@ def parse():
     ap.add_argument("--decode-batch", type=int, default=64, help="--decode: sequences decoded together")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--per-segment", action="store_true",
+                    help="streaming: one forward_segment call per segment of the stream (default workload: 1M tokens)")
+    ap.add_argument("--pool-segments", type=int, default=16,
+                    help="distinct segments drawn for streams longer than this (used cyclically)")
     return ap.parse_args()
 
 
@@ -70,38 +86,120 @@ def traffic_from_profiles(kernel_hash: str):
     return float(m_bytes.group(1))
 
 
+def _blas_info():
+    """(library description, threads) of the BLAS numpy uses here."""
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if infos:
+            p = infos[0]
+            return f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer', '')})", int(p.get("num_threads", 1))
+    except Exception:
+        pass
+    return "unknown", 1
+
+
+def _oracle_worker_init():
+    import numpy  # noqa: F401
+    from compressive_memory_transformer_segment_amd import workloads  # noqa: F401
+    from oracle import infini_oracle  # noqa: F401
+
+
+def _oracle_worker_ready(_):
+    return os.getpid()
+
+
+def _oracle_unit(job):
+    """One (batch element, head) of a workload through the oracle with one BLAS thread (the
+    process-pool worker); see _oracle_pair.  Returns the seconds spent in the oracle."""
+    from threadpoolctl import threadpool_limits
+    w, b, h, segs, synthetic_state = job
+    with threadpool_limits(1):
+        return _oracle_pair(w, b, h, segs, synthetic_state)
+
+
 def cpu_baseline(w, budget_s: float):
-    """The oracle (numpy float64, as written) on whole heads of the same stream until about
-    budget_s seconds of CPU work; reported as layer tokens/s (all heads)."""
+    """The oracle (numpy float64, as written), timed on the host cores:
+    * value: all cores, a process pool over the (batch, head) pairs with one BLAS thread per
+      worker (the pairs' chains are independent), wall time of the pool;
+    * single_core: one (batch, head) pair on one core, scaled to all pairs;
+    * blas_threaded: whole heads in this process with the BLAS library's own threads.
+    Streams of up to 32 segments run in full from the zero state; longer ones run a seeded
+    sample of segments (first 2, last 2, 4 random) from a synthetic state and the rate is
+    extrapolated (a segment's cost does not depend on the state).  Tokens/s of the layer
+    (all heads)."""
+    import multiprocessing as mp
+    import numpy as np
+    blas, blas_threads = _blas_info()
+    cores = len(os.sched_getaffinity(0))
+    S = w.n_segments
+    if S <= 32:
+        segs, synthetic, sample = list(range(S)), False, "the full stream"
+    else:
+        rng = np.random.default_rng(w.seed)
+        mid = sorted(rng.choice(np.arange(2, S - 2), size=4, replace=False).tolist())
+        segs, synthetic = [0, 1] + mid + [S - 2, S - 1], True
+        sample = f"segments {segs} (extrapolated to all {S})"
+    seg_tokens = sum(w.segment_len_of(s) for s in segs)
+    units = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    # single core: one pair
+    t_one = _oracle_unit((w, 0, 0, segs, synthetic))
+    single = {"value": w.batch * w.n_tokens / (t_one * (w.n_tokens / seg_tokens) * len(units)), "cores": 1,
+              "sample": f"one (batch, head) pair, {sample}, {t_one:.1f} s, scaled to {len(units)} pairs"}
+    # all cores: pool over the pairs (as many as fit the budget, at least one round)
+    workers = max(1, min(cores, len(units), 16))
+    per_unit = t_one
+    n_units = max(workers, min(len(units), int(budget_s * workers / max(per_unit, 1e-9)) // workers * workers))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers, initializer=_oracle_worker_init) as pool:
+        pool.map(_oracle_worker_ready, range(workers))   # workers started, modules imported
+        t0 = time.perf_counter()
+        pool.map(_oracle_unit, [(w, b, h, segs, synthetic) for b, h in units[:n_units]], chunksize=1)
+        wall = time.perf_counter() - t0
+    value = w.batch * w.n_tokens / (wall * (w.n_tokens / seg_tokens) * (len(units) / n_units))
+    return {"value": value, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "affinity_cores": cores, "blas": blas,
+            "sample": (f"process pool of {workers} workers (one BLAS thread each) over {n_units} of "
+                       f"{len(units)} (batch, head) pairs, {sample}, {wall:.1f} s wall (input generation "
+                       "included, worker start-up not)" + ("" if n_units == len(units) else ", scaled to all pairs")),
+            "single_core": single,
+            "blas_threaded": cpu_baseline_threaded(w, min(budget_s, 6.0), blas_threads, segs, synthetic, sample)}
+
+
+def cpu_baseline_threaded(w, budget_s, blas_threads, segs, synthetic, sample):
+    """Whole (batch, head) pairs in this process, BLAS with its own threads."""
+    done, el = 0, 0.0
+    for h in range(w.heads):
+        el += _oracle_pair(w, 0, h, segs, synthetic)
+        done += 1
+        if el >= budget_s:
+            break
+    seg_tokens = sum(w.segment_len_of(s) for s in segs)
+    per_unit = el / done * (w.n_tokens / seg_tokens)
+    return {"value": w.batch * w.n_tokens / (per_unit * w.batch * w.heads), "cores": blas_threads,
+            "sample": f"{done} (batch, head) pairs, {sample}, {el:.1f} s, scaled to all pairs"}
+
+
+def _oracle_pair(w, b, h, segs, synthetic_state):
+    """segment_forward on the listed segments of pair (b, h) in order, the state carried
+    from M0, z0: zero (the exact stream from its start) or, for a sample of segments, a
+    synthetic state (a segment's cost does not depend on the state's values).  Returns the
+    seconds spent in the oracle (input generation excluded)."""
     import numpy as np
     from compressive_memory_transformer_segment_amd import workloads as wl
     from oracle import infini_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
-    beta = wl.beta_for(w)
-    done_heads, elapsed = 0, 0.0
-    for h in range(w.heads):
-        qkv = [np.empty((1, 1, w.n_tokens, w.head_dim), dtype=np.float32) for _ in range(3)]
-        for s in range(w.n_segments):
-            lo = s * w.segment_len
-            parts = wl.segment_inputs(w, 0, s, heads=[h])
-            for x, p in zip(qkv, parts):
-                x[0, 0, lo:lo + p.shape[1]] = p[0]
+    beta = wl.beta_for(w)[h]
+    scale = 1.0 / np.sqrt(w.head_dim)
+    d = w.head_dim
+    M = np.full((d, d), 1e-3) if synthetic_state else np.zeros((d, d))
+    z = np.full(d, 1.0) if synthetic_state else np.zeros(d)
+    el = 0.0
+    for s in segs:
+        q, k, v = (x[0].astype(np.float64) for x in wl.segment_inputs(w, b, s, heads=[h]))
         t0 = time.perf_counter()
-        orc.forward(*qkv, beta[h:h + 1], w.segment_len, w.update, eps=w.eps)
-        elapsed += time.perf_counter() - t0
-        done_heads += 1
-        if elapsed >= budget_s:
-            break
-    per_head_s = elapsed / done_heads
-    value = w.batch * w.n_tokens / (per_head_s * w.heads)
-    return {"value": value, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "affinity_cores": len(os.sched_getaffinity(0)),
-            "sample": (f"oracle.forward over the full {w.n_tokens}-token stream of {done_heads} of "
-                       f"{w.heads} heads ({elapsed:.1f} s), scaled to all heads")}
+        _, M, z, _, _ = orc.segment_forward(q, k, v, M, z, beta, w.update, w.eps, scale)
+        el += time.perf_counter() - t0
+    return el
 
 
 def cpu_baseline_layer(w, d_model: int, budget_s: float):
@@ -375,16 +473,169 @@ def main_backward(args):
     print(json.dumps(rec), flush=True)
 
 
+def device_inputs(w, dev, pool_segments: int):
+    """Q, K, V [B, H, L, d] bf16 on the device.  Streams of at most pool_segments segments
+    are drawn exactly; longer ones repeat the first pool_segments segments cyclically (the
+    kernels' work does not depend on the values), with the planted pair, if any, written at
+    its place (token 0 of segment 0; the query at the last token).  Returns the tensors and
+    a description."""
+    import torch
+    from compressive_memory_transformer_segment_amd import workloads as wl
+    shape = (w.batch, w.heads, w.n_tokens, w.head_dim)
+    Q, K, V = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    S, N = w.n_segments, w.segment_len
+    exact = S <= pool_segments
+    for b in range(w.batch):
+        for s in range(S if exact else pool_segments):
+            lo = s * N
+            for x, p in zip((Q, K, V), wl.segment_inputs(w, b, s, plant=False)):
+                x[b, :, lo:lo + p.shape[1]] = torch.from_numpy(p).to(dev, torch.bfloat16)
+        if not exact:   # segments pool_segments .. S - 1 repeat the pool
+            span = pool_segments * N
+            for lo in range(span, w.n_tokens, span):
+                n = min(span, w.n_tokens - lo)
+                for x in (Q, K, V):
+                    x[b, :, lo:lo + n] = x[b, :, :n]
+    if w.plant:
+        k_star, v_star = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in wl.planted_pair(w))
+        K[:, :, 0], V[:, :, 0], Q[:, :, w.n_tokens - 1] = k_star, v_star, k_star
+    torch.cuda.synchronize()
+    desc = ("exact seeded draws" if exact else
+            f"first {pool_segments} segments drawn (seeded), repeated cyclically over the {S} segments")
+    return Q, K, V, desc
+
+
+def timed_steps(step, steps: int, stream):
+    """K steps between two synchronisations, each step bracketed by HIP events on the launch
+    stream; returns (per-step milliseconds, wall milliseconds of the K steps)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    return [e0.elapsed_time(e1) for e0, e1 in evs], wall_ms
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def main_per_segment(args):
+    """The streaming path: the stream fed one infini_attn_forward_segment call per segment
+    (as a caller streaming segment by segment would), against forward_stream on the same
+    stream; plus the device-memory evidence of constant memory in the stream length."""
+    import torch
+    from compressive_memory_transformer_segment_amd import binding, profiling
+    from compressive_memory_transformer_segment_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload or "h8-d128-n2048-l1m-linear-planted"]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    Q, K, V, desc = device_inputs(w, dev, args.pool_segments)
+    out = torch.empty_like(Q)
+    N, S = w.segment_len, w.n_segments
+    seg_views = [tuple(x[:, :, s * N:min((s + 1) * N, w.n_tokens)].contiguous() for x in (Q, K, V))
+                 for s in range(min(S, args.pool_segments))]   # contiguous [B, H, n, d] per call
+    seg_out = torch.empty_like(seg_views[0][0])
+    layer = binding.InfiniAttention(w.batch, w.heads, w.head_dim, N, update=w.update, io_dtype="bf16",
+                                    eps=w.eps, beta=wl.beta_for(w))
+    stream = torch.cuda.current_stream()
+    mem = {}
+
+    def step_segments(record_mem=False):
+        layer.reset_state(stream)
+        for s in range(S):
+            q, k, v = seg_views[s % len(seg_views)]
+            layer.forward_segment(q, k, v, out=seg_out, stream=stream)
+            if record_mem and (s + 1) in (1, 64, 256, 512):
+                torch.cuda.synchronize()
+                free, total = torch.cuda.mem_get_info()
+                mem[s + 1] = total - free
+
+    def step_stream():
+        layer.reset_state(stream)
+        layer.forward_stream(Q, K, V, out=out, stream=stream)
+
+    step_segments(record_mem=True)
+    for _ in range(args.warmup):
+        step_segments()
+        step_stream()
+    torch.cuda.synchronize()
+    steps = max(3, args.steps // 4)
+    print(f"[bench] {w.name} per segment: timing {steps} streams of {S} forward_segment calls", file=sys.stderr,
+          flush=True)
+    seg_ms, wall_ms = timed_steps(step_segments, steps, stream)
+    str_ms, _ = timed_steps(step_stream, steps, stream)
+    layer.profile_enable(True)
+    step_segments()
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    torch.cuda.synchronize()
+    ms = median(seg_ms)
+    tokens = w.batch * w.n_tokens
+    att_ms, att_n = prof["attention"]
+    seg_flops = profiling.attention_kernel_flops(w.batch, w.heads, w.head_dim, N, N)
+    achieved = seg_flops / (att_ms / att_n / 1e3) / 1e12
+    rec = {
+        "metric": METRIC + " [streamed: one forward_segment call per segment]",
+        "value": tokens / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "mean_ms_per_step": sum(seg_ms) / len(seg_ms),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + "-per-segment", "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "segment_len": N, "n_tokens": w.n_tokens, "update": w.update, "inputs": desc,
+                   "step": f"reset_state + {S} forward_segment calls of {N} tokens", "parallelism": "none"},
+        "roofline": {
+            "kernel": "k_attn_bf16 (local attention + retrieval + gate), one segment per launch",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": profiling.PEAK_BF16_FLOPS / 1e12,
+            "unit": "TFLOP/s",
+            "frac": achieved / (profiling.PEAK_BF16_FLOPS / 1e12),
+            "traffic": None,
+            "algorithmic_flops": seg_flops,
+            "avg_launch_us": att_ms / att_n * 1e3,
+        },
+        "forward_stream_same_stream": {"ms_per_step": median(str_ms), "value": tokens / (median(str_ms) / 1e3),
+                                       "per_segment_over_windowed": median(seg_ms) / median(str_ms)},
+        "kernels_avg_us": {k: (t / n * 1e3 if n else None) for k, (t, n) in prof.items()},
+        "wall_ms_per_step": wall_ms / steps,
+        "memory": {"device_bytes": layer.device_bytes(),
+                   "used_bytes_after_segments": {str(k): v for k, v in sorted(mem.items())},
+                   "constant": len(set(mem.values())) == 1},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget_s),
+    }
+    layer.close()
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
-    if args.decode and args.gpus == 1:
-        return main_decode(args)
-    if args.backward and args.gpus == 1:
-        return main_backward(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        return main_decode(args)
+    if args.backward:
+        return main_backward(args)
+    if args.per_segment:
+        return main_per_segment(args)
 
     import numpy as np
     import torch
@@ -405,13 +656,7 @@ def main():
         del Xh, Wqh, Woh
         out_l = torch.empty_like(X)
     else:            # per-head Q, K, V
-        shape = (w.batch, w.heads, w.n_tokens, w.head_dim)
-        Q, K, V = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
-        for b in range(w.batch):
-            for s in range(w.n_segments):
-                lo = s * w.segment_len
-                for x, p in zip((Q, K, V), wl.segment_inputs(w, b, s)):
-                    x[b, :, lo:lo + p.shape[1]] = torch.from_numpy(p).to(dev, torch.bfloat16)
+        Q, K, V, inputs_desc = device_inputs(w, dev, args.pool_segments)
         out = torch.empty_like(Q)
     layer = binding.InfiniAttention(w.batch, w.heads, w.head_dim, w.segment_len, update=w.update,
                                     io_dtype="bf16", eps=w.eps, beta=wl.beta_for(w))
@@ -441,17 +686,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: warmup {args.warmup} done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    # timed region: K steps between two synchronisations
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    ms = ev0.elapsed_time(ev1) / args.steps
+    # timed region: K steps between two synchronisations, each step between two events
+    step_ms, wall_ms = timed_steps(step, args.steps, stream)
+    ms = median(step_ms)
 
     # the same K steps with every kernel bracketed by HIP events on the launch stream
     layer.profile_enable(True)
@@ -490,6 +727,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "mean_ms_per_step": sum(step_ms) / len(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -499,7 +737,8 @@ def main():
                    "head_dim": w.head_dim, "segment_len": w.segment_len, "n_tokens": w.n_tokens,
                    "update": w.update, "local_qk": bool(args.local_qk),
                    "projections": bool(args.layer), "d_model": d_model if args.layer else None,
-                   "parallelism": "none"},
+                   "inputs": "exact seeded draws" if args.layer else inputs_desc,
+                   "step_time": "median of the timed steps", "parallelism": "none"},
         "pct_bf16_peak": 100.0 * flops_step / (ms / 1e3) / profiling.PEAK_BF16_FLOPS,
         "roofline": {
             "kernel": rooflines[dominant]["kernel"],
