@@ -81,9 +81,15 @@ typedef struct {
                                   bounds the workspace; <= 0 picks a default */
 } infini_attn_config_t;
 
-/* Create a layer.  beta_host: H gate logits (host memory, copied; +-inf allowed).
- * Allocates M = 0, z = 0 and the workspace on the current device.  hip_stream orders
- * the zero fill.  *out receives the handle. */
+/* Create a layer (architecture summary, section "Multi-Head Infini-Attention": every head
+ * keeps its own compressive memory, a d_key x d_value matrix M and a d_key vector z, and
+ * its own gate scalar beta; Eq. 10 mixes the two arms with sigmoid(beta)).
+ * beta_host: H gate logits (host memory, copied; +-inf allowed: sigmoid(beta) and
+ * 1 - sigmoid(beta) are formed in double as exact complements, so +-inf selects one arm).
+ * Allocates M = 0, z = 0 (the empty memory before the first segment, Eq. 4), the gate
+ * values and the workspace on the current device.  hip_stream orders the zero fill.
+ * *out receives the handle.  Errors: INVALID_ARG for a bad config or NULL pointers,
+ * UNSUPPORTED for head_dim other than 64 / 128 or segment_len > 2^22, OOM, HIP. */
 int infini_attn_create(const infini_attn_config_t* cfg, const float* beta_host,
                        void* hip_stream, infini_attn_t* out);
 
@@ -143,12 +149,16 @@ int infini_attn_reset_state(infini_attn_t h, void* hip_stream);
 int infini_attn_get_state(infini_attn_t h, float* M, float* z, void* hip_stream);
 int infini_attn_set_state(infini_attn_t h, const float* M, const float* z, void* hip_stream);
 
-/* Replace the H gate logits (host memory).  Waits for the device to be idle first. */
+/* Replace the H gate logits beta of Eq. 10 (host memory; one per head, section "The Gating
+ * Mechanism").  Waits for the device to be idle first, so no call in flight sees a mix. */
 int infini_attn_set_beta(infini_attn_t h, const float* beta_host);
 
 /* Device bytes the handle holds: state + gate values + workspace, plus the layer scratch
  * once forward_layer has run (at most one window's worth) and the decode cache once
- * decode_step has run (one segment).  Independent of how many tokens have been processed. */
+ * decode_step has run (one segment).  Independent of how many tokens have been processed:
+ * the bounded-memory property of the compressive memory (summary page, "Multi-Head
+ * Infini-Attention", memory footprint per layer: H (d_key d_value + d_key) numbers of
+ * state, here in fp32, 66,048 bytes per head at d = 128). */
 int64_t infini_attn_device_bytes(infini_attn_t h);
 
 /* Tokens per internal window of forward_stream (window segments * N). */
@@ -239,7 +249,7 @@ int infini_attn_backward(infini_attn_t h, const void* q, const void* k, const vo
  * handle launches is bracketed by two events on the call's stream.  profile_read waits
  * for the recorded events, reports the summed durations per kernel kind, and clears the
  * record.  Kernel kinds: 0 = key sums (delta rule only), 1 = state pass (per-segment
- * sigma(K)^T V, key sums, delta Gram term, V transpose), 2 = memory chain (Eq. 8/9
+ * sigma(K)^T V, key sums, delta Gram term), 2 = memory chain (Eq. 8/9
  * recurrence), 3 = fused local attention + retrieval + gate (Eq. 6, 7, 10),
  * 4 = Q/K/V projection (Eq. 5), 5 = output projection (Eq. 11), 6 = decoding step,
  * 7 = backward (all gradient kernels of one call; the recomputed forward counts as 0-3). */
