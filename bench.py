@@ -287,6 +287,7 @@ def main_decode(args):
     layer = binding.InfiniAttention(B, H, d, N, update=base.update, io_dtype="bf16", eps=base.eps,
                                     beta=wl.beta_for(base))
     stream = torch.cuda.current_stream()
+    copy_probe(args.copy_probe_mib, dev)
 
     def step():   # one whole segment token by token; the last token closes it into the memory
         for t in range(N):
@@ -473,6 +474,18 @@ def main_backward(args):
     print(json.dumps(rec), flush=True)
 
 
+def copy_probe(mib: int, dev) -> None:
+    """One device copy of `mib` MiB before timing (calibrates the HBM byte counters)."""
+    if mib <= 0:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def device_inputs(w, dev, pool_segments: int):
     """Q, K, V [B, H, L, d] bf16 on the device.  Streams of at most pool_segments segments
     are drawn exactly; longer ones repeat the first pool_segments segments cyclically (the
@@ -547,6 +560,7 @@ def main_per_segment(args):
     layer = binding.InfiniAttention(w.batch, w.heads, w.head_dim, N, update=w.update, io_dtype="bf16",
                                     eps=w.eps, beta=wl.beta_for(w))
     stream = torch.cuda.current_stream()
+    copy_probe(args.copy_probe_mib, dev)
     mem = {}
 
     def step_segments(record_mem=False):
@@ -662,12 +676,7 @@ def main():
                                     io_dtype="bf16", eps=w.eps, beta=wl.beta_for(w))
     stream = torch.cuda.current_stream()
 
-    if args.copy_probe_mib > 0:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(args.copy_probe_mib, dev)
 
     if args.local_qk and not args.layer:   # distinct buffers; the values do not change the kernels' work
         Ql, Kl = Q.clone(), K.clone()

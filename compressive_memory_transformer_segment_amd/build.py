@@ -51,6 +51,23 @@ def _compile(src: str, obj: str) -> None:
         print(msgs, file=sys.stderr)
 
 
+PROBES = {"ceilings.hip": "ceilings"}   # hardware-ceiling probe (measurement only, not linked)
+
+
+def build_probes(verbose: bool = True) -> None:
+    """Compile the measurement probes under probes/ into executables next to their sources."""
+    pdir = os.path.join(PKG_DIR, "probes")
+    for src, exe in PROBES.items():
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               os.path.join(pdir, src), "-o", os.path.join(pdir, exe)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for probes/{src}:\n{res.stdout}\n{res.stderr}")
+        if verbose:
+            print(f"built {os.path.join(pdir, exe)}")
+
+
 def build(verbose: bool = True) -> str:
     """Compile all sources (in parallel) and link the shared library; returns its path."""
     obj_dir = os.path.join(PKG_DIR, "_build")
@@ -67,6 +84,7 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+    build_probes(verbose)
     return LIB_PATH
 
 

@@ -168,6 +168,69 @@ def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int, algorithmic_bytes
     return "\n".join(lines)
 
 
+def _stats_avg_us(stats_csv: str):
+    """Average duration (us) per kernel (short name) from a --kernel-trace --stats csv."""
+    out = {}
+    for r in csv.DictReader(open(stats_csv)):
+        name = r.get("Name") or r.get("KernelName") or ""
+        out[_short(name)] = float(r.get("AverageNs", 0)) / 1e3
+    return out
+
+
+def traffic_table(fetch_csv: str, write_csv: str, copy_mib: int, stats_csv: str, algorithmic=None) -> str:
+    """Markdown table of the HBM bytes per dispatch of every library kernel in two counter
+    passes (FETCH_SIZE, WRITE_SIZE), each scaled by the factor the same counter reads for
+    the device copy of ``copy_mib`` MiB, with the achieved bandwidth over the kernel's
+    average duration from a kernel-trace run of the same command, against 8 TB/s.
+    ``algorithmic``: optional {kernel short name: algorithmic bytes per dispatch}."""
+    known = copy_mib * 1024.0
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    kf = known / max(fetch["__amd_rocclr_copyBuffer"])
+    kw = known / max(write["__amd_rocclr_copyBuffer"])
+    avg_us = _stats_avg_us(stats_csv)
+    algorithmic = algorithmic or {}
+    lines = [f"copy-probe factors: FETCH_SIZE x{kf:.4f}, WRITE_SIZE x{kw:.4f}", "",
+             "| kernel | dispatches | read MB | write MB | total MB | avg us | GB/s | of 8 TB/s | algorithmic MB | ratio |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for name in fetch:
+        if not name.startswith("k_") or name not in write:
+            continue
+        fr = sum(fetch[name]) / len(fetch[name]) * kf * 1024 / 1e6
+        wr = sum(write[name]) / len(write[name]) * kw * 1024 / 1e6
+        tot = fr + wr
+        us = avg_us.get(name)
+        gbs = tot * 1e6 / (us * 1e-6) / 1e9 if us else None
+        alg = algorithmic.get(name)
+        lines.append(f"| `{name}` | {len(fetch[name])} | {fr:.1f} | {wr:.1f} | {tot:.1f} | "
+                     + (f"{us:.1f} | {gbs:.0f} | {gbs / (PEAK_HBM_BYTES / 1e9):.2f}" if us else "- | - | -")
+                     + (f" | {alg / 1e6:.1f} | {tot * 1e6 / alg:.2f} |" if alg else " | - | - |"))
+    return "\n".join(lines)
+
+
+def state_kernel_bytes(batch, heads, head_dim, segment_len, n_tokens, update, chunks):
+    """Algorithmic HBM bytes of the state pass and the chain over one window holding the
+    whole stream (S segments, `chunks` partial slots per segment): the state pass reads K
+    and V once (bf16) and writes its partial sums once (fp32: key sums, (sigma(K)^T V)^T and,
+    delta, the Gram term); the chain reads the partials and the state, writes the state,
+    the bf16 M^T_{s-1} and the z_{s-1} of every segment.  Returns {kernel: bytes}."""
+    d, S = head_dim, len(segment_lengths(n_tokens, segment_len))
+    bh = batch * heads
+    kv = bh * n_tokens * d * 2 * 2
+    part = d * 4 + d * d * 4 + (d * d * 4 if update == "delta" else 0)
+    parts = bh * S * chunks * part
+    state = bh * (d * d + d) * 4
+    chain = parts + 2 * state + bh * S * (d * d * 2 + d * 4)
+    out = {}
+    if update == "delta":
+        out["k_keysum_bf16<128>"] = bh * n_tokens * d * 2 + bh * S * chunks * d * 4
+        out["k_state_delta_bf16<128>"] = kv + parts
+    else:
+        out["k_state_lin_bf16<128>"] = kv + parts
+    out["chain"] = chain
+    return out
+
+
 if __name__ == "__main__":
     what = sys.argv[1]
     if what == "stats":
@@ -178,6 +241,9 @@ if __name__ == "__main__":
         # hbm <fetch csv> <write csv> <copy MiB> : the C1-shaped attention launch
         alg = attention_kernel_bytes(1, 8, 128, 2048, 32768)
         print(hbm_summary(sys.argv[2], sys.argv[3], int(sys.argv[4]), alg))
+    elif what == "traffic":
+        # traffic <fetch csv> <write csv> <copy MiB> <kernel stats csv>
+        print(traffic_table(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5]))
     elif what == "hash":
         print(kernel_source_hash())
     else:
