@@ -46,6 +46,21 @@ struct infini_attn {
   size_t bwd_bytes = 0;
   void* dec_cache = nullptr;   // decoding: K then V cache of the open segment, [B,H,N,D] each
   int dec_p = 0;               // tokens of the open decode segment (0: none open)
+  // bf16 handles: M^T of the carried state in bf16 ([B,H,d_value,d_key]), the retrieval
+  // operand of one-segment calls and of decoding; written by every chain launch (and by
+  // set_state), zero while state_zero is set
+  void* mt_cur = nullptr;
+  // one-segment calls with few (batch, head) pairs: split-key attention partials and counts,
+  // and a second stream on which the memory-update kernels run next to the attention
+  void* split_buf = nullptr;
+  size_t split_bytes = 0;
+  float* split_acc = nullptr;
+  float* split_ml = nullptr;
+  int* split_cnt = nullptr;
+  int split_kc = 0;            // key tiles per chunk
+  int split_slots = 0;         // partial slots per (batch, head) pair
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   infini::Workspace ws;
   // per-kernel event timing (measurement only)
   bool profiling = false;
@@ -292,6 +307,31 @@ hipError_t timed(infini_attn* h, int kind, hipStream_t st, F&& launch) {
   return e;
 }
 
+int device_compute_units(int device) {
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || c <= 0) {
+    (void)hipGetLastError();
+    c = 256;
+  }
+  return c;
+}
+
+constexpr int kQueryTile = 256;   // queries per attention item (bf16)
+constexpr int kKeyTile = 64;      // keys per attention tile (bf16)
+
+// Split-key chunks of query tile qt of an n-token segment, kc key tiles per chunk.
+int split_chunks(int qt, int n, int kc) {
+  const int nkv = (std::min(qt * kQueryTile + kQueryTile, n) + kKeyTile - 1) / kKeyTile;
+  return (nkv + kc - 1) / kc;
+}
+
+// Split-key items of one (batch, head) pair for an n-token segment.
+int split_items(int n, int kc) {
+  int p = 0;
+  for (int qt = 0; qt * kQueryTile < n; ++qt) p += split_chunks(qt, n, kc);
+  return p;
+}
+
 int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void* out, float* a_mem,
                float* a_dot, int64_t n_tokens, void* hip_stream, const void* q_loc = nullptr,
                const void* k_loc = nullptr, const WindowPlan* plan_in = nullptr) {
@@ -344,6 +384,38 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   a.z = h->z;
   a.ws = plan.ws;
   a.zero_state = h->state_zero;
+  a.mt_cur = h->mt_cur;
+  if (h->split_buf && !plan_in && a.S == 1 && !a_mem && !a_dot) {
+    // One segment with few (batch, head) pairs.  The attention reads the carried state
+    // (its bf16 M^T and z) and does not depend on this segment's memory update, so the
+    // update kernels run on the second stream meanwhile; the chain, which writes the new
+    // state, runs after both.  The attention splits the keys of a query tile over several
+    // workgroups, so that the few pairs fill the compute units.
+    a.s0 = 0;
+    a.W = 1;
+    a.chk = chunks_for(*h, 1, plan.part_cap);
+    a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
+    hipError_t e = hipEventRecord(h->ev_fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
+    if (e == hipSuccess && h->delta) e = timed(h, 0, h->side, [&] { return infini::launch_key_sums(a, h->side); });
+    if (e == hipSuccess) e = timed(h, 1, h->side, [&] { return infini::launch_state_pass(a, h->side); });
+    if (e == hipSuccess) e = hipEventRecord(h->ev_join, h->side);
+    infini::WindowArgs at = a;
+    at.ws.mt = h->mt_cur;
+    at.ws.zb = h->z;
+    at.split_kc = h->split_kc;
+    at.split_items = split_items(a.n_last, h->split_kc);
+    at.split_slots = h->split_slots;
+    at.split_acc = h->split_acc;
+    at.split_ml = h->split_ml;
+    at.split_cnt = h->split_cnt;
+    if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(at, st); });
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_join, 0);
+    if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+    if (e != hipSuccess) return INFINI_ERR_HIP;
+    h->state_zero = false;
+    return INFINI_OK;
+  }
   for (int s0 = 0; s0 < a.S; s0 += plan.window) {
     a.s0 = s0;
     a.W = std::min(plan.window, a.S - s0);
@@ -498,6 +570,39 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   }
   h->ws_bytes = carve(*h, h->window, h->part_cap, h->ws_base, h->ws);
   (void)scratch_resolve(h->device);   // for forward_stream_noalloc; checked again there
+  if (h->bf16) {
+    const size_t mt_bytes = size_t(h->BH) * DD * 2;
+    bool ok = hipMalloc(&h->mt_cur, mt_bytes) == hipSuccess;
+    // split-key attention for one-segment calls when the pairs' query tiles fill at most
+    // the compute units: at most 4 chunks per query tile
+    const int nq = (h->N + kQueryTile - 1) / kQueryTile;
+    if (ok && int64_t(h->BH) * nq <= device_compute_units(h->device)) {
+      h->split_kc = std::max(8, (nq + 3) / 4 * 4);
+      h->split_slots = split_items(h->N, h->split_kc);
+      const size_t slots = size_t(h->BH) * h->split_slots;
+      const size_t acc_b = align_up(slots * 256 * h->D * 4, 256), ml_b = align_up(slots * 1024 * 4, 256);
+      const size_t cnt_b = align_up(size_t(h->BH) * nq * 4, 256);
+      h->split_bytes = acc_b + ml_b + cnt_b;
+      ok = hipMalloc(&h->split_buf, h->split_bytes) == hipSuccess &&
+           hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) == hipSuccess;
+      if (ok) {
+        h->split_acc = static_cast<float*>(h->split_buf);
+        h->split_ml = reinterpret_cast<float*>(static_cast<char*>(h->split_buf) + acc_b);
+        h->split_cnt = reinterpret_cast<int*>(static_cast<char*>(h->split_buf) + acc_b + ml_b);
+      }
+    }
+    if (!ok) {
+      (void)hipGetLastError();
+      {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        g_live.insert(h);
+      }
+      infini_attn_destroy(h);
+      return INFINI_ERR_OOM;
+    }
+  }
   {
     std::lock_guard<std::mutex> lk(g_live_mu);
     g_live.insert(h);
@@ -509,6 +614,9 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   hipError_t e = hipMemcpy(h->gate, gv, size_t(2) * c.heads * 4, hipMemcpyHostToDevice);
   delete[] gv;
   if (e == hipSuccess) e = hipMemsetAsync(h->M, 0, m_bytes + z_bytes, st);
+  if (e == hipSuccess && h->mt_cur) e = hipMemsetAsync(h->mt_cur, 0, size_t(h->BH) * DD * 2, st);
+  if (e == hipSuccess && h->split_cnt)
+    e = hipMemsetAsync(h->split_cnt, 0, size_t(h->BH) * ((h->N + kQueryTile - 1) / kQueryTile) * 4, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) { infini_attn_destroy(h); return INFINI_ERR_HIP; }
   *out = h;
@@ -530,6 +638,11 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   if (h->layer_buf) (void)hipFree(h->layer_buf);
   if (h->dec_cache) (void)hipFree(h->dec_cache);
   if (h->bwd_buf) (void)hipFree(h->bwd_buf);
+  if (h->mt_cur) (void)hipFree(h->mt_cur);
+  if (h->split_buf) (void)hipFree(h->split_buf);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->side) (void)hipStreamDestroy(h->side);
   delete h;
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
@@ -591,7 +704,8 @@ INFINI_EXPORT int infini_attn_reset_state(infini_attn_t h, void* hip_stream) {
 static hipError_t materialize_zero_state(infini_attn* h, hipStream_t st) {
   if (!h->state_zero) return hipSuccess;
   const int64_t DD = int64_t(h->D) * h->D;
-  const hipError_t e = zero_f32(h->M, int64_t(h->BH) * (DD + h->D), st);   // M and z
+  hipError_t e = zero_f32(h->M, int64_t(h->BH) * (DD + h->D), st);   // M and z
+  if (e == hipSuccess && h->mt_cur) e = zero_f32(static_cast<float*>(h->mt_cur), int64_t(h->BH) * DD / 2, st);
   if (e == hipSuccess) h->state_zero = false;
   return e;
 }
@@ -616,6 +730,7 @@ INFINI_EXPORT int infini_attn_set_state(infini_attn_t h, const float* M, const f
   hipError_t e = materialize_zero_state(h, st);   // a part not given keeps its (zero) value
   if (e == hipSuccess && M) e = hipMemcpyAsync(h->M, M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
   if (e == hipSuccess && z) e = hipMemcpyAsync(h->z, z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
+  if (e == hipSuccess && M && h->mt_cur) e = infini::launch_state_to_mt(h->M, h->mt_cur, h->BH, h->D, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
@@ -639,7 +754,8 @@ INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
   return int64_t(h->BH) * DD * 4 + int64_t(h->BH) * h->D * 4 + int64_t(2) * h->cfg.heads * 4 +
          static_cast<int64_t>(h->ws_bytes) + static_cast<int64_t>(h->layer_bytes) +
          (h->dec_cache ? int64_t(2) * h->BH * h->N * h->D * (h->bf16 ? 2 : 4) : 0) +
-         static_cast<int64_t>(h->bwd_bytes);
+         static_cast<int64_t>(h->bwd_bytes) + (h->mt_cur ? int64_t(h->BH) * DD * 2 : 0) +
+         static_cast<int64_t>(h->split_bytes);
 }
 
 INFINI_EXPORT int64_t infini_attn_window_tokens(infini_attn_t h) {
@@ -802,6 +918,7 @@ int close_decode_segment(infini_attn* h, int n, hipStream_t st) {
   a.z = h->z;
   a.ws = h->ws;
   a.zero_state = h->state_zero;
+  a.mt_cur = h->mt_cur;
   a.chk = chunks_for(*h, 1);
   a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
   hipError_t e = hipSuccess;
@@ -844,6 +961,7 @@ INFINI_EXPORT int infini_attn_decode_step(infini_attn_t h, const void* q, const 
   a.kc = h->dec_cache;
   a.vc = static_cast<char*>(h->dec_cache) + size_t(h->BH) * h->N * h->D * es;
   a.M = h->M;
+  a.mt = h->mt_cur;
   a.z = h->z;
   a.gate_g = h->gate;
   a.gate_omg = h->gate + h->cfg.heads;
@@ -1016,6 +1134,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
   if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
   if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+  a.zero_state = false;   // the chain has recorded every segment's M^T_{s-1}, z_{s-1}
   if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(a, st); });
   if (e != hipSuccess) return INFINI_ERR_HIP;
 

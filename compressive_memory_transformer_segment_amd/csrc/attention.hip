@@ -79,6 +79,8 @@ struct FastDiv {
 // B x H and H.
 struct Sched {
   FastDiv units, grp, last, bh, h;
+  FastDiv kc;   // split mode: key tiles per chunk
+  int items;    // split mode: items per (batch, head) pair
 };
 
 __device__ __forceinline__ bool item_at(const Sched& sd, int units, int nq, int G, int r, int& u, int& qt) {
@@ -110,12 +112,40 @@ __device__ __forceinline__ bool item_at(const Sched& sd, int units, int nq, int 
   return true;
 }
 
+// Split mode (one segment): item i = k * units + u, where k ranks the pair's items --
+// query tiles from the last one down, and the key chunks of each in order (longest query
+// tiles, whose chunks are all full, first).  Chunk c of query tile qt holds key tiles
+// [c kc, min((c + 1) kc, nkv)).
+__device__ __forceinline__ bool split_item_at(const Sched& sd, int units, int n, int G, int r, int& u, int& qt,
+                                              int& c) {
+  const int b = static_cast<int>(blockIdx.x);
+  const int i = r * G + ((r & 1) ? G - 1 - b : b);
+  if (i >= units * sd.items) return false;
+  int k = sd.units.div(i);
+  u = i - k * units;
+  const int kc = static_cast<int>(sd.kc.d);
+  for (int t = (n + kBMA - 1) / kBMA - 1; t >= 0; --t) {
+    const int nkv = (min(t * kBMA + kBMA, n) + kBN - 1) / kBN;
+    const int nc = sd.kc.div(nkv + kc - 1);
+    if (k < nc) {
+      qt = t;
+      c = k;
+      return true;
+    }
+    k -= nc;
+  }
+  return false;
+}
+
 // MODE: 0 = the gated output; 1 = also A_mem, A_dot (fp32) and the log-sum-exp; 2 = the
 // backward's per-token terms instead of the output: log-sum-exp, D = dO . A_dot, the
 // retrieval denominator, its gradient -g dO . A_mem / den, and the gate term
 // g (1 - g) dO . (A_mem - A_dot) (dO given in bwd_dout).
-template <int D, int MODE>
+// SPLIT: split-key mode (MODE 0 only): an item is one key chunk of a query tile; a query
+// tile split into several chunks is finished by the workgroup whose chunk completes last.
+template <int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(const WindowArgs a, const Sched sd) {
+  static_assert(!SPLIT || MODE == 0, "split-key mode writes the gated output only");
   constexpr int KS = D / 16;                  // k-steps over the head dimension
   constexpr int DB = D / 32;                  // 32-row blocks of the head dimension
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -152,13 +182,26 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   const int l32 = lane & 31, hl = lane >> 5;
 
   // the next item of this workgroup at or after round r whose query tile holds tokens
-  auto find = [&](int& r, int& u_, int& qt_, int& n_) __attribute__((always_inline)) -> bool {
-    while (item_at(sd, units, nq, G, r, u_, qt_)) {
-      n_ = a.seg_tokens(sd.bh.div(u_));
-      if (qt_ * kBMA < n_) return true;
-      ++r;
+  auto find = [&](int& r, int& u_, int& qt_, int& n_, int& c_) __attribute__((always_inline)) -> bool {
+    if constexpr (SPLIT) {
+      n_ = a.seg_tokens(0);
+      return split_item_at(sd, units, n_, G, r, u_, qt_, c_);
+    } else {
+      c_ = 0;
+      while (item_at(sd, units, nq, G, r, u_, qt_)) {
+        n_ = a.seg_tokens(sd.bh.div(u_));
+        if (qt_ * kBMA < n_) return true;
+        ++r;
+      }
+      return false;
     }
-    return false;
+  };
+  const int kc = SPLIT ? static_cast<int>(sd.kc.d) : 0;
+  // key tiles an item loads: [t0, te)
+  auto item_t0 = [&](int c_) __attribute__((always_inline)) -> int { return SPLIT ? c_ * kc : 0; };
+  auto item_te = [&](int qt_, int n_, int c_) __attribute__((always_inline)) -> int {
+    const int nkv_ = (min(qt_ * kBMA + kBMA, n_) + kBN - 1) / kBN;
+    return SPLIT ? min(c_ * kc + kc, nkv_) : nkv_;
   };
   // token row of the segment start of unit u_
   auto seg_row0 = [&](int u_) __attribute__((always_inline)) -> int64_t {
@@ -169,8 +212,8 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     return (min(qt_ * kBMA + kBMA, n_) + kBN - 1) / kBN;
   };
 
-  int r = 0, u, qt, n;
-  if (!find(r, u, qt, n)) return;
+  int r = 0, u, qt, n, c;
+  if (!find(r, u, qt, n, c)) return;
 
   // Q and K of the local attention (position-embedded when the caller supplies them)
   const uint16_t* qloc = static_cast<const uint16_t*>(a.q_loc);
@@ -238,9 +281,12 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   // ---- prologue of the first item: its Q rows straight into the B-operand registers,
   // tiles 0, 1 and 2 into buffers 0, 1 and 2.
   load_q(qloc, seg_row0(u), n, qt * kBMA + 32 * wave);
-  issue_tile(seg_row0(u), n, 0, buf0);
-  if (kBN < n) issue_tile(seg_row0(u), n, 1, buf1);
-  if (2 * kBN < n) issue_tile(seg_row0(u), n, 2, buf2);
+  {
+    const int t0_ = item_t0(c), te_ = item_te(qt, n, c);
+    issue_tile(seg_row0(u), n, t0_, buf0);
+    if (t0_ + 1 < te_) issue_tile(seg_row0(u), n, t0_ + 1, buf1);
+    if (t0_ + 2 < te_) issue_tile(seg_row0(u), n, t0_ + 2, buf2);
+  }
   wait_vm_le(0);
   __builtin_amdgcn_s_barrier();
 
@@ -258,27 +304,36 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     const int jm = q0 / kBN;   // unmasked tiles (a multiple of 4); tiles jm .. jm + 3 hold the diagonal
     const int qw0 = q0 + 32 * wave;
     const int q = qw0 + l32;
-    int rn = r + 1, un = 0, qtn = 0, nn = 0;
-    const bool has_next = find(rn, un, qtn, nn);
+    // The item's steps: unmasked tiles [t0, tu), then, if it holds the diagonal (the
+    // query tile's last chunk), the four diagonal steps jm .. jm + 3; tend ends the step
+    // sequence.  Every bound is a multiple of 4, so buffer j % 4 holds tile j throughout.
+    const int t0 = item_t0(c), te = item_te(qt, n, c);
+    const bool last = !SPLIT || te == nkv;
+    const int tu = last ? jm : te;
+    const int tend = last ? jm + 4 : tu;
+    int rn = r + 1, un = 0, qtn = 0, nn = 0, cn = 0;
+    const bool has_next = find(rn, un, qtn, nn, cn);
     const int64_t row0n = has_next ? seg_row0(un) : 0;
-    const int nkvn = has_next ? kv_tiles(qtn, nn) : 0;
+    const int t0n = has_next ? item_t0(cn) : 0;
+    const int ten = has_next ? item_te(qtn, nn, cn) : 0;
 
-    // Copy number i of the item's sequence: K and V of tile i for i < nkv; tiles 0, 1, 2
-    // of the next item for i = jm + 4 .. jm + 6; nothing otherwise.  count: the copy
-    // instructions this wave issues for it.
+    // Copy number i of the item's sequence: K and V of tile i for i < te; tiles t0n,
+    // t0n + 1, t0n + 2 of the next item for i = tend .. tend + 2; nothing otherwise.
+    // count: the copy instructions this wave issues for it.
     auto issue = [&](int i, uint16_t* dst) __attribute__((always_inline)) {
-      if (i < nkv) issue_tile(row0, n, i, dst);
-      else if (i >= jm + 4 && i - (jm + 4) < nkvn) issue_tile(row0n, nn, i - (jm + 4), dst);
+      if (i < te) issue_tile(row0, n, i, dst);
+      else if (i >= tend && t0n + (i - tend) < ten) issue_tile(row0n, nn, t0n + (i - tend), dst);
     };
     auto count = [&](int i) __attribute__((always_inline)) -> int {
-      return (i < nkv || (i >= jm + 4 && i - (jm + 4) < nkvn)) ? 2 * CW : 0;
+      return (i < te || (i >= tend && t0n + (i - tend) < ten)) ? 2 * CW : 0;
     };
     // M^T_{s-1} into its buffer: issued at the start of the item's second step, when every
     // wave is past the previous item's retrieval
     auto issue_mt = [&]() __attribute__((always_inline)) {
       const uint16_t* msrc = static_cast<const uint16_t*>(a.ws.mt) + static_cast<int64_t>(u) * D * D;
 #pragma unroll
-      for (int t = 0; t < MW; ++t) copy_group(wave * MW + t, msrc, D * D * 2, bufm);
+      // (a state still zero after a reset is read as zeros: an empty source range)
+      for (int t = 0; t < MW; ++t) copy_group(wave * MW + t, msrc, a.zero_state ? 0u : D * D * 2u, bufm);
     };
 
     float m_run = -INFINITY;   // running row maximum, scaled (log2 domain)
@@ -413,7 +468,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     };
     f32x16 sc0, sc1;
     KOps kq;
-    load_k(buf0, 0, kq);
+    load_k(buf0, 0, kq);   // tile t0
     sc0 = zero16();
     sc1 = zero16();
     qk_part(kq, 0, sc0, sc1);
@@ -423,11 +478,11 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     // Tile 2 (issued last in the previous item) is complete here in every wave, ahead of
     // its Q rows in the wave's load order; after the barrier it is visible to all.
     __builtin_amdgcn_s_barrier();
-    if (jm > 0) load_k(buf1, 0, kq);   // tile 1, k-steps 0 .. KH - 1
+    if (tu > t0) load_k(buf1, 0, kq);   // tile t0 + 1, k-steps 0 .. KH - 1
     auto pstep = [&](int j, auto bufc) __attribute__((always_inline)) {
       constexpr int b = decltype(bufc)::value;
       maybe_rescale(mxc);
-      if (j == 1) issue_mt();
+      if (j == t0 + 1) issue_mt();
       issue(j + 3, bufp(IC<b + 3>{}));
       const uint16_t* kt = bufp(bufc);
       f32x16 n0 = zero16(), n1 = zero16();
@@ -484,7 +539,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       wait_vm_le(0);
       __builtin_amdgcn_s_barrier();
     };
-    for (int j = 0; j < jm; j += 4) {
+    for (int j = t0; j < tu; j += 4) {
       pstep(j, IC<0>{});
       pstep(j + 1, IC<1>{});
       pstep(j + 2, IC<2>{});
@@ -499,7 +554,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     auto mstep = [&](int j, auto bufc, bool have_scores) __attribute__((always_inline)) {
       constexpr int b = decltype(bufc)::value;
       const uint16_t* kt = bufp(bufc);
-      if (j == 1) issue_mt();
+      if (j == t0 + 1) issue_mt();
       issue(j + 3, bufp(IC<b + 3>{}));
       const int kv0 = j * kBN;
       if (j < nkv && kv0 <= qw0 + 31) {
@@ -513,14 +568,103 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       else wait_vm_le(count(j + 2) + count(j + 3));
       __builtin_amdgcn_s_barrier();
     };
-    mstep(jm, IC<0>{}, true);
-    mstep(jm + 1, IC<1>{}, false);
-    mstep(jm + 2, IC<2>{}, false);
-    mstep(jm + 3, IC<3>{}, false);
+    if (last) {
+      mstep(jm, IC<0>{}, true);
+      mstep(jm + 1, IC<1>{}, false);
+      mstep(jm + 2, IC<2>{}, false);
+      mstep(jm + 3, IC<3>{}, false);
+    }
+    // (A chunk without the diagonal has computed scores of the next item's first tile in
+    // its last step: they are not used.)
 
     // ---------------------------------------------------------------- epilogue
-    // M^T_{s-1} is in bufm.  The next item's tiles 0 .. 2 are in buffers 0 .. 2; this
+    // M^T_{s-1} is in bufm.  The next item's first tiles are in buffers 0 .. 2; this
     // item's Q registers are free once sigma(Q) is formed, and take the next item's Q.
+    bool finish = true;
+    if constexpr (SPLIT) {
+      const int nchunks = sd.kc.div(nkv + kc - 1);
+      if (nchunks > 1) {
+        // Hand the partial softmax state (O^T unnormalised, running maximum, row sum) to
+        // the query tile's slot c with device-coherent stores; once every wave's stores
+        // have completed, count the chunk.  The workgroup that counts the last chunk merges
+        // all of them in chunk order (the same arithmetic whichever workgroup it is) and
+        // finishes the tile; the others go on to their next item.  Nothing waits.
+        const int tile = u * nq + qt;
+        int base = 0;   // chunks of the query tiles before qt in a full segment
+        for (int t = 0; t < qt; ++t) base += sd.kc.div((min(t * kBMA + kBMA, a.N) + kBN - 1) / kBN + kc - 1);
+        const int64_t slot0 = static_cast<int64_t>(u) * a.split_slots + base;
+        constexpr uint32_t kAccBytes = 256u * D * 4u, kMlBytes = 512u * 8u;
+        auto acc_rsrc = [&](int ch) __attribute__((always_inline)) {
+          return buffer_rsrc(a.split_acc + (slot0 + ch) * (256 * D), kAccBytes);
+        };
+        auto ml_rsrc = [&](int ch) __attribute__((always_inline)) {
+          return buffer_rsrc(a.split_ml + (slot0 + ch) * 1024, kMlBytes);
+        };
+        auto acc_off = [&](int db, int r4) __attribute__((always_inline)) -> uint32_t {
+          return static_cast<uint32_t>(((wave * 4 * DB + 4 * db + r4) * 64 + lane) * 16);
+        };
+        {
+          const auto ar = acc_rsrc(c);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              buffer_st16_dev(ar, acc_off(db, r4),
+                              u32x4{__float_as_uint(acc_o[db][4 * r4]), __float_as_uint(acc_o[db][4 * r4 + 1]),
+                                    __float_as_uint(acc_o[db][4 * r4 + 2]), __float_as_uint(acc_o[db][4 * r4 + 3])});
+          buffer_st8_dev(ml_rsrc(c), static_cast<uint32_t>((wave * 64 + lane) * 8),
+                         u32x2{__float_as_uint(m_run), __float_as_uint(l_part)});
+        }
+        wait_vm_le(0);
+        __builtin_amdgcn_s_barrier();
+        // buffer 3 is free here (its last tile is consumed; the next item's copy into it
+        // is issued after the next item's first barrier): it carries the count to all waves
+        int* flag = reinterpret_cast<int*>(buf3);
+        if (tid == 0)
+          flag[0] = __hip_atomic_fetch_add(a.split_cnt + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int done = __builtin_amdgcn_readfirstlane(flag[0]);
+        finish = done == nchunks - 1;
+        if (!finish) {
+          if (has_next) load_q(qloc, row0n, nn, qtn * kBMA + 32 * wave);
+        } else {
+          if (tid == 0) __hip_atomic_store(a.split_cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          float mc[4], lc[4];
+          float m_all = -INFINITY;
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) {
+            if (ch < nchunks) {
+              const u32x2 ml = buffer_ld8_dev(ml_rsrc(ch), static_cast<uint32_t>((wave * 64 + lane) * 8));
+              mc[ch] = __uint_as_float(ml[0]);
+              lc[ch] = __uint_as_float(ml[1]);
+              m_all = fmaxf(m_all, mc[ch]);
+            }
+          }
+          float lsum = 0.f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc_o[db] = zero16();
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) {
+            if (ch < nchunks) {
+              const float f = __builtin_amdgcn_exp2f(mc[ch] - m_all);
+              lsum = fmaf(f, lc[ch], lsum);
+              const auto ar = acc_rsrc(ch);
+#pragma unroll
+              for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                  const u32x4 v = buffer_ld16_dev(ar, acc_off(db, r4));
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc_o[db][4 * r4 + e] = fmaf(f, __uint_as_float(v[e]), acc_o[db][4 * r4 + e]);
+                }
+            }
+          }
+          l_part = lsum;
+          m_run = m_all;
+        }
+      }
+    }
+    if (finish) {
     const float l_tot = sum_across_halves(l_part);
     const float inv_l = 1.f / l_tot;
     if constexpr (MODE >= 1) {
@@ -532,8 +676,8 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       const f32x4* zq = reinterpret_cast<const f32x4*>(a.ws.zb + static_cast<int64_t>(u) * D);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        zr[ks][0] = zq[4 * ks + 2 * hl];
-        zr[ks][1] = zq[4 * ks + 2 * hl + 1];
+        zr[ks][0] = a.zero_state ? f32x4{0.f, 0.f, 0.f, 0.f} : zq[4 * ks + 2 * hl];
+        zr[ks][1] = a.zero_state ? f32x4{0.f, 0.f, 0.f, 0.f} : zq[4 * ks + 2 * hl + 1];
       }
     }
     // With a separate local Q the retrieval reads the PE-free Q rows.
@@ -634,11 +778,13 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
         a.bwd_bq[rq] = (emp - ddp) * g * omg;
       }
     }
+    }   // finish
     if (!has_next) break;
     r = rn;
     u = un;
     qt = qtn;
     n = nn;
+    c = cn;
   }
 }
 
@@ -768,9 +914,22 @@ hipError_t launch_attention_d(const WindowArgs& a, hipStream_t st) {
     sd.last = FastDiv(static_cast<uint32_t>((units / 8) % kGroup));
     sd.bh = FastDiv(static_cast<uint32_t>(a.B * a.H));
     sd.h = FastDiv(static_cast<uint32_t>(a.H));
-    if (a.bwd_dout) hipLaunchKernelGGL((k_attn_bf16<D, 2>), grid, dim3(kThreadsA), 0, st, a, sd);
-    else if (a.a_mem || a.a_dot || a.lse) hipLaunchKernelGGL((k_attn_bf16<D, 1>), grid, dim3(kThreadsA), 0, st, a, sd);
-    else hipLaunchKernelGGL((k_attn_bf16<D, 0>), grid, dim3(kThreadsA), 0, st, a, sd);
+    if (a.split_kc > 0) {
+      // split-key mode: one segment, MODE 0, items counted by the host
+      if (a.W != 1 || a.bwd_dout || a.a_mem || a.a_dot || a.lse || a.split_kc % 4 != 0 || a.split_items < 1 ||
+          a.split_slots < a.split_items || !a.split_acc || !a.split_ml || !a.split_cnt)
+        return hipErrorInvalidValue;
+      sd.kc = FastDiv(static_cast<uint32_t>(a.split_kc));
+      sd.items = a.split_items;
+      const dim3 sgrid(min(units * a.split_items, compute_units()));
+      hipLaunchKernelGGL((k_attn_bf16<D, 0, true>), sgrid, dim3(kThreadsA), 0, st, a, sd);
+    } else if (a.bwd_dout) {
+      hipLaunchKernelGGL((k_attn_bf16<D, 2, false>), grid, dim3(kThreadsA), 0, st, a, sd);
+    } else if (a.a_mem || a.a_dot || a.lse) {
+      hipLaunchKernelGGL((k_attn_bf16<D, 1, false>), grid, dim3(kThreadsA), 0, st, a, sd);
+    } else {
+      hipLaunchKernelGGL((k_attn_bf16<D, 0, false>), grid, dim3(kThreadsA), 0, st, a, sd);
+    }
   } else {
     const dim3 grid(a.units() * ((a.N + 63) / 64));
     hipLaunchKernelGGL((k_attn_f32<D>), grid, dim3(64 * (D / 32)), 0, st, a);

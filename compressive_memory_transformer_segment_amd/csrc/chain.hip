@@ -20,11 +20,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D, int EPT, int CHK, bool BF16>
+// Linear rule.  A workgroup owns 16 rows of M^T (value features rb .. rb + 15) of one
+// (b,h); thread (r, cg) owns row rb + r, columns EPT cg .. EPT cg + EPT - 1 (EPT = D / 16),
+// so a wave reads four whole rows of every U^T partial.  M ([d_key][d_value]) is read
+// and written once per window through an LDS transpose, with 16-byte accesses that cover
+// the workgroup's 64-byte pieces of M's rows.
+template <int D, int CHK, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
-  constexpr int CG = D / EPT;             // thread columns per row
-  constexpr int RB = kThreads / CG;       // rows of M^T per workgroup
-  constexpr int kBatch = 8;               // segments whose partials are loaded together
+  constexpr int RB = 16;                  // rows of M^T per workgroup
+  constexpr int EPT = D / 16;             // elements per thread
+  constexpr int CG = D / EPT;             // thread columns per row (16)
+  constexpr int kBatch = CHK >= 2 ? 16 / CHK : 8;    // segments whose partials are loaded together
+  static_assert(RB * CG == kThreads, "one thread per (row, column group)");
+  __shared__ float tr[D][RB + 1];         // M[i][rb + c] at tr[i][c]
   const int BH = a.B * a.H;
   const int bh = blockIdx.x / (D / RB);
   const int rb = (blockIdx.x % (D / RB)) * RB;
@@ -33,16 +41,31 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
   const int dv = rb + r;
   const int i0 = cg * EPT;
   const int64_t DD = static_cast<int64_t>(D) * D;
+  float* Mb = a.M + bh * DD + rb;
 
   float m[EPT];
+  if (a.zero_state) {
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) m[e] = a.zero_state ? 0.f : a.M[bh * DD + static_cast<int64_t>(i0 + e) * D + dv];
+    for (int e = 0; e < EPT; ++e) m[e] = 0.f;
+  } else {
+    // thread t: row t / 4 (+ 64 k) of M, columns rb + 4 (t % 4) .. +3
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int i = tid / 4 + 64 * k;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(Mb + static_cast<int64_t>(i) * D + 4 * (tid % 4));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tr[i][4 * (tid % 4) + c] = v[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) m[e] = tr[i0 + e][r];
+  }
   const bool zown = rb == 0 && tid < D;
   float z = zown && !a.zero_state ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
 
   for (int s0 = 0; s0 < a.W; s0 += kBatch) {
     // all chunk partials of the batch are independent of the chain: issue them together
-    float ut[kBatch][CHK][EPT];
+    f32x4 ut[kBatch][CHK][EPT / 4];
     float dzv[kBatch][CHK];
 #pragma unroll
     for (int sb = 0; sb < kBatch; ++sb) {
@@ -52,14 +75,8 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
       for (int c = 0; c < CHK; ++c) {
         const int64_t slot = u * CHK + c;
         const float* src = a.ws.u + slot * DD + static_cast<int64_t>(dv) * D + i0;
-        if constexpr (EPT == 2) {
-          const f32x2 v = *reinterpret_cast<const f32x2*>(src);
-          ut[sb][c][0] = v[0];
-          ut[sb][c][1] = v[1];
-        } else {
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) ut[sb][c][e] = src[e];
-        }
+        for (int q = 0; q < EPT / 4; ++q) ut[sb][c][q] = *reinterpret_cast<const f32x4*>(src + 4 * q);
         // every thread loads (threads past D re-read the first D; only owners use them):
         // a load under the owner test made the compiler wait for each one before the next
         dzv[sb][c] = a.ws.dz[slot * D + (tid & (D - 1))];
@@ -73,16 +90,18 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
       const int64_t off = u * DD + static_cast<int64_t>(dv) * D + i0;
       if constexpr (BF16) {
         uint16_t* mt = static_cast<uint16_t*>(a.ws.mt) + off;
-        if constexpr (EPT == 2) {
-          *reinterpret_cast<uint32_t*>(mt) = pack_bf16x2(m[0], m[1]);
-        } else {
+        uint32_t pk[EPT / 2];
 #pragma unroll
-          for (int e = 0; e < EPT; ++e) mt[e] = f32_to_bf16(m[e]);
+        for (int e = 0; e < EPT / 2; ++e) pk[e] = pack_bf16x2(m[2 * e], m[2 * e + 1]);
+        if constexpr (EPT == 8) {
+          st16(mt, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        } else {
+          st8(mt, u32x2{pk[0], pk[1]});
         }
       } else {
         float* mt = static_cast<float*>(a.ws.mt) + off;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) mt[e] = m[e];
+        for (int q = 0; q < EPT / 4; ++q) *reinterpret_cast<f32x4*>(mt + 4 * q) = f32x4{m[4 * q], m[4 * q + 1], m[4 * q + 2], m[4 * q + 3]};
       }
       if (zown) {
         a.ws.zb[u * D + tid] = z;
@@ -95,14 +114,35 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
       for (int e = 0; e < EPT; ++e) {
         float add = 0.f;
 #pragma unroll
-        for (int c = 0; c < CHK; ++c) add += ut[sb][c][e];
+        for (int c = 0; c < CHK; ++c) add += ut[sb][c][e / 4][e % 4];
         m[e] += add;
       }
     }
   }
+  if (BF16 && a.mt_cur) {   // the final state as the retrieval operand of the next call
+    uint16_t* mc = static_cast<uint16_t*>(a.mt_cur) + bh * DD + static_cast<int64_t>(dv) * D + i0;
+    uint32_t pk[EPT / 2];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) a.M[bh * DD + static_cast<int64_t>(i0 + e) * D + dv] = m[e];
+    for (int e = 0; e < EPT / 2; ++e) pk[e] = pack_bf16x2(m[2 * e], m[2 * e + 1]);
+    if constexpr (EPT == 8) {
+      st16(mc, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    } else {
+      st8(mc, u32x2{pk[0], pk[1]});
+    }
+  }
   if (zown) a.z[static_cast<int64_t>(bh) * D + tid] = z;
+  __syncthreads();   // every thread is past its reads of tr
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) tr[i0 + e][r] = m[e];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) {
+    const int i = tid / 4 + 64 * k;
+    f32x4 v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = tr[i][4 * (tid % 4) + c];
+    *reinterpret_cast<f32x4*>(Mb + static_cast<int64_t>(i) * D + 4 * (tid % 4)) = v;
+  }
 }
 
 // Delta rule, G_s summed over the chunks beforehand (k_gsum).  A workgroup owns four
@@ -130,8 +170,15 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
   const int row = rb + r;                 // this thread's row of M^T
   const int64_t DD = static_cast<int64_t>(D) * D;
 
-  // M^T[row][i] = M[i][row]
-  float m = a.zero_state ? 0.f : a.M[bh * DD + static_cast<int64_t>(i) * D + row];
+  // M^T[row][i] = M[i][row]: the workgroup's 4 columns of M through LDS (4 lanes read one
+  // row's 16 bytes)
+  float* Mb = a.M + bh * DD + rb;
+  float m = 0.f;
+  if (!a.zero_state) {
+    m_lds[0][tid % 4][tid / 4] = Mb[static_cast<int64_t>(tid / 4) * D + tid % 4];
+    __syncthreads();
+    m = m_lds[0][r][i];
+  }
   const bool zown = rb == 0 && tid < D;
   float z = zown && !a.zero_state ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
 
@@ -215,8 +262,31 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
       }
     }
   }
-  a.M[bh * DD + static_cast<int64_t>(i) * D + row] = m;
   if (zown) a.z[static_cast<int64_t>(bh) * D + tid] = z;
+  if (BF16 && a.mt_cur)   // the final state as the retrieval operand of the next call
+    static_cast<uint16_t*>(a.mt_cur)[bh * DD + static_cast<int64_t>(row) * D + i] = f32_to_bf16(m);
+  __syncthreads();   // every thread is past the last step's reads of m_lds
+  m_lds[0][r][i] = m;
+  __syncthreads();
+  Mb[static_cast<int64_t>(tid / 4) * D + tid % 4] = m_lds[0][tid % 4][tid / 4];
+}
+
+// M [pairs][D][D] (fp32, [d_key][d_value]) -> M^T in bf16 ([d_value][d_key]), through a
+// 32 x 32 LDS tile: the retrieval operand of a state set from outside.
+template <int D>
+__global__ __launch_bounds__(256) void k_state_to_mt(const float* __restrict__ M, uint16_t* __restrict__ mt) {
+  __shared__ float tile[32][33];
+  constexpr int TB = D / 32;
+  const int64_t pair = blockIdx.x / (TB * TB);
+  const int tb = blockIdx.x % (TB * TB), ti = (tb / TB) * 32, tj = (tb % TB) * 32;   // rows of M, columns of M
+  const float* src = M + pair * D * D;
+  uint16_t* dst = mt + pair * D * D;
+  const int x = threadIdx.x % 32, y = threadIdx.x / 32;
+#pragma unroll
+  for (int r = y; r < 32; r += 8) tile[r][x] = src[static_cast<int64_t>(ti + r) * D + tj + x];
+  __syncthreads();
+#pragma unroll
+  for (int r = y; r < 32; r += 8) dst[static_cast<int64_t>(tj + r) * D + ti + x] = f32_to_bf16(tile[x][r]);
 }
 
 // G_s = sum of its chunk partials, in chunk order (the order the state pass's partials were
@@ -251,14 +321,12 @@ hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
     else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_delta<D, 4, true>), grid, block, 0, st, a, gsum);
     else hipLaunchKernelGGL((k_chain_delta<D, 8, true>), grid, block, 0, st, a, gsum);
   } else {
-    constexpr int EPT = 2;
-    constexpr int RB = kThreads / (D / EPT);
-    const dim3 grid(BH * (D / RB));
-    if (!a.bf16) hipLaunchKernelGGL((k_chain_linear<D, EPT, 1, false>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_linear<D, EPT, 1, true>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_linear<D, EPT, 2, true>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_linear<D, EPT, 4, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_chain_linear<D, EPT, 8, true>), grid, dim3(kThreads), 0, st, a);
+    const dim3 grid(BH * (D / 16));
+    if (!a.bf16) hipLaunchKernelGGL((k_chain_linear<D, 1, false>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_linear<D, 1, true>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_linear<D, 2, true>), grid, dim3(kThreads), 0, st, a);
+    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_linear<D, 4, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((k_chain_linear<D, 8, true>), grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -267,6 +335,15 @@ hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
 
 hipError_t launch_chain(const WindowArgs& a, hipStream_t st) {
   return a.D == 128 ? launch_chain_d<128>(a, st) : launch_chain_d<64>(a, st);
+}
+
+hipError_t launch_state_to_mt(const float* M, void* mt, int pairs, int D, hipStream_t st) {
+  const int tb = (D / 32) * (D / 32);
+  if (D == 128)
+    hipLaunchKernelGGL((k_state_to_mt<128>), dim3(pairs * tb), dim3(256), 0, st, M, static_cast<uint16_t*>(mt));
+  else
+    hipLaunchKernelGGL((k_state_to_mt<64>), dim3(pairs * tb), dim3(256), 0, st, M, static_cast<uint16_t*>(mt));
+  return hipGetLastError();
 }
 
 }  // namespace infini

@@ -128,6 +128,22 @@ __device__ __forceinline__ u32x2 buffer_ld8(__amdgpu_buffer_rsrc_t r, uint32_t v
 __device__ __forceinline__ void buffer_st16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voffset), 0, 0);
 }
+// Device-coherent forms (cache policy SC1: the access is performed at device scope, so a
+// store is visible to every XCD once it has completed, and a load does not return a line
+// another XCD's L2 may hold stale).  For data one workgroup hands to another inside a launch.
+constexpr int kCpolDevice = 16;
+__device__ __forceinline__ void buffer_st16_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voffset), 0, kCpolDevice);
+}
+__device__ __forceinline__ u32x4 buffer_ld16_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voffset), 0, kCpolDevice));
+}
+__device__ __forceinline__ void buffer_st8_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(voffset), 0, kCpolDevice);
+}
+__device__ __forceinline__ u32x2 buffer_ld8_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voffset), 0, kCpolDevice));
+}
 
 // Buffer -> LDS copy of 16 bytes per lane (gfx950): lane i's bytes land at lds_base + 16 i
 // (lds_base wave-uniform); offsets past the resource end write zeros.

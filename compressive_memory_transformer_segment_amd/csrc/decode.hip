@@ -18,8 +18,10 @@
 // state (exp2 domain, scale folded into q) over a strided subset of the keys, and the
 // partial states are merged through LDS.  The key loop is double-buffered: the raw loads of
 // the next batch of rounds (8 keys per lane group for bf16) are in flight while a batch is
-// consumed, and the first batch is issued before the retrieval, which reads the fp32
-// M_{s-1} row by row with 16-byte loads.
+// consumed, and the first batch is issued before the retrieval.  The retrieval reads, with
+// bf16 inputs, the bf16 M_{s-1}^T that the forward pass's retrieval uses (the chain keeps it
+// next to the fp32 state; one row of 2d bytes per value feature, split over 256 / d
+// threads), and with f32 inputs the fp32 M_{s-1} row by row with 16-byte loads.
 #include <type_traits>
 
 #include "common.hpp"
@@ -147,20 +149,40 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     sq[tid] = elu_plus_one(qf);
   }
 
-  // ---- retrieval partial sums: thread (slice, column quad) over D / RS rows of M_{s-1}
+  // ---- retrieval partial sums
+  //  f32: thread (slice, column quad) over D / RS rows of M_{s-1}
+  //  bf16: thread (slice, value feature dv) over D / NS entries of row dv of M_{s-1}^T
+  constexpr int NS = kDecThreads / D;   // bf16: slices
   const int cq = tid % (D / 4), slice = tid / (D / 4);
   constexpr int RPS = D / RS;   // rows per slice
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float numt = 0.f;
   __syncthreads();   // sq
   if (!a.zero_state) {
-    const float* Mb = a.M + static_cast<int64_t>(bh) * D * D + 4 * cq;
-#pragma unroll 8
-    for (int r = 0; r < RPS; ++r) {
-      const int i = slice * RPS + r;
-      const u32x4 w = ld16(Mb + static_cast<int64_t>(i) * D);
-      const float s = sq[i];
+    if constexpr (BF16) {
+      const int dv = tid % D, sl = tid / D;
+      const uint16_t* row = static_cast<const uint16_t*>(a.mt) + (static_cast<int64_t>(bh) * D + dv) * D + sl * (D / NS);
+      u32x4 w[D / NS / 8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) num[c] = fmaf(s, __uint_as_float(w[c]), num[c]);
+      for (int j = 0; j < D / NS / 8; ++j) w[j] = ld16(row + 8 * j);
+#pragma unroll
+      for (int j = 0; j < D / NS / 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = sl * (D / NS) + 8 * j + 2 * e;
+          numt = fmaf(sq[i], bf16lo_to_f32(w[j][e]), numt);
+          numt = fmaf(sq[i + 1], bf16hi_to_f32(w[j][e]), numt);
+        }
+    } else {
+      const float* Mb = a.M + static_cast<int64_t>(bh) * D * D + 4 * cq;
+#pragma unroll 8
+      for (int r = 0; r < RPS; ++r) {
+        const int i = slice * RPS + r;
+        const u32x4 w = ld16(Mb + static_cast<int64_t>(i) * D);
+        const float s = sq[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) num[c] = fmaf(s, __uint_as_float(w[c]), num[c]);
+      }
     }
     if (wave == 0) {   // sigma(q) . z_{s-1}
       float zs = 0.f;
@@ -172,8 +194,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   } else if (tid == 0) {
     zden[0] = 0.f;
   }
+  if constexpr (BF16) {
+    red[tid / D][tid % D] = numt;
+  } else {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) red[slice][4 * cq + c] = num[c];
+    for (int c = 0; c < 4; ++c) red[slice][4 * cq + c] = num[c];
+  }
 
   // ---- local attention over keys 0 .. p (key p is this token, from the inputs)
   float qv[8];
@@ -235,7 +261,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     const float a_dot = nd / dd;
     float nm = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < RS; ++sl) nm += red[sl][tid];
+    for (int sl = 0; sl < (BF16 ? NS : RS); ++sl) nm += red[sl][tid];
     const float a_mem = nm / (zden[0] + a.eps);
     const float o = a.gate_g[h] * a_mem + a.gate_omg[h] * a_dot;
     T* og = static_cast<T*>(a.out) + static_cast<int64_t>(bh) * D;

@@ -54,6 +54,19 @@ struct WindowArgs {
   const float* gate_omg;  // [H] 1 - sigmoid(beta)
   float* M;          // state [B,H,D,D]
   float* z;          // state [B,H,D]
+  void* mt_cur;      // optional [B,H,D,D] bf16: the chain writes M^T of the window's final state here
+  // Split-key mode of the bf16 attention (one segment, few (batch, head) pairs): the keys
+  // of a query tile are split into chunks of split_kc tiles processed by different
+  // workgroups; each writes its partial softmax state, and the last to finish merges them
+  // (in chunk order) and runs the retrieval, gate and store.  split_kc = 0: off.
+  int split_kc;
+  int split_items;   // items per (batch, head) pair (this segment)
+  int split_slots;   // partial slots per (batch, head) pair: the items of a full segment;
+                     // chunk c of query tile qt of pair u uses slot
+                     // u * split_slots + (chunks of the query tiles before qt in a full segment) + c
+  float* split_acc;  // [slots][D * 256] partial O^T per slot
+  float* split_ml;   // [slots][512][2] partial row maximum and row sum per lane
+  int* split_cnt;    // [pairs * tiles] chunks finished per query tile (back to 0 after the merge)
   Workspace ws;
 
   __host__ __device__ int units() const { return W * B * H; }
@@ -89,7 +102,8 @@ struct DecodeArgs {
   void* out;              // [B, H, D]
   void* kc;               // [B, H, N, D] the segment's cached keys; this token goes to row p
   void* vc;
-  const float* M;         // [B, H, D, D] M_{s-1}
+  const float* M;         // [B, H, D, D] M_{s-1} (f32 path)
+  const void* mt;         // [B, H, D, D] M_{s-1}^T in bf16 (bf16 path: the forward's retrieval operand)
   const float* z;         // [B, H, D]    z_{s-1}
   const float* gate_g;    // [H]
   const float* gate_omg;  // [H]
@@ -144,6 +158,7 @@ hipError_t launch_bwd_r_mfma(const BackwardArgs& b, hipStream_t st);        // b
 hipError_t launch_key_sums(const WindowArgs& a, hipStream_t st);       // delta only
 hipError_t launch_state_pass(const WindowArgs& a, hipStream_t st);     // U (+G), dz (linear), V^T
 hipError_t launch_chain(const WindowArgs& a, hipStream_t st);          // M/z recurrence
+hipError_t launch_state_to_mt(const float* M, void* mt, int pairs, int D, hipStream_t st);   // M -> bf16 M^T
 hipError_t launch_attention(const WindowArgs& a, hipStream_t st);      // local attn + retrieval + gate
 
 }  // namespace infini
