@@ -46,21 +46,26 @@ struct infini_attn {
   size_t bwd_bytes = 0;
   void* dec_cache = nullptr;   // decoding: K then V cache of the open segment, [B,H,N,D] each
   int dec_p = 0;               // tokens of the open decode segment (0: none open)
-  // bf16 handles: M^T of the carried state in bf16 ([B,H,d_value,d_key]), the retrieval
-  // operand of one-segment calls and of decoding; written by every chain launch (and by
-  // set_state), zero while state_zero is set
-  void* mt_cur = nullptr;
+  // bf16 handles: copies of the carried state for the kernels that read it while a chain
+  // may be writing the next one -- M^T in bf16 ([B,H,d_value,d_key], the retrieval operand
+  // of one-segment calls and of decoding) and z -- in two buffers: buffer `cur` holds the
+  // current state; every chain launch writes the other one and flips `cur` (set_state
+  // rebuilds the current one; while state_zero is set the kernels read zeros instead)
+  void* mt_buf = nullptr;      // [2][B,H,D,D] bf16
+  float* zc_buf = nullptr;     // [2][B,H,D]
+  int cur = 0;
   // one-segment calls with few (batch, head) pairs: split-key attention partials and counts,
   // and a second stream on which the memory-update kernels run next to the attention
   void* split_buf = nullptr;
   size_t split_bytes = 0;
-  float* split_acc = nullptr;
+  void* split_acc = nullptr;
   float* split_ml = nullptr;
   int* split_cnt = nullptr;
   int split_kc = 0;            // key tiles per chunk
   int split_slots = 0;         // partial slots per (batch, head) pair
   hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_sp = nullptr, ev_chain = nullptr;
+  bool side_pending = false;   // a chain on the side stream may still run (see join_side)
   infini::Workspace ws;
   // per-kernel event timing (measurement only)
   bool profiling = false;
@@ -307,6 +312,29 @@ hipError_t timed(infini_attn* h, int kind, hipStream_t st, F&& launch) {
   return e;
 }
 
+void* mt_of(const infini_attn* h, int i) {
+  return h->mt_buf ? static_cast<char*>(h->mt_buf) + size_t(i) * h->BH * h->D * h->D * 2 : nullptr;
+}
+float* zc_of(const infini_attn* h, int i) {
+  return h->zc_buf ? h->zc_buf + size_t(i) * h->BH * h->D : nullptr;
+}
+
+// Where the chain of the launch being set up writes its copies of the final state; the
+// caller flips h->cur once the chain is enqueued.
+void chain_outputs(const infini_attn* h, infini::WindowArgs& a) {
+  a.mt_cur = mt_of(h, h->cur ^ 1);
+  a.z_cur = zc_of(h, h->cur ^ 1);
+}
+
+// Orders stream st after a chain that a one-segment call left running on the side stream
+// (every call that reads or writes the state, the workspace or the copies does this first).
+hipError_t join_side(infini_attn* h, hipStream_t st) {
+  if (!h->side_pending) return hipSuccess;
+  const hipError_t e = hipStreamWaitEvent(st, h->ev_chain, 0);
+  if (e == hipSuccess) h->side_pending = false;
+  return e;
+}
+
 int device_compute_units(int device) {
   int c = 0;
   if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || c <= 0) {
@@ -384,37 +412,45 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
   a.z = h->z;
   a.ws = plan.ws;
   a.zero_state = h->state_zero;
-  a.mt_cur = h->mt_cur;
+  if (join_side(h, st) != hipSuccess) return INFINI_ERR_HIP;
   if (h->split_buf && !plan_in && a.S == 1 && !a_mem && !a_dot) {
     // One segment with few (batch, head) pairs.  The attention reads the carried state
-    // (its bf16 M^T and z) and does not depend on this segment's memory update, so the
-    // update kernels run on the second stream meanwhile; the chain, which writes the new
-    // state, runs after both.  The attention splits the keys of a query tile over several
-    // workgroups, so that the few pairs fill the compute units.
+    // (the current bf16 M^T and z copies) and does not depend on this segment's memory
+    // update, so the update kernels -- state pass, then the chain, which writes the new
+    // state and its copies into the other buffer -- run on the second stream meanwhile.
+    // The launch stream waits for the state pass (the last reader of the caller's K, V)
+    // before the call's work on it ends; the chain, which touches library memory only, is
+    // joined by the next call that needs the state.  The attention splits the keys of a
+    // query tile over several workgroups, so that the few pairs fill the compute units.
     a.s0 = 0;
     a.W = 1;
     a.chk = chunks_for(*h, 1, plan.part_cap);
     a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
-    hipError_t e = hipEventRecord(h->ev_fork, st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
-    if (e == hipSuccess && h->delta) e = timed(h, 0, h->side, [&] { return infini::launch_key_sums(a, h->side); });
-    if (e == hipSuccess) e = timed(h, 1, h->side, [&] { return infini::launch_state_pass(a, h->side); });
-    if (e == hipSuccess) e = hipEventRecord(h->ev_join, h->side);
+    chain_outputs(h, a);
     infini::WindowArgs at = a;
-    at.ws.mt = h->mt_cur;
-    at.ws.zb = h->z;
+    at.ws.mt = mt_of(h, h->cur);
+    at.ws.zb = zc_of(h, h->cur);
     at.split_kc = h->split_kc;
     at.split_items = split_items(a.n_last, h->split_kc);
     at.split_slots = h->split_slots;
     at.split_acc = h->split_acc;
     at.split_ml = h->split_ml;
     at.split_cnt = h->split_cnt;
+    hipError_t e = hipEventRecord(h->ev_fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
+    if (e == hipSuccess && h->delta) e = timed(h, 0, h->side, [&] { return infini::launch_key_sums(a, h->side); });
+    if (e == hipSuccess) e = timed(h, 1, h->side, [&] { return infini::launch_state_pass(a, h->side); });
+    if (e == hipSuccess) e = hipEventRecord(h->ev_sp, h->side);
+    if (e == hipSuccess) e = timed(h, 2, h->side, [&] { return infini::launch_chain(a, h->side); });
+    if (e == hipSuccess) e = hipEventRecord(h->ev_chain, h->side);
+    if (e == hipSuccess) {
+      h->side_pending = true;
+      h->cur ^= 1;
+      h->state_zero = false;
+    }
     if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(at, st); });
-    if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_join, 0);
-    if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
-    if (e != hipSuccess) return INFINI_ERR_HIP;
-    h->state_zero = false;
-    return INFINI_OK;
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_sp, 0);
+    return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
   }
   for (int s0 = 0; s0 < a.S; s0 += plan.window) {
     a.s0 = s0;
@@ -424,8 +460,10 @@ int run_stream(infini_attn* h, const void* q, const void* k, const void* v, void
     hipError_t e = hipSuccess;
     if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
     if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
+    chain_outputs(h, a);
     if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
     if (e == hipSuccess) {   // the chain has written the carried state
+      h->cur ^= 1;
       h->state_zero = false;
       a.zero_state = false;
     }
@@ -571,24 +609,32 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   h->ws_bytes = carve(*h, h->window, h->part_cap, h->ws_base, h->ws);
   (void)scratch_resolve(h->device);   // for forward_stream_noalloc; checked again there
   if (h->bf16) {
-    const size_t mt_bytes = size_t(h->BH) * DD * 2;
-    bool ok = hipMalloc(&h->mt_cur, mt_bytes) == hipSuccess;
+    const size_t mt_bytes = 2 * size_t(h->BH) * DD * 2;
+    bool ok = hipMalloc(&h->mt_buf, mt_bytes) == hipSuccess &&
+              hipMalloc(reinterpret_cast<void**>(&h->zc_buf), 2 * size_t(h->BH) * h->D * 4) == hipSuccess;
     // split-key attention for one-segment calls when the pairs' query tiles fill at most
-    // the compute units: at most 4 chunks per query tile
+    // the compute units: chunks of kc key tiles (a multiple of 4, default 8), at most 8 per
+    // query tile; INFINI_ATTN_SPLIT_KC overrides kc (tuning)
     const int nq = (h->N + kQueryTile - 1) / kQueryTile;
     if (ok && int64_t(h->BH) * nq <= device_compute_units(h->device)) {
-      h->split_kc = std::max(8, (nq + 3) / 4 * 4);
+      int kc = 8;
+      if (const char* env = std::getenv("INFINI_ATTN_SPLIT_KC")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v >= 4 && v % 4 == 0 && v <= 4096) kc = static_cast<int>(v);
+      }
+      h->split_kc = std::max(kc, (nq + 7) / 8 * 4);   // 4 nq key tiles in at most 8 chunks
       h->split_slots = split_items(h->N, h->split_kc);
       const size_t slots = size_t(h->BH) * h->split_slots;
-      const size_t acc_b = align_up(slots * 256 * h->D * 4, 256), ml_b = align_up(slots * 1024 * 4, 256);
+      const size_t acc_b = align_up(slots * 512 * h->D, 256), ml_b = align_up(slots * 1024 * 4, 256);
       const size_t cnt_b = align_up(size_t(h->BH) * nq * 4, 256);
       h->split_bytes = acc_b + ml_b + cnt_b;
       ok = hipMalloc(&h->split_buf, h->split_bytes) == hipSuccess &&
            hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) == hipSuccess &&
            hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) == hipSuccess;
+           hipEventCreateWithFlags(&h->ev_sp, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&h->ev_chain, hipEventDisableTiming) == hipSuccess;
       if (ok) {
-        h->split_acc = static_cast<float*>(h->split_buf);
+        h->split_acc = h->split_buf;
         h->split_ml = reinterpret_cast<float*>(static_cast<char*>(h->split_buf) + acc_b);
         h->split_cnt = reinterpret_cast<int*>(static_cast<char*>(h->split_buf) + acc_b + ml_b);
       }
@@ -614,7 +660,8 @@ INFINI_EXPORT int infini_attn_create(const infini_attn_config_t* cfg, const floa
   hipError_t e = hipMemcpy(h->gate, gv, size_t(2) * c.heads * 4, hipMemcpyHostToDevice);
   delete[] gv;
   if (e == hipSuccess) e = hipMemsetAsync(h->M, 0, m_bytes + z_bytes, st);
-  if (e == hipSuccess && h->mt_cur) e = hipMemsetAsync(h->mt_cur, 0, size_t(h->BH) * DD * 2, st);
+  if (e == hipSuccess && h->mt_buf) e = hipMemsetAsync(h->mt_buf, 0, 2 * size_t(h->BH) * DD * 2, st);
+  if (e == hipSuccess && h->zc_buf) e = hipMemsetAsync(h->zc_buf, 0, 2 * size_t(h->BH) * h->D * 4, st);
   if (e == hipSuccess && h->split_cnt)
     e = hipMemsetAsync(h->split_cnt, 0, size_t(h->BH) * ((h->N + kQueryTile - 1) / kQueryTile) * 4, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -638,10 +685,12 @@ INFINI_EXPORT int infini_attn_destroy(infini_attn_t h) {
   if (h->layer_buf) (void)hipFree(h->layer_buf);
   if (h->dec_cache) (void)hipFree(h->dec_cache);
   if (h->bwd_buf) (void)hipFree(h->bwd_buf);
-  if (h->mt_cur) (void)hipFree(h->mt_cur);
+  if (h->mt_buf) (void)hipFree(h->mt_buf);
+  if (h->zc_buf) (void)hipFree(h->zc_buf);
   if (h->split_buf) (void)hipFree(h->split_buf);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
-  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->ev_sp) (void)hipEventDestroy(h->ev_sp);
+  if (h->ev_chain) (void)hipEventDestroy(h->ev_chain);
   if (h->side) (void)hipStreamDestroy(h->side);
   delete h;
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
@@ -705,7 +754,8 @@ static hipError_t materialize_zero_state(infini_attn* h, hipStream_t st) {
   if (!h->state_zero) return hipSuccess;
   const int64_t DD = int64_t(h->D) * h->D;
   hipError_t e = zero_f32(h->M, int64_t(h->BH) * (DD + h->D), st);   // M and z
-  if (e == hipSuccess && h->mt_cur) e = zero_f32(static_cast<float*>(h->mt_cur), int64_t(h->BH) * DD / 2, st);
+  if (e == hipSuccess && h->mt_buf) e = zero_f32(static_cast<float*>(mt_of(h, h->cur)), int64_t(h->BH) * DD / 2, st);
+  if (e == hipSuccess && h->zc_buf) e = zero_f32(zc_of(h, h->cur), int64_t(h->BH) * h->D, st);
   if (e == hipSuccess) h->state_zero = false;
   return e;
 }
@@ -715,7 +765,8 @@ INFINI_EXPORT int infini_attn_get_state(infini_attn_t h, float* M, float* z, voi
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const size_t DD = size_t(h->D) * h->D;
-  hipError_t e = materialize_zero_state(h, st);
+  hipError_t e = join_side(h, st);
+  if (e == hipSuccess) e = materialize_zero_state(h, st);
   if (e == hipSuccess && M) e = hipMemcpyAsync(M, h->M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
   if (e == hipSuccess && z) e = hipMemcpyAsync(z, h->z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -727,10 +778,13 @@ INFINI_EXPORT int infini_attn_set_state(infini_attn_t h, const float* M, const f
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const size_t DD = size_t(h->D) * h->D;
-  hipError_t e = materialize_zero_state(h, st);   // a part not given keeps its (zero) value
+  hipError_t e = join_side(h, st);
+  if (e == hipSuccess) e = materialize_zero_state(h, st);   // a part not given keeps its (zero) value
   if (e == hipSuccess && M) e = hipMemcpyAsync(h->M, M, size_t(h->BH) * DD * 4, hipMemcpyDefault, st);
   if (e == hipSuccess && z) e = hipMemcpyAsync(h->z, z, size_t(h->BH) * h->D * 4, hipMemcpyDefault, st);
-  if (e == hipSuccess && M && h->mt_cur) e = infini::launch_state_to_mt(h->M, h->mt_cur, h->BH, h->D, st);
+  if (e == hipSuccess && M && h->mt_buf) e = infini::launch_state_to_mt(h->M, mt_of(h, h->cur), h->BH, h->D, st);
+  if (e == hipSuccess && z && h->zc_buf)
+    e = hipMemcpyAsync(zc_of(h, h->cur), h->z, size_t(h->BH) * h->D * 4, hipMemcpyDeviceToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }
@@ -754,7 +808,8 @@ INFINI_EXPORT int64_t infini_attn_device_bytes(infini_attn_t h) {
   return int64_t(h->BH) * DD * 4 + int64_t(h->BH) * h->D * 4 + int64_t(2) * h->cfg.heads * 4 +
          static_cast<int64_t>(h->ws_bytes) + static_cast<int64_t>(h->layer_bytes) +
          (h->dec_cache ? int64_t(2) * h->BH * h->N * h->D * (h->bf16 ? 2 : 4) : 0) +
-         static_cast<int64_t>(h->bwd_bytes) + (h->mt_cur ? int64_t(h->BH) * DD * 2 : 0) +
+         static_cast<int64_t>(h->bwd_bytes) + (h->mt_buf ? int64_t(2) * h->BH * DD * 2 : 0) +
+         (h->zc_buf ? int64_t(2) * h->BH * h->D * 4 : 0) +
          static_cast<int64_t>(h->split_bytes);
 }
 
@@ -780,7 +835,8 @@ INFINI_EXPORT int infini_attn_profile_read(infini_attn_t h, infini_attn_profile_
   for (const auto& m : h->ev_marks) {
     if (e != hipSuccess) break;
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, h->ev_pool[m.second], h->ev_pool[m.second + 1]);
+    e = hipEventSynchronize(h->ev_pool[m.second + 1]);   // kernels on the side stream end on their own
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, h->ev_pool[m.second], h->ev_pool[m.second + 1]);
     out->total_ms[m.first] += ms;
     out->launches[m.first] += 1;
   }
@@ -918,7 +974,7 @@ int close_decode_segment(infini_attn* h, int n, hipStream_t st) {
   a.z = h->z;
   a.ws = h->ws;
   a.zero_state = h->state_zero;
-  a.mt_cur = h->mt_cur;
+  chain_outputs(h, a);
   a.chk = chunks_for(*h, 1);
   a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
   hipError_t e = hipSuccess;
@@ -926,6 +982,7 @@ int close_decode_segment(infini_attn* h, int n, hipStream_t st) {
   if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
   if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
   if (e != hipSuccess) return INFINI_ERR_HIP;
+  h->cur ^= 1;
   h->state_zero = false;
   return INFINI_OK;
 }
@@ -946,6 +1003,7 @@ INFINI_EXPORT int infini_attn_decode_step(infini_attn_t h, const void* q, const 
   DeviceGuard dg(h->device);
   if (!dg.ok) return INFINI_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (join_side(h, st) != hipSuccess) return INFINI_ERR_HIP;
   if (!h->dec_cache) {
     if (hipMalloc(&h->dec_cache, 2 * size_t(h->BH) * h->N * h->D * es) != hipSuccess) {
       (void)hipGetLastError();
@@ -961,7 +1019,7 @@ INFINI_EXPORT int infini_attn_decode_step(infini_attn_t h, const void* q, const 
   a.kc = h->dec_cache;
   a.vc = static_cast<char*>(h->dec_cache) + size_t(h->BH) * h->N * h->D * es;
   a.M = h->M;
-  a.mt = h->mt_cur;
+  a.mt = mt_of(h, h->cur);
   a.z = h->z;
   a.gate_g = h->gate;
   a.gate_omg = h->gate + h->cfg.heads;
@@ -990,6 +1048,7 @@ INFINI_EXPORT int infini_attn_decode_flush(infini_attn_t h, void* hip_stream) {
   if (!dg.ok) return INFINI_ERR_HIP;
   const int n = h->dec_p;
   h->dec_p = 0;
+  if (join_side(h, static_cast<hipStream_t>(hip_stream)) != hipSuccess) return INFINI_ERR_HIP;
   return close_decode_segment(h, n, static_cast<hipStream_t>(hip_stream));
 }
 
@@ -1030,6 +1089,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   DeviceGuard dg(h->device);
   if (!dg.ok) return INFINI_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (join_side(h, st) != hipSuccess) return INFINI_ERR_HIP;   // the workspace is shared
 
   const int S = static_cast<int>(S64);
   const int64_t U = int64_t(S) * h->BH;

@@ -42,6 +42,7 @@ constexpr int kThreadsA = 512;   // bf16 path: 8 waves
 constexpr int kBMA = 256;        // bf16 path: queries per workgroup (8 waves x 32)
 constexpr int kBN = 64;          // keys per tile
 constexpr float kTau = 8.f;
+constexpr int kMaxChunks = 8;    // split mode: key chunks per query tile at most
 
 template <int N_>
 using IC = std::integral_constant<int, N_>;
@@ -584,34 +585,40 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     if constexpr (SPLIT) {
       const int nchunks = sd.kc.div(nkv + kc - 1);
       if (nchunks > 1) {
-        // Hand the partial softmax state (O^T unnormalised, running maximum, row sum) to
-        // the query tile's slot c with device-coherent stores; once every wave's stores
-        // have completed, count the chunk.  The workgroup that counts the last chunk merges
-        // all of them in chunk order (the same arithmetic whichever workgroup it is) and
+        // Hand the partial softmax state (O^T unnormalised, in bf16; the running maximum
+        // and row sum in fp32) to the query tile's slot c with device-coherent stores; once
+        // every wave's stores have completed, count the chunk.  The workgroup that counts
+        // the last chunk merges all of them in chunk order, using for its own chunk the same
+        // bf16 values it stored (the same arithmetic whichever workgroup merges), and
         // finishes the tile; the others go on to their next item.  Nothing waits.
         const int tile = u * nq + qt;
         int base = 0;   // chunks of the query tiles before qt in a full segment
         for (int t = 0; t < qt; ++t) base += sd.kc.div((min(t * kBMA + kBMA, a.N) + kBN - 1) / kBN + kc - 1);
         const int64_t slot0 = static_cast<int64_t>(u) * a.split_slots + base;
-        constexpr uint32_t kAccBytes = 256u * D * 4u, kMlBytes = 512u * 8u;
+        constexpr int PG = 2 * DB;                       // 16-byte groups per lane (8 values each)
+        constexpr uint32_t kAccBytes = 8u * PG * 64u * 16u, kMlBytes = 512u * 8u;
         auto acc_rsrc = [&](int ch) __attribute__((always_inline)) {
-          return buffer_rsrc(a.split_acc + (slot0 + ch) * (256 * D), kAccBytes);
+          return buffer_rsrc(static_cast<const char*>(a.split_acc) + (slot0 + ch) * kAccBytes, kAccBytes);
         };
         auto ml_rsrc = [&](int ch) __attribute__((always_inline)) {
           return buffer_rsrc(a.split_ml + (slot0 + ch) * 1024, kMlBytes);
         };
-        auto acc_off = [&](int db, int r4) __attribute__((always_inline)) -> uint32_t {
-          return static_cast<uint32_t>(((wave * 4 * DB + 4 * db + r4) * 64 + lane) * 16);
+        auto acc_off = [&](int g) __attribute__((always_inline)) -> uint32_t {
+          return static_cast<uint32_t>(((wave * PG + g) * 64 + lane) * 16);
         };
+        // group g = 2 db + hh holds acc_o[db][8 hh .. 8 hh + 7]
+        u32x4 own[PG];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              own[2 * db + hh][e] = pack_bf16x2(acc_o[db][8 * hh + 2 * e], acc_o[db][8 * hh + 2 * e + 1]);
         {
           const auto ar = acc_rsrc(c);
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-              buffer_st16_dev(ar, acc_off(db, r4),
-                              u32x4{__float_as_uint(acc_o[db][4 * r4]), __float_as_uint(acc_o[db][4 * r4 + 1]),
-                                    __float_as_uint(acc_o[db][4 * r4 + 2]), __float_as_uint(acc_o[db][4 * r4 + 3])});
+          for (int g = 0; g < PG; ++g) buffer_st16_dev(ar, acc_off(g), own[g]);
           buffer_st8_dev(ml_rsrc(c), static_cast<uint32_t>((wave * 64 + lane) * 8),
                          u32x2{__float_as_uint(m_run), __float_as_uint(l_part)});
         }
@@ -629,10 +636,10 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
           if (has_next) load_q(qloc, row0n, nn, qtn * kBMA + 32 * wave);
         } else {
           if (tid == 0) __hip_atomic_store(a.split_cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          float mc[4], lc[4];
+          float mc[kMaxChunks], lc[kMaxChunks];
           float m_all = -INFINITY;
 #pragma unroll
-          for (int ch = 0; ch < 4; ++ch) {
+          for (int ch = 0; ch < kMaxChunks; ++ch) {
             if (ch < nchunks) {
               const u32x2 ml = buffer_ld8_dev(ml_rsrc(ch), static_cast<uint32_t>((wave * 64 + lane) * 8));
               mc[ch] = __uint_as_float(ml[0]);
@@ -643,20 +650,41 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
           float lsum = 0.f;
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc_o[db] = zero16();
+          // chunks in windows of kWin: the other chunks' loads of a window are all in
+          // flight before the window is added (in chunk order)
+          constexpr int kWin = 2;
 #pragma unroll
-          for (int ch = 0; ch < 4; ++ch) {
-            if (ch < nchunks) {
-              const float f = __builtin_amdgcn_exp2f(mc[ch] - m_all);
-              lsum = fmaf(f, lc[ch], lsum);
-              const auto ar = acc_rsrc(ch);
+          for (int w0 = 0; w0 < kMaxChunks; w0 += kWin) {
+            if (w0 < nchunks) {
+              u32x4 pb[kWin][PG];
 #pragma unroll
-              for (int db = 0; db < DB; ++db)
+              for (int j = 0; j < kWin; ++j) {
+                const int ch = w0 + j;
+                if (ch < nchunks && ch != c) {
+                  const auto ar = acc_rsrc(ch);
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                  const u32x4 v = buffer_ld16_dev(ar, acc_off(db, r4));
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) acc_o[db][4 * r4 + e] = fmaf(f, __uint_as_float(v[e]), acc_o[db][4 * r4 + e]);
+                  for (int g = 0; g < PG; ++g) pb[j][g] = buffer_ld16_dev(ar, acc_off(g));
                 }
+              }
+#pragma unroll
+              for (int j = 0; j < kWin; ++j) {
+                const int ch = w0 + j;
+                if (ch < nchunks) {
+                  const float f = __builtin_amdgcn_exp2f(mc[ch] - m_all);
+                  lsum = fmaf(f, lc[ch], lsum);
+                  const bool mine = ch == c;
+#pragma unroll
+                  for (int g = 0; g < PG; ++g) {
+                    const u32x4 v = mine ? own[g] : pb[j][g];
+                    const int db = g / 2, o = 8 * (g % 2);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                      acc_o[db][o + 2 * e] = fmaf(f, bf16lo_to_f32(v[e]), acc_o[db][o + 2 * e]);
+                      acc_o[db][o + 2 * e + 1] = fmaf(f, bf16hi_to_f32(v[e]), acc_o[db][o + 2 * e + 1]);
+                    }
+                  }
+                }
+              }
             }
           }
           l_part = lsum;
@@ -916,7 +944,8 @@ hipError_t launch_attention_d(const WindowArgs& a, hipStream_t st) {
     sd.h = FastDiv(static_cast<uint32_t>(a.H));
     if (a.split_kc > 0) {
       // split-key mode: one segment, MODE 0, items counted by the host
-      if (a.W != 1 || a.bwd_dout || a.a_mem || a.a_dot || a.lse || a.split_kc % 4 != 0 || a.split_items < 1 ||
+      if (a.W != 1 || a.bwd_dout || a.a_mem || a.a_dot || a.lse || a.split_kc % 4 != 0 ||
+          a.split_kc * kMaxChunks < 4 * nq || a.split_items < 1 ||
           a.split_slots < a.split_items || !a.split_acc || !a.split_ml || !a.split_cnt)
         return hipErrorInvalidValue;
       sd.kc = FastDiv(static_cast<uint32_t>(a.split_kc));

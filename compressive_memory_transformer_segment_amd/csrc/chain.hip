@@ -130,7 +130,10 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
       st8(mc, u32x2{pk[0], pk[1]});
     }
   }
-  if (zown) a.z[static_cast<int64_t>(bh) * D + tid] = z;
+  if (zown) {
+    a.z[static_cast<int64_t>(bh) * D + tid] = z;
+    if (a.z_cur) a.z_cur[static_cast<int64_t>(bh) * D + tid] = z;
+  }
   __syncthreads();   // every thread is past its reads of tr
 #pragma unroll
   for (int e = 0; e < EPT; ++e) tr[i0 + e][r] = m[e];
@@ -262,7 +265,10 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
       }
     }
   }
-  if (zown) a.z[static_cast<int64_t>(bh) * D + tid] = z;
+  if (zown) {
+    a.z[static_cast<int64_t>(bh) * D + tid] = z;
+    if (a.z_cur) a.z_cur[static_cast<int64_t>(bh) * D + tid] = z;
+  }
   if (BF16 && a.mt_cur)   // the final state as the retrieval operand of the next call
     static_cast<uint16_t*>(a.mt_cur)[bh * DD + static_cast<int64_t>(row) * D + i] = f32_to_bf16(m);
   __syncthreads();   // every thread is past the last step's reads of m_lds

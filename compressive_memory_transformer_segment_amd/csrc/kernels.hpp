@@ -55,6 +55,7 @@ struct WindowArgs {
   float* M;          // state [B,H,D,D]
   float* z;          // state [B,H,D]
   void* mt_cur;      // optional [B,H,D,D] bf16: the chain writes M^T of the window's final state here
+  float* z_cur;      // optional [B,H,D]: ... and the final z
   // Split-key mode of the bf16 attention (one segment, few (batch, head) pairs): the keys
   // of a query tile are split into chunks of split_kc tiles processed by different
   // workgroups; each writes its partial softmax state, and the last to finish merges them
@@ -64,7 +65,7 @@ struct WindowArgs {
   int split_slots;   // partial slots per (batch, head) pair: the items of a full segment;
                      // chunk c of query tile qt of pair u uses slot
                      // u * split_slots + (chunks of the query tiles before qt in a full segment) + c
-  float* split_acc;  // [slots][D * 256] partial O^T per slot
+  void* split_acc;   // [slots][512 * D bytes] partial O^T per slot, bf16, in result-register order
   float* split_ml;   // [slots][512][2] partial row maximum and row sum per lane
   int* split_cnt;    // [pairs * tiles] chunks finished per query tile (back to 0 after the merge)
   Workspace ws;

@@ -94,7 +94,18 @@ int infini_attn_create(const infini_attn_config_t* cfg, const float* beta_host,
                        void* hip_stream, infini_attn_t* out);
 
 /* One segment (Eq. 4): 1 <= n_tokens <= N tokens of Q/K/V [B,H,n_tokens,d] -> out.
- * Reads the state, writes out, advances the state by this segment. */
+ * Reads the state, writes out, advances the state by this segment.  This is the
+ * streaming call (the summary page's section 1: a stream processed segment by segment
+ * with bounded memory).  Since the segment's output depends only on the state carried in
+ * (Eq. 7 reads M_{s-1}, z_{s-1}), a bf16 handle runs the memory update (Eq. 8 / 9) on a
+ * second stream of its own while the attention runs on hip_stream: once the call's work
+ * on hip_stream has completed, q, k, v and out may be reused; the new state itself may
+ * still be in the making, and every later call on the handle (on any stream) waits for it
+ * before it touches the state.  With few (batch, head) pairs the attention splits each
+ * query tile's keys over several workgroups (results do not vary from run to run).  The
+ * same applies to forward_stream calls of one segment without a_mem / a_dot.
+ * Device memory for this (the split partials, two bf16 copies of M^T and of z) is
+ * allocated by create and counted by device_bytes. */
 int infini_attn_forward_segment(infini_attn_t h, const void* q, const void* k, const void* v,
                                 void* out, int32_t n_tokens, void* hip_stream);
 
@@ -246,7 +257,8 @@ int infini_attn_backward(infini_attn_t h, const void* q, const void* k, const vo
                          int64_t n_tokens, void* hip_stream);
 
 /* Per-kernel timing with HIP events, for measurement.  While enabled, every kernel the
- * handle launches is bracketed by two events on the call's stream.  profile_read waits
+ * handle launches is bracketed by two events on the stream it runs on (the call's stream,
+ * or the handle's second stream for the memory update of a one-segment call).  profile_read waits
  * for the recorded events, reports the summed durations per kernel kind, and clears the
  * record.  Kernel kinds: 0 = key sums (delta rule only), 1 = state pass (per-segment
  * sigma(K)^T V, key sums, delta Gram term), 2 = memory chain (Eq. 8/9

@@ -4,9 +4,11 @@ through the C-ABI against the CPU oracle.
 With few (batch, head) pairs a one-segment call splits the keys of each 256-query tile into
 chunks handled by different workgroups (the last one to finish merges the partial softmax
 states in chunk order), reads the carried state from its bf16 M^T copy, and runs the
-memory-update kernels on a second stream.  These tests cover that path at the workload
-shape (8 heads, d = 128, N = 2048: query tiles split into up to four chunks), at d = 64, on
-ragged segments, after reset_state and set_state, and its run-to-run determinism.
+memory-update kernels on a second stream (the chain, which writes the new state, is joined
+by the next call that needs it).  These tests cover that path at the workload shape (8
+heads, d = 128, N = 2048: query tiles split into up to four chunks), at d = 64, on ragged
+segments, after reset_state and set_state, mixed with the other calls on one handle, and
+its run-to-run determinism.
 Tolerances are in tests/gpu_util.py."""
 
 import numpy as np
@@ -127,3 +129,34 @@ def test_segment_calls_are_deterministic_and_agree_with_forward_stream(update):
     assert d_out <= 2 * 2**-8 * float(np.abs(ref).max()), d_out
     assert gu.rel(runs[0][1], M) <= 1e-5
     assert gu.rel(runs[0][2], z) <= 1e-6
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_mixed_calls_on_one_handle(update):
+    """One handle, one stream: forward_segment, a two-segment forward_stream, forward_segment
+    again, then token-by-token decoding and a flush.  Each call must see the state the
+    previous one left (the one-segment calls leave their memory update running on the
+    second stream), and the whole equals the oracle over the same segmentation."""
+    gu.require_gpu()
+    B, H, d, N = 1, 8, 128, 2048
+    n_dec = 5
+    L = 4 * N + n_dec
+    w = wl.Workload(f"seg-mixed-{update}", B, H, d, N, L, "bf16", update, seed=75)
+    gu.note(f"[segment] mixed calls {update}")
+    Q, K, V = wl.stream_inputs(w)
+    beta = wl.beta_for(w)
+    dev = [gu.to_dev(x, "bf16") for x in (Q, K, V)]
+    sl = lambda lo, hi: [x[:, :, lo:hi].contiguous() for x in dev]   # noqa: E731
+    with binding.InfiniAttention(B, H, d, N, update=update, eps=w.eps, beta=beta) as layer:
+        outs = [layer.forward_segment(*sl(0, N)), layer.forward_stream(*sl(N, 3 * N)),
+                layer.forward_segment(*sl(3 * N, 4 * N))]
+        for t in range(4 * N, L):
+            outs.append(layer.decode_step(*(x[:, :, t].contiguous() for x in dev))[:, :, None])
+        layer.decode_flush()
+        M, z = layer.get_state()
+        torch.cuda.synchronize()
+        out = torch.cat(outs, dim=2).float().cpu().numpy()
+        M, z = M.cpu().numpy(), z.cpu().numpy()
+    o_ref, M_ref, z_ref = orc.forward(Q, K, V, beta, N, update, eps=w.eps)
+    gu.check_output(out, o_ref, gu.BF16_TOL, "out")
+    gu.check_state(M, z, M_ref, z_ref, gu.BF16_TOL)
