@@ -1071,7 +1071,7 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   if (!dq || !dk || !dv || !dbeta) return INFINI_ERR_INVALID_ARG;
   if ((m0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_INVALID_ARG;
   const int64_t S64 = (n_tokens + h->N - 1) / h->N;
-  if (S64 > h->window) return INFINI_ERR_UNSUPPORTED;   // the whole call must fit one window
+  if (S64 > (int64_t(1) << 30)) return INFINI_ERR_INVALID_ARG;
   for (const void* p : {static_cast<const void*>(m0), static_cast<const void*>(z0),
                         static_cast<const void*>(dm_final), static_cast<const void*>(dz_final),
                         static_cast<const void*>(dq), static_cast<const void*>(dk), static_cast<const void*>(dv),
@@ -1092,7 +1092,14 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   if (join_side(h, st) != hipSuccess) return INFINI_ERR_HIP;   // the workspace is shared
 
   const int S = static_cast<int>(S64);
-  const int64_t U = int64_t(S) * h->BH;
+  // Windows of at most h->window segments: a call longer than one window first runs the
+  // memory recurrence forward to record the state at every window start, then runs the
+  // windows in reverse, each recomputing its forward from its recorded start state and
+  // handing the gradient of that state to the window before it as its final-state
+  // gradient (backpropagation through time over the whole call).
+  const int Wn = static_cast<int>(std::min<int64_t>(S, h->window));
+  const int nw = (S + Wn - 1) / Wn;
+  const int64_t U = int64_t(Wn) * h->BH;
   const int D = h->D;
   const int pt = (h->N + 63) / 64;
   // chunks of the sigma(Q)^T dnum pass: 512-token chunks on the matrix-core path
@@ -1100,8 +1107,9 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
                     : static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (512 + U - 1) / U)));
   const size_t rows = size_t(h->BH) * size_t(n_tokens);
   // scratch layout (256-byte aligned pieces)
+  const size_t st_floats = size_t(h->BH) * (size_t(D) * D + D);   // one (M, z) state
   const size_t sz[] = {
-      rows * D * es,                      // 0 forward output
+      h->bf16 ? 256 : rows * D * es,      // 0 forward output (the bf16 recomputation writes none)
       h->bf16 ? 0 : rows * D * 4,         // 1 A_mem (the bf16 recomputation needs neither)
       h->bf16 ? 0 : rows * D * 4,         // 2 A_dot
       rows * 4, rows * 4, rows * 4, rows * 4,   // 3-6 lse, dd, den, dden
@@ -1114,6 +1122,8 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
       size_t(h->BH) * D * D * 4,          // 13 state copy M
       size_t(h->BH) * D * 4,              // 14 state copy z
       h->bf16 && !h->delta ? size_t(U) * D * D * 4 : 0,   // 15 G_s packed in bf16, two orientations
+      nw > 1 ? size_t(nw) * st_floats * 4 : 0,             // 16 the state at every window start
+      nw > 1 ? 2 * st_floats * 4 : 0,                      // 17 state gradients between windows
   };
   constexpr int NP = sizeof(sz) / sizeof(sz[0]);
   size_t total = 0;
@@ -1140,8 +1150,9 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
       p += align_up(sz[i], 256);
     }
   }
-  float* Ms = static_cast<float*>(part[13]);
+  float* Ms = static_cast<float*>(part[13]);   // M then z: one (M, z) state
   float* zs = static_cast<float*>(part[14]);
+  const int64_t DDl = int64_t(D) * D;
   hipError_t e = hipSuccess;
   if (m0) {
     e = hipMemcpyAsync(Ms, m0, sz[13], hipMemcpyDefault, st);
@@ -1149,8 +1160,8 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
     if (e != hipSuccess) return INFINI_ERR_HIP;
   }
 
-  // the forward over the call, from (m0, z0) or zero, keeping A_mem, A_dot, lse and the
-  // per-segment states in the workspace; the handle's own state is not touched
+  // the forward of a window, keeping the backward's per-token terms (or A_mem, A_dot) and
+  // the per-segment states in the workspace; the handle's own state is not touched
   infini::WindowArgs a{};
   a.q = q;
   a.k = k;
@@ -1176,8 +1187,6 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   a.N = h->N;
   a.S = S;
   a.n_last = static_cast<int>(n_tokens - int64_t(S - 1) * h->N);
-  a.s0 = 0;
-  a.W = S;
   a.delta = h->delta;
   a.bf16 = h->bf16;
   a.eps = h->cfg.eps;
@@ -1188,19 +1197,50 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   a.M = Ms;
   a.z = zs;
   a.ws = h->ws;
-  a.zero_state = (m0 == nullptr);
-  a.chk = chunks_for(*h, S);
-  a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
-  if (h->delta) e = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
-  if (e == hipSuccess) e = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
-  if (e == hipSuccess) e = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
-  a.zero_state = false;   // the chain has recorded every segment's M^T_{s-1}, z_{s-1}
-  if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(a, st); });
-  if (e != hipSuccess) return INFINI_ERR_HIP;
+  auto set_window = [&](int w) {
+    a.s0 = w * Wn;
+    a.W = std::min(Wn, S - a.s0);
+    a.chk = chunks_for(*h, a.W);
+    a.ch = static_cast<int>(align_up(size_t((h->N + a.chk - 1) / a.chk), 64));
+  };
+  // state pass and chain of the window set in a: the chain leaves the window's final state
+  // in (Ms, zs) and records every segment's M^T_{s-1}, z_{s-1}
+  auto recurrence = [&](bool zero) -> hipError_t {
+    a.zero_state = zero;
+    hipError_t er = hipSuccess;
+    if (h->delta) er = timed(h, 0, st, [&] { return infini::launch_key_sums(a, st); });
+    if (er == hipSuccess) er = timed(h, 1, st, [&] { return infini::launch_state_pass(a, st); });
+    if (er == hipSuccess) er = timed(h, 2, st, [&] { return infini::launch_chain(a, st); });
+    a.zero_state = false;
+    return er;
+  };
+  float* ckpt = nw > 1 ? static_cast<float*>(part[16]) : nullptr;
+  float* gbuf = nw > 1 ? static_cast<float*>(part[17]) : nullptr;
+  // Ms holds M and zs holds z; a recorded state is M then z, st_floats in all
+  auto save_state = [&](float* dst) -> hipError_t {
+    hipError_t er = hipMemcpyAsync(dst, Ms, sz[13], hipMemcpyDeviceToDevice, st);
+    if (er == hipSuccess) er = hipMemcpyAsync(dst + h->BH * DDl, zs, sz[14], hipMemcpyDeviceToDevice, st);
+    return er;
+  };
+  auto load_state = [&](const float* src) -> hipError_t {
+    hipError_t er = hipMemcpyAsync(Ms, src, sz[13], hipMemcpyDeviceToDevice, st);
+    if (er == hipSuccess) er = hipMemcpyAsync(zs, src + h->BH * DDl, sz[14], hipMemcpyDeviceToDevice, st);
+    return er;
+  };
+  if (nw > 1) {   // the state at every window start
+    if (!m0) e = zero_f32(Ms, int64_t(h->BH) * DDl, st);
+    if (!m0 && e == hipSuccess) e = zero_f32(zs, int64_t(h->BH) * D, st);
+    for (int w = 0; w < nw && e == hipSuccess; ++w) {
+      e = save_state(ckpt + size_t(w) * st_floats);
+      if (e == hipSuccess && w + 1 < nw) {
+        set_window(w);
+        e = recurrence(false);
+      }
+    }
+    if (e != hipSuccess) return INFINI_ERR_HIP;
+  }
 
   infini::BackwardArgs bw{};
-  bw.w = a;
-  bw.w.zero_state = false;
   bw.dout = d_out;
   bw.dd = static_cast<float*>(part[4]);
   bw.den = static_cast<float*>(part[5]);
@@ -1215,14 +1255,34 @@ INFINI_EXPORT int infini_attn_backward(infini_attn_t h, const void* q, const voi
   bw.gz = static_cast<float*>(part[11]);
   bw.gpk = sz[15] ? static_cast<uint16_t*>(part[15]) : nullptr;
   bw.bq = static_cast<float*>(part[12]);
-  bw.dm_final = dm_final;
-  bw.dz_final = dz_final;
-  bw.dm0 = dm0;
-  bw.dz0 = dz0;
   bw.dbeta = dbeta;
   bw.rch = rch;
   bw.pt = pt;
   bw.ct = h->bf16 ? (h->N + 127) / 128 : pt;   // the bf16 update kernel works on 128-token tiles
-  e = timed(h, 7, st, [&] { return infini::launch_backward(bw, st); });
+  bw.skip_dbeta = nw > 1;
+  for (int w = nw - 1; w >= 0 && e == hipSuccess; --w) {
+    set_window(w);
+    if (nw > 1) e = load_state(ckpt + size_t(w) * st_floats);
+    if (e == hipSuccess) e = recurrence(nw == 1 && m0 == nullptr);
+    if (e == hipSuccess) e = timed(h, 3, st, [&] { return infini::launch_attention(a, st); });
+    if (e != hipSuccess) break;
+    bw.w = a;
+    bw.w.zero_state = false;
+    // gradient of this window's final state: the caller's for the last window, else what
+    // the next window handed back; the gradient of its start state goes to the window
+    // before it (or to the caller's dm0, dz0)
+    float* gnext = gbuf ? gbuf + size_t((w + 1) & 1) * st_floats : nullptr;
+    float* gmine = gbuf ? gbuf + size_t(w & 1) * st_floats : nullptr;
+    bw.dm_final = w == nw - 1 ? dm_final : gnext;
+    bw.dz_final = w == nw - 1 ? dz_final : gnext + h->BH * DDl;
+    bw.dm0 = w == 0 ? dm0 : gmine;
+    bw.dz0 = w == 0 ? dz0 : gmine + h->BH * DDl;
+    e = timed(h, 7, st, [&] { return infini::launch_backward(bw, st); });
+  }
+  if (e == hipSuccess && nw > 1) {
+    bw.w.s0 = 0;
+    bw.w.W = S;
+    e = timed(h, 7, st, [&] { return infini::launch_bwd_dbeta(bw, st); });
+  }
   return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP;
 }

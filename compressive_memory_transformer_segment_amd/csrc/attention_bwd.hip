@@ -601,7 +601,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void k_bwd_update_mfma(const Backwa
   const int s_local = u / BH, bh = u % BH;
   const int n = w.seg_tokens(s_local);
   const int t0 = tile * 128;
-  if (t0 >= n) return;
+  if (t0 >= n) {   // a tile past a short segment's end: its sigma(K)^T ddenk partial is zero
+    if (threadIdx.x < D) b.cpart[(static_cast<int64_t>(u) * b.ct + tile) * D + threadIdx.x] = 0.f;
+    return;
+  }
   const int64_t row0 = static_cast<int64_t>(bh) * w.T + static_cast<int64_t>(w.s0 + s_local) * w.N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

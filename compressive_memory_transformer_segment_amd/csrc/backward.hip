@@ -647,11 +647,16 @@ hipError_t launch_all(const BackwardArgs& b, hipStream_t st) {
     hipLaunchKernelGGL((k_bwd_zchain<D>), dim3(BH), dim3(D), 0, st, b);
     hipLaunchKernelGGL((k_bwd_final<D, BF16>), dim3(tiles), dim3(kBT), 0, st, b);
   }
-  hipLaunchKernelGGL(k_bwd_dbeta, dim3(static_cast<unsigned>(w.H)), dim3(kBetaThreads), 0, st, b);
+  if (!b.skip_dbeta) hipLaunchKernelGGL(k_bwd_dbeta, dim3(static_cast<unsigned>(w.H)), dim3(kBetaThreads), 0, st, b);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_bwd_dbeta(const BackwardArgs& b, hipStream_t st) {
+  hipLaunchKernelGGL(k_bwd_dbeta, dim3(static_cast<unsigned>(b.w.H)), dim3(kBetaThreads), 0, st, b);
+  return hipGetLastError();
+}
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t st) {
   if (b.w.D == 128) return b.w.bf16 ? launch_all<128, true>(b, st) : launch_all<128, false>(b, st);

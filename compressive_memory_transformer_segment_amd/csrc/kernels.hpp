@@ -143,12 +143,14 @@ struct BackwardArgs {
   float* dm0;            // optional [B,H,D,D] gradient of the initial M
   float* dz0;            // optional [B,H,D]
   float* dbeta;          // [H]
+  bool skip_dbeta;       // leave dbeta to a later launch_bwd_dbeta over the whole call
   int rch;               // token chunks of the R pass per segment
   int pt;                // 64-token tiles per segment (prep, dq, dkv, update, final)
   int ct;                // token tiles per segment of the cpart partials (pt, or 128-token tiles)
 };
 
 hipError_t launch_backward(const BackwardArgs& b, hipStream_t st);
+hipError_t launch_bwd_dbeta(const BackwardArgs& b, hipStream_t st);   // dbeta over all b.w.T tokens
 hipError_t launch_bwd_dq_mfma(const BackwardArgs& b, hipStream_t st);    // bf16: dQ (local + retrieval)
 hipError_t launch_bwd_dkv_mfma(const BackwardArgs& b, bool fuse_update, hipStream_t st);   // bf16: dK, dV
                                            // (local; + the linear memory-update part if fuse_update)

@@ -248,9 +248,13 @@ int64_t infini_attn_decode_position(infini_attn_t h);
  *   m0 [B, H, d, d], z0 [B, H, d], dm_final, dz_final: float32 device pointers or NULL;
  *   dq, dk, dv: float32 [B, H, n_tokens, d]; dbeta: float32 [H];
  *   dm0 [B, H, d, d], dz0 [B, H, d]: float32 or NULL (not wanted).
- * The handle's own state is neither read nor changed.  The call must fit one internal
- * window (n_tokens <= window_tokens): INFINI_ERR_UNSUPPORTED otherwise.  Device memory for
- * the recomputed forward and the gradient scratch is library-owned and kept for reuse. */
+ * The handle's own state is neither read nor changed.  A call longer than one internal
+ * window (window_tokens) runs the memory recurrence forward once to record the state at
+ * every window start (B*H*(d*d + d)*4 bytes per window), then the windows in reverse, each
+ * recomputing its forward from its recorded start state and passing the gradient of that
+ * state to the window before it: the gradients are those of the whole call.  Device memory
+ * for the recomputed forward and the gradient scratch (per-token terms for the whole call,
+ * per-segment terms for one window) is library-owned and kept for reuse. */
 int infini_attn_backward(infini_attn_t h, const void* q, const void* k, const void* v, const void* d_out,
                          const float* m0, const float* z0, const float* dm_final, const float* dz_final,
                          float* dq, float* dk, float* dv, float* dbeta, float* dm0, float* dz0,

@@ -91,14 +91,21 @@ CASES = [
     # the gate open, an initial state and gradients of the final state
     ("bf16-linear-d128-n2048-bench", 1, 2, 128, 2048, 4 * 2048 + 300, "bf16", "linear", True, True),
     ("bf16-delta-d128-n2048-bench", 1, 2, 128, 2048, 4 * 2048 + 300, "bf16", "delta", True, True),
+    # calls longer than one internal window (the last field: segments per window): the state
+    # at every window start recorded forward, the windows run in reverse
+    ("bf16-linear-d128-win2", 1, 2, 128, 256, 5 * 256 + 40, "bf16", "linear", True, True, 2),
+    ("bf16-delta-d128-win2", 2, 1, 128, 256, 5 * 256 + 40, "bf16", "delta", False, True, 2),
+    ("f32-delta-d64-win1", 1, 2, 64, 64, 3 * 64 + 5, "f32", "delta", True, True, 1),
+    ("bf16-linear-d128-n2048-win2", 1, 2, 128, 2048, 4 * 2048 + 300, "bf16", "linear", True, True, 2),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_backward_matches_oracle(case):
     gu.require_gpu()
-    name, B, H, d, N, L, dtype, update, with_state, with_dstate = case
-    gu.note(f"[backward] {name}: B={B} H={H} d={d} N={N} L={L} {dtype} {update}")
+    name, B, H, d, N, L, dtype, update, with_state, with_dstate = case[:10]
+    win = case[10] if len(case) > 10 else 0
+    gu.note(f"[backward] {name}: B={B} H={H} d={d} N={N} L={L} {dtype} {update} window {win or 'default'}")
     w = wl.Workload(name, B, H, d, N, L, dtype, update, seed=61)
     Q, K, V = wl.stream_inputs(w)
     beta = wl.beta_for(w)
@@ -116,7 +123,8 @@ def test_backward_matches_oracle(case):
         dM = (rng.standard_normal((B, H, d, d)) * 0.05).astype(np.float32)
         dz = (rng.standard_normal((B, H, d)) * 0.05).astype(np.float32)
     dev = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to("cuda")   # noqa: E731
-    with binding.InfiniAttention(B, H, d, N, update=update, io_dtype=dtype, eps=w.eps, beta=beta) as layer:
+    with binding.InfiniAttention(B, H, d, N, update=update, io_dtype=dtype, eps=w.eps, beta=beta,
+                                 max_window_segments=win) as layer:
         res = layer.backward(*(gu.to_dev(x, dtype) for x in (Q, K, V, dO)), m0=dev(M0), z0=dev(z0),
                              dm_final=dev(dM), dz_final=dev(dz))
         torch.cuda.synchronize()
@@ -240,3 +248,69 @@ def test_full_size_linear_update_gradients_closed_form():
         ref_dk = (v64 @ m.T + dzf[0, h].astype(np.float64)) * dsig
         _check_grad(dv[0, h, toks], ref_dv, 2e-2, f"dv h{h}")
         _check_grad(dk[0, h, toks], ref_dk, 2e-2, f"dk h{h}")
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_full_size_multi_window_backward_agrees_with_one_window(update):
+    """2 heads, d=128, N=2048, 32 segments (64K tokens): the backward of the whole stream
+    as one internal window and as four windows of 8 segments (states recorded at the
+    window starts, windows run in reverse, the state gradient handed back between them)
+    agree to rounding, with an initial state and final-state gradients."""
+    gu.require_gpu()
+    B, H, d, N, S = 1, 2, 128, 2048, 32
+    w = wl.Workload(f"bwd-multiwin-{update}", B, H, d, N, S * N, "bf16", update, seed=69)
+    gu.note(f"[backward] full size, 4 windows vs 1: {update}")
+    dev = [gu.to_dev(x, "bf16") for x in wl.stream_inputs(w)]
+    rng = np.random.default_rng(70)
+    d_out = gu.to_dev(rng.standard_normal((B, H, S * N, d)).astype(np.float32), "bf16")
+    m0 = torch.from_numpy((rng.standard_normal((B, H, d, d)) * 0.02).astype(np.float32)).cuda()
+    z0 = torch.from_numpy(np.abs(rng.standard_normal((B, H, d)) * 100).astype(np.float32)).cuda()
+    dmf = torch.from_numpy((rng.standard_normal((B, H, d, d)) * 0.05).astype(np.float32)).cuda()
+    dzf = torch.from_numpy((rng.standard_normal((B, H, d)) * 0.05).astype(np.float32)).cuda()
+    res = {}
+    for win in (32, 8):
+        with binding.InfiniAttention(B, H, d, N, update=update, eps=w.eps, beta=wl.beta_for(w),
+                                     max_window_segments=win) as layer:
+            g = layer.backward(*dev, d_out, m0=m0, z0=z0, dm_final=dmf, dz_final=dzf)
+            torch.cuda.synchronize()
+            res[win] = {k_: t.cpu().numpy() for k_, t in g.items()}
+            del g
+    for k_ in res[32]:
+        _check_grad(res[8][k_], res[32][k_], 1e-3, f"{k_} (4 windows vs 1)",
+                    seg_len=N if k_ in ("dq", "dk", "dv") else None)
+
+
+@pytest.mark.parametrize("update", ["linear", "delta"])
+def test_backward_scratch_reuse_with_a_short_last_segment(update):
+    """One handle, two backward calls: a long one (every token tile of every segment
+    written), then one whose last segment is short.  The second reuses the scratch of the
+    first; per-tile partials of the tiles past the short segment's end must not leak in.
+    Both start from a carried state, as in training.  (From a zero state the delta rule's
+    first-segment dV is a small residual -- the second segment's update nearly erases the
+    first one's contribution -- and its per-segment error against float64 reaches ~2.5%.)"""
+    gu.require_gpu()
+    B, H, d, N = 1, 2, 128, 2048
+    beta = wl.beta_for(wl.Workload("reuse", B, H, d, N, N, "bf16", update, seed=76))
+    _, M0, z0 = ob.forward_torch(*(torch.tensor(x, dtype=torch.float64) for x in wl.stream_inputs(
+        wl.Workload("reuse-pre", B, H, d, N, 2 * N, "bf16", update, seed=63))),
+        torch.tensor(beta, dtype=torch.float64), N, update)
+    M0, z0 = M0.numpy().astype(np.float32), z0.numpy().astype(np.float32)
+    with binding.InfiniAttention(B, H, d, N, update=update, eps=1e-6, beta=beta) as layer:
+        for L, seed in ((2 * N, 77), (N + 40, 78)):
+            w = wl.Workload(f"reuse-{update}-{L}", B, H, d, N, L, "bf16", update, seed=seed)
+            gu.note(f"[backward] scratch reuse {update}: L={L}")
+            Q, K, V = wl.stream_inputs(w)
+            rng = np.random.default_rng(seed)
+            dO = wl.round_to_bf16(rng.standard_normal((B, H, L, d)).astype(np.float32))
+            dM = (rng.standard_normal((B, H, d, d)) * 0.05).astype(np.float32)
+            dz = (rng.standard_normal((B, H, d)) * 0.05).astype(np.float32)
+            res = layer.backward(*(gu.to_dev(x, "bf16") for x in (Q, K, V, dO)),
+                                 m0=torch.from_numpy(M0).cuda(), z0=torch.from_numpy(z0).cuda(),
+                                 dm_final=torch.from_numpy(dM).cuda(), dz_final=torch.from_numpy(dz).cuda())
+            torch.cuda.synchronize()
+            got = {k_: t.cpu().numpy() for k_, t in res.items()}
+            ref = ob.gradients(Q, K, V, beta, dO, N, update, w.eps, None, M0, z0, dM, dz)
+            for gname, rname in (("dq", "dQ"), ("dk", "dK"), ("dv", "dV"), ("dbeta", "dbeta"), ("dm0", "dM0"),
+                                 ("dz0", "dz0")):
+                _check_grad(got[gname], ref[rname], GRAD_TOL["bf16"], f"{gname} L={L}",
+                            seg_len=N if gname in ("dq", "dk", "dv") else None)
