@@ -11,6 +11,8 @@
 // waits on another.  For every segment of the window the chain first records the state
 // the segment reads (M^T_{s-1} in the attention kernel's operand type, and z_{s-1}), then
 // advances it; the window's final state goes back to the handle's M ([d_key][d_value]) and z.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -148,39 +150,55 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
   }
 }
 
-// Delta rule, G_s summed over the chunks beforehand (k_gsum).  A workgroup owns four
-// rows of M^T of one (b,h); thread (r, i) owns row rb + r, column i (the row is the same
-// for the whole wave, so the reads of M^T rows are broadcasts; thread i reads row i of
-// G_s).  Nothing but M^T itself depends on the chain, so step s + 1's G and U^T / key-sum
-// partials are loaded into registers while step s multiplies, and G_{s+1} is staged into
-// the other of two LDS buffers at the end of step s.  One barrier per step.  Two waves
-// per SIMD, so that one wave's LDS latency is covered by the other's FMAs.  Rows of M^T
-// evolve independently, so workgroups never wait on each other.
-template <int D, int CHK, bool BF16>
+// Delta rule, G_s summed over the chunks beforehand (k_gsum).  A workgroup owns R = 4 RPT
+// rows of M^T of one (b,h); thread (g, i) owns rows rb + RPT g .. + RPT - 1, column i (g is
+// wave-uniform, so the reads of M^T rows are broadcasts; thread i reads row i of G_s once
+// per step for its RPT rows).  Nothing but M^T itself depends on the chain, so step s + 1's G
+// and U^T / key-sum partials are loaded into registers while step s multiplies, and G_{s+1}
+// is staged into the other of two LDS buffers at the end of step s.  One barrier per step.
+// Two waves per SIMD, so that one wave's LDS latency is covered by the other's FMAs.  Rows of
+// M^T evolve independently, so workgroups never wait on each other.  Every workgroup stages
+// all of G_s each step: more rows per workgroup (RPT = 4) divide that traffic by four when
+// there are enough (b,h) pairs to fill the compute units with fewer workgroups.
+template <int D, int CHK, bool BF16, int RPT>
 __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, const float* __restrict__ gsum) {
   constexpr int NT = 4 * D;
+  constexpr int R = 4 * RPT;              // rows of M^T per workgroup
   constexpr int GP = D + 4;               // LDS row pitch of G and of the M^T rows (floats)
   constexpr int GV = D * D / 4 / NT;      // float4 elements of G_s per thread
+  constexpr int MPT = R * D / NT;         // elements of M per thread in the transposing loads (RPT)
   __shared__ __align__(16) float g_lds[2][D][GP];
-  __shared__ __align__(16) float m_lds[2][4][GP];
+  __shared__ __align__(16) float m_lds[2][R][GP];
 
   const int BH = a.B * a.H;
   const int W = a.W;
-  const int bh = blockIdx.x / (D / 4);
-  const int rb = (blockIdx.x % (D / 4)) * 4;
+  const int bh = blockIdx.x / (D / R);
+  const int rb = (blockIdx.x % (D / R)) * R;
   const int tid = threadIdx.x;
-  const int r = tid / D, i = tid % D;     // r is wave-uniform (D is a multiple of 64)
-  const int row = rb + r;                 // this thread's row of M^T
+  const int g = tid / D, i = tid % D;     // g is wave-uniform (D is a multiple of 64)
+  const int r0 = RPT * g;                 // this thread's first row in the workgroup's block
   const int64_t DD = static_cast<int64_t>(D) * D;
 
-  // M^T[row][i] = M[i][row]: the workgroup's 4 columns of M through LDS (4 lanes read one
-  // row's 16 bytes)
+  // M^T[rb + r][i] = M[i][rb + r]: the workgroup's R columns of M through LDS (thread t reads
+  // MPT consecutive columns of row t / (R / MPT))
   float* Mb = a.M + bh * DD + rb;
-  float m = 0.f;
+  const int mrow = tid / (R / MPT), mcol = (tid % (R / MPT)) * MPT;
+  float m[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) m[j] = 0.f;
   if (!a.zero_state) {
-    m_lds[0][tid % 4][tid / 4] = Mb[static_cast<int64_t>(tid / 4) * D + tid % 4];
+    const float* src = Mb + static_cast<int64_t>(mrow) * D + mcol;
+    if constexpr (MPT == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) m_lds[0][mcol + c][mrow] = v[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < MPT; ++c) m_lds[0][mcol + c][mrow] = src[c];
+    }
     __syncthreads();
-    m = m_lds[0][r][i];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) m[j] = m_lds[0][r0 + j][i];
   }
   const bool zown = rb == 0 && tid < D;
   float z = zown && !a.zero_state ? a.z[static_cast<int64_t>(bh) * D + tid] : 0.f;
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
   // what one step loads ahead of the chain
   struct Pre {
     f32x4 g[GV];
-    float up[CHK];
+    float up[CHK][RPT];
     float dz[CHK];
   };
   auto fetch = [&](int s, Pre& p) __attribute__((always_inline)) {
@@ -198,7 +216,9 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
     for (int v = 0; v < GV; ++v) p.g[v] = *reinterpret_cast<const f32x4*>(src + 4 * (tid + v * NT));
 #pragma unroll
     for (int c = 0; c < CHK; ++c) {
-      p.up[c] = a.ws.u[(u * CHK + c) * DD + static_cast<int64_t>(row) * D + i];
+#pragma unroll
+      for (int j = 0; j < RPT; ++j)
+        p.up[c][j] = a.ws.u[(u * CHK + c) * DD + static_cast<int64_t>(rb + r0 + j) * D + i];
       p.dz[c] = a.ws.dz[(u * CHK + c) * D + i];   // used by owners only
     }
   };
@@ -215,9 +235,13 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
     const int b = s & 1;
     const int64_t u = static_cast<int64_t>(s) * BH + bh;
     // record the state this segment reads
-    const int64_t off = u * DD + static_cast<int64_t>(row) * D + i;
-    if constexpr (BF16) static_cast<uint16_t*>(a.ws.mt)[off] = f32_to_bf16(m);
-    else static_cast<float*>(a.ws.mt)[off] = m;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int64_t off = u * DD + static_cast<int64_t>(rb + r0 + j) * D + i;
+      if constexpr (BF16) static_cast<uint16_t*>(a.ws.mt)[off] = f32_to_bf16(m[j]);
+      else static_cast<float*>(a.ws.mt)[off] = m[j];
+      m_lds[b][r0 + j][i] = m[j];
+    }
     if (zown) {
       a.ws.zb[u * D + tid] = z;
       float dz = 0.f;
@@ -225,28 +249,35 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
       for (int c = 0; c < CHK; ++c) dz += p.dz[c];
       z += dz;
     }
-    m_lds[b][r][i] = m;
     __syncthreads();   // G_s and this step's rows of M^T are in LDS
     // (M^T G^T)[row][i] = sum_k M^T[row][k] G[i][k], as four interleaved partial sums
-    // (k mod 4); k in blocks of 16 whose 8 LDS reads are issued together
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // (k mod 4) per row; k in blocks of 16 whose G reads serve all RPT rows
+    f32x4 acc[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int kk = 0; kk < D; kk += 16) {
-      f32x4 gk[4], mk[4];
+      f32x4 gk[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        gk[j] = *reinterpret_cast<const f32x4*>(&g_lds[b][i][kk + 4 * j]);
-        mk[j] = *reinterpret_cast<const f32x4*>(&m_lds[b][r][kk + 4 * j]);
+      for (int q = 0; q < 4; ++q) gk[q] = *reinterpret_cast<const f32x4*>(&g_lds[b][i][kk + 4 * q]);
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        f32x4 mk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mk[q] = *reinterpret_cast<const f32x4*>(&m_lds[b][r0 + j][kk + 4 * q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(mk[q][e], gk[q][e], acc[j][e]);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(mk[j][e], gk[j][e], acc[e]);
     }
-    float ut = 0.f;
 #pragma unroll
-    for (int c = 0; c < CHK; ++c) ut += p.up[c];
-    m = (m - ((acc[0] + acc[1]) + (acc[2] + acc[3]))) + ut;
+    for (int j = 0; j < RPT; ++j) {
+      float ut = 0.f;
+#pragma unroll
+      for (int c = 0; c < CHK; ++c) ut += p.up[c][j];
+      m[j] = (m[j] - ((acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]))) + ut;
+    }
     // G_{s+1} into the buffer step s - 1 read (every thread is past this step's barrier)
     stage(b ^ 1, nx);
   };
@@ -270,11 +301,25 @@ __global__ __launch_bounds__(4 * D, 1) void k_chain_delta(const WindowArgs a, co
     if (a.z_cur) a.z_cur[static_cast<int64_t>(bh) * D + tid] = z;
   }
   if (BF16 && a.mt_cur)   // the final state as the retrieval operand of the next call
-    static_cast<uint16_t*>(a.mt_cur)[bh * DD + static_cast<int64_t>(row) * D + i] = f32_to_bf16(m);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+      static_cast<uint16_t*>(a.mt_cur)[bh * DD + static_cast<int64_t>(rb + r0 + j) * D + i] = f32_to_bf16(m[j]);
   __syncthreads();   // every thread is past the last step's reads of m_lds
-  m_lds[0][r][i] = m;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) m_lds[0][r0 + j][i] = m[j];
   __syncthreads();
-  Mb[static_cast<int64_t>(tid / 4) * D + tid % 4] = m_lds[0][tid % 4][tid / 4];
+  {
+    float* dst = Mb + static_cast<int64_t>(mrow) * D + mcol;
+    if constexpr (MPT == 4) {
+      f32x4 v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = m_lds[0][mcol + c][mrow];
+      *reinterpret_cast<f32x4*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int c = 0; c < MPT; ++c) dst[c] = m_lds[0][mcol + c][mrow];
+    }
+  }
 }
 
 // M [pairs][D][D] (fp32, [d_key][d_value]) -> M^T in bf16 ([d_value][d_key]), through a
@@ -319,13 +364,26 @@ hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((k_gsum<D>), dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, a);
       gsum = a.ws.gs;
     }
-    const dim3 grid(BH * (D / 4));
     const dim3 block(4 * D);
-    if (!a.bf16) hipLaunchKernelGGL((k_chain_delta<D, 1, false>), grid, block, 0, st, a, gsum);
-    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_delta<D, 1, true>), grid, block, 0, st, a, gsum);
-    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_delta<D, 2, true>), grid, block, 0, st, a, gsum);
-    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_delta<D, 4, true>), grid, block, 0, st, a, gsum);
-    else hipLaunchKernelGGL((k_chain_delta<D, 8, true>), grid, block, 0, st, a, gsum);
+    // 16 rows of M^T per workgroup once that still gives every compute unit a workgroup
+    // (one workgroup per compute unit: 152 KB of LDS), else 4
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    const bool wide = BH * (D / 16) >= cus;
+    const dim3 grid(BH * (D / (wide ? 16 : 4)));
+    auto go = [&](auto chk_c, auto bf_c) {
+      constexpr int C = decltype(chk_c)::value;
+      constexpr bool BF = decltype(bf_c)::value;
+      if (wide) hipLaunchKernelGGL((k_chain_delta<D, C, BF, 4>), grid, block, 0, st, a, gsum);
+      else hipLaunchKernelGGL((k_chain_delta<D, C, BF, 1>), grid, block, 0, st, a, gsum);
+    };
+    if (!a.bf16) go(std::integral_constant<int, 1>{}, std::false_type{});
+    else if (a.chk == 1) go(std::integral_constant<int, 1>{}, std::true_type{});
+    else if (a.chk == 2) go(std::integral_constant<int, 2>{}, std::true_type{});
+    else if (a.chk <= 4) go(std::integral_constant<int, 4>{}, std::true_type{});
+    else go(std::integral_constant<int, 8>{}, std::true_type{});
   } else {
     const dim3 grid(BH * (D / 16));
     if (!a.bf16) hipLaunchKernelGGL((k_chain_linear<D, 1, false>), grid, dim3(kThreads), 0, st, a);
