@@ -442,18 +442,6 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       pv(vb, p2, p3);
     };
 
-    // Unmasked tiles j < jm run software-pipelined: iteration j holds the scores of tile j
-    // (sc0 / sc1, maximum mxc) and computes those of tile j + 1 while it exponentiates and
-    // multiplies tile j, so a wave's own MFMAs run under its softmax arithmetic.  Every
-    // group of MFMAs finds its LDS operands already in registers: the operands of the next
-    // group are read while a group runs.  An iteration has four phases of 8 MFMAs each:
-    //   1. S^T(j + 1), k-steps 0 .. KS/2 - 1 (both key halves) | exp of tile j, half 0 | read K, k-steps KS/2 ..
-    //   2. S^T(j + 1), k-steps KS/2 .. KS - 1                 | exp of tile j, half 1 | read V^T(j), half 0
-    //   3. O^T += V^T P^T(j), half 0                          | max of tile j + 1    | read V^T(j), half 1
-    //   4. O^T += V^T P^T(j), half 1                          |                      | read K(j + 2), k-steps 0 ..
-    // Buffer j % 4 holds tile j.  Copy j + 3 of the sequence is issued at the start of
-    // iteration j into buffer (j + 3) % 4 (tile j - 1, done with at the previous barrier) and
-    // waited for at its end, so tiles j + 1 and j + 2 are complete throughout iteration j.
     auto load_k = [&](const uint16_t* kt, int k0, KOps& ak) __attribute__((always_inline)) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -467,74 +455,130 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
         s1 = mfma32x32x16(ak[1][i], as_bf16x8(qreg[k0 + i]), s1);
       }
     };
+    // Unmasked tiles j < jm run software-pipelined: iteration j holds the scores of tile j
+    // (sc0 / sc1, maximum mxc) and computes those of tile j + 1 while it exponentiates and
+    // multiplies tile j.  The exponentials are the largest VALU cost (a quarter-rate
+    // instruction per score), so they are spread evenly over the iteration's MFMAs, in key
+    // quarters (16 keys: 8 score registers of one half): quarter q of tile j is exponentiated
+    // in group q and multiplied (O^T += V^T P^T, one MFMA per 32-row block of the head
+    // dimension) in group q + 1, alternating with the score MFMAs of tile j + 1:
+    //   group 0: S^T(j + 1) k-steps 0 .. KG - 1             | P quarter 0
+    //   group 1: S^T(j + 1) next KG k-steps | PV quarter 0  | P quarter 1
+    //   group 2: S^T(j + 1) next KG k-steps | PV quarter 1  | P quarter 2
+    //   group 3: S^T(j + 1) last KG k-steps | PV quarter 2  | P quarter 3
+    //   group 4:                              PV quarter 3  | maximum of tile j + 1
+    // Every MFMA is a slot of its own (a scheduling barrier after it) holding its share of
+    // the group's exponentials and of the LDS reads for the next group (the K^T operands of
+    // its score k-steps, the V^T operands of its PV quarter), so no slot carries more VALU
+    // work than the MFMA before it covers.  Products and row sums add in the same order as
+    // with whole halves.  Buffer j % 4 holds tile j.  Copy j + 3 of the sequence is issued at
+    // the start of iteration j into buffer (j + 3) % 4 (tile j - 1, done with at the previous
+    // barrier) and waited for at its end, so tiles j + 1 and j + 2 are complete throughout
+    // iteration j.
+    constexpr int KG = KS / 4;    // score k-steps per group (2 KG = DB MFMAs of each kind)
+    typedef bf16x8 KGrp[2][KG];   // [key half][k-step]
+    typedef u32x2 VQ[DB][2];      // V^T operands of one key quarter, two transpose reads each
+    auto read_k = [&](const uint16_t* kt, int k0, int r, KGrp& ak) __attribute__((always_inline)) {
+      ak[r % 2][r / 2] = as_bf16x8(ld16(kt + g_rd + (r % 2) * 256 * CPR + 256 * (k0 + r / 2)));
+    };
+    auto read_v = [&](const uint16_t* kt, int q, int r, VQ& vq) __attribute__((always_inline)) {
+      vq[r / 2][r % 2] = lds_read_tr16(kt + v_rd + 4 * q * 32 * CPR + 128 * (r / 2) + (r % 2) * 2 * 32 * CPR);
+    };
+    auto s_mfma = [&](const KGrp& ak, int k0, int m, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+      if (m % 2 == 0) s0 = mfma32x32x16(ak[0][m / 2], as_bf16x8(qreg[k0 + m / 2]), s0);
+      else s1 = mfma32x32x16(ak[1][m / 2], as_bf16x8(qreg[k0 + m / 2]), s1);
+    };
+    auto pv_mfma = [&](const VQ& vq, int db, const u32x4& pq) __attribute__((always_inline)) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{vq[db][0][0], vq[db][0][1], vq[db][1][0], vq[db][1][1]});
+      acc_o[db] = mfma32x32x16(av, as_bf16x8(pq), acc_o[db]);
+    };
+    // score e of a key quarter (registers r0 .. r0 + 7 of sc) -> P; an odd e also packs the
+    // pair and adds it to the row sum
+    auto p_elem = [&](f32x16& sc, int r0, int e, u32x4& pq) __attribute__((always_inline)) {
+      sc[r0 + e] = __builtin_amdgcn_exp2f(fmaf(sc[r0 + e], c2, -m_run));
+      if (e % 2 == 1) {
+        pq[e / 2] = pack_bf16x2(sc[r0 + e - 1], sc[r0 + e]);
+        l_part = add_bf16x2(pq[e / 2], l_part);
+      }
+    };
     f32x16 sc0, sc1;
-    KOps kq;
-    load_k(buf0, 0, kq);   // tile t0
-    sc0 = zero16();
-    sc1 = zero16();
-    qk_part(kq, 0, sc0, sc1);
-    load_k(buf0, KH, kq);
-    qk_part(kq, KH, sc0, sc1);   // tile 0
+    {
+      KOps kq;
+      load_k(buf0, 0, kq);   // tile t0
+      sc0 = zero16();
+      sc1 = zero16();
+      qk_part(kq, 0, sc0, sc1);
+      load_k(buf0, KH, kq);
+      qk_part(kq, KH, sc0, sc1);   // tile 0
+    }
     float mxc = tile_max(sc0, sc1);
     // Tile 2 (issued last in the previous item) is complete here in every wave, ahead of
     // its Q rows in the wave's load order; after the barrier it is visible to all.
     __builtin_amdgcn_s_barrier();
-    if (tu > t0) load_k(buf1, 0, kq);   // tile t0 + 1, k-steps 0 .. KH - 1
+    KGrp kg0;
+    if (tu > t0) {   // tile t0 + 1, the first group's k-steps
+#pragma unroll
+      for (int r = 0; r < 2 * KG; ++r) read_k(buf1, 0, r, kg0);
+    }
     auto pstep = [&](int j, auto bufc) __attribute__((always_inline)) {
       constexpr int b = decltype(bufc)::value;
       maybe_rescale(mxc);
       if (j == t0 + 1) issue_mt();
       issue(j + 3, bufp(IC<b + 3>{}));
       const uint16_t* kt = bufp(bufc);
+      const uint16_t* kn = bufp(IC<b + 1>{});
+      const uint16_t* kn2 = bufp(IC<b + 2>{});
       f32x16 n0 = zero16(), n1 = zero16();
-      bf16x8 p0, p1, p2, p3;
-      KOps kq2;
-      bf16x8 va[DB][2], vb[DB][2];
-      // phase 1
-      load_k(bufp(IC<b + 1>{}), KH, kq2);
-      qk_part(kq, 0, n0, n1);
-      half_exp(sc0, p0, p1);
-      // interleave: each MFMA followed by its share of the LDS reads and the VALU work
-#pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);   // VALU
-      }
+      u32x4 pq[4];
+      KGrp kg1;
+      VQ va, vb;
       __builtin_amdgcn_sched_barrier(0);
-      // phase 2
-      v_operands(kt, 0, va);
-      qk_part(kq2, KH, n0, n1);
-      half_exp(sc1, p2, p3);
+      // group 0: DB score MFMAs; reads: K^T of group 1, V^T of quarter 0
 #pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB / KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // phase 3
-      v_operands(kt, 1, vb);
-      pv(va, p0, p1);
-      const float mh0 = half_max(n0);
+      for (int i = 0; i < DB; ++i) {
+        s_mfma(kg0, 0, i, n0, n1);
 #pragma unroll
-      for (int i = 0; i < 2 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // phase 4
-      load_k(bufp(IC<b + 2>{}), 0, kq);   // tile j + 2 (read but unused past the last tile)
-      pv(vb, p2, p3);
-      mxc = max_across_halves(fmaxf(mh0, half_max(n1))) * c2;
+        for (int r = 3 * DB * i / DB; r < 3 * DB * (i + 1) / DB; ++r) {
+          if (r < DB) read_k(kn, KG, r, kg1);
+          else read_v(kt, 0, r - DB, va);
+        }
 #pragma unroll
-      for (int i = 0; i < 2 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, KS / DB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        for (int e = 8 * i / DB; e < 8 * (i + 1) / DB; ++e) p_elem(sc0, 0, e, pq[0]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // groups 1 .. 3: score and PV MFMAs alternating
+      auto mid = [&](auto gc, const KGrp& ak, KGrp& an, const VQ& vu, VQ& vn, f32x16& sq) __attribute__((always_inline)) {
+        constexpr int G = decltype(gc)::value;
+#pragma unroll
+        for (int i = 0; i < 2 * DB; ++i) {
+          if (i % 2 == 0) s_mfma(ak, G * KG, i / 2, n0, n1);
+          else pv_mfma(vu, i / 2, pq[G - 1]);
+          // reads: K^T of group G + 1 (of tile j + 2's group 0 in group 3), V^T of quarter G
+#pragma unroll
+          for (int r = 3 * DB * i / (2 * DB); r < 3 * DB * (i + 1) / (2 * DB); ++r) {
+            // group 4 runs PV only: group 3 reads its V^T first
+            const int rk = G < 3 ? r : r - 2 * DB, rv = G < 3 ? r - DB : r;
+            if (rk >= 0 && rk < DB) read_k(G < 3 ? kn : kn2, G < 3 ? (G + 1) * KG : 0, rk, an);
+            else read_v(kt, G, rv, vn);
+          }
+#pragma unroll
+          for (int e = 8 * i / (2 * DB); e < 8 * (i + 1) / (2 * DB); ++e) p_elem(sq, 8 * (G % 2), e, pq[G]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      mid(IC<1>{}, kg1, kg0, va, vb, sc0);
+      mid(IC<2>{}, kg0, kg1, vb, va, sc1);
+      mid(IC<3>{}, kg1, kg0, va, vb, sc1);   // kg0 <- tile j + 2, read but unused past the last tile
+      // group 4: PV quarter 3, the maximum of tile j + 1
+      float mh0 = 0.f, mh1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) {
+        pv_mfma(vb, i, pq[3]);
+        if (i == 0) mh0 = half_max(n0);
+        if (i == 1) mh1 = half_max(n1);
+        if (i == DB - 1) mxc = max_across_halves(fmaxf(mh0, mh1)) * c2;
+        __builtin_amdgcn_sched_barrier(0);
+      }
       sc0 = n0;
       sc1 = n1;
       wait_vm_le(0);
