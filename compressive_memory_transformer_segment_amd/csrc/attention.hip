@@ -502,24 +502,90 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       }
     };
     f32x16 sc0, sc1;
-    {
-      KOps kq;
-      load_k(buf0, 0, kq);   // tile t0
-      sc0 = zero16();
-      sc1 = zero16();
-      qk_part(kq, 0, sc0, sc1);
-      load_k(buf0, KH, kq);
-      qk_part(kq, KH, sc0, sc1);   // tile 0
-    }
+    KOps kq;
+    load_k(buf0, 0, kq);   // tile t0
+    sc0 = zero16();
+    sc1 = zero16();
+    qk_part(kq, 0, sc0, sc1);
+    load_k(buf0, KH, kq);
+    qk_part(kq, KH, sc0, sc1);   // tile 0
     float mxc = tile_max(sc0, sc1);
     // Tile 2 (issued last in the previous item) is complete here in every wave, ahead of
     // its Q rows in the wave's load order; after the barrier it is visible to all.
     __builtin_amdgcn_s_barrier();
     KGrp kg0;
     if (tu > t0) {   // tile t0 + 1, the first group's k-steps
+      if constexpr (SPLIT) {
+        load_k(buf1, 0, kq);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 2 * KG; ++r) read_k(buf1, 0, r, kg0);
+        for (int r = 0; r < 2 * KG; ++r) read_k(buf1, 0, r, kg0);
+      }
     }
+    // The split-key kernel (one-segment calls) keeps the earlier schedule: per iteration,
+    // S^T(j + 1) in two k-step halves with tile j's exponentials, then the two PV halves.
+    // With its chunk bookkeeping live, the quarter schedule spills there and measured 6%
+    // slower per segment.
+    auto pstep_halves = [&](int j, auto bufc) __attribute__((always_inline)) {
+      constexpr int b = decltype(bufc)::value;
+      maybe_rescale(mxc);
+      if (j == t0 + 1) issue_mt();
+      issue(j + 3, bufp(IC<b + 3>{}));
+      const uint16_t* kt = bufp(bufc);
+      f32x16 n0 = zero16(), n1 = zero16();
+      bf16x8 p0, p1, p2, p3;
+      KOps kq2;
+      bf16x8 va[DB][2], vb[DB][2];
+      // phase 1
+      load_k(bufp(IC<b + 1>{}), KH, kq2);
+      qk_part(kq, 0, n0, n1);
+      half_exp(sc0, p0, p1);
+      // interleave: each MFMA followed by its share of the LDS reads and the VALU work
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);   // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2
+      v_operands(kt, 0, va);
+      qk_part(kq2, KH, n0, n1);
+      half_exp(sc1, p2, p3);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB / KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 3
+      v_operands(kt, 1, vb);
+      pv(va, p0, p1);
+      const float mh0 = half_max(n0);
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 4
+      load_k(bufp(IC<b + 2>{}), 0, kq);   // tile j + 2 (read but unused past the last tile)
+      pv(vb, p2, p3);
+      mxc = max_across_halves(fmaxf(mh0, half_max(n1))) * c2;
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS / DB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      sc0 = n0;
+      sc1 = n1;
+      wait_vm_le(0);
+      __builtin_amdgcn_s_barrier();
+    };
     auto pstep = [&](int j, auto bufc) __attribute__((always_inline)) {
       constexpr int b = decltype(bufc)::value;
       maybe_rescale(mxc);
@@ -585,10 +651,17 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       __builtin_amdgcn_s_barrier();
     };
     for (int j = t0; j < tu; j += 4) {
-      pstep(j, IC<0>{});
-      pstep(j + 1, IC<1>{});
-      pstep(j + 2, IC<2>{});
-      pstep(j + 3, IC<3>{});
+      if constexpr (SPLIT) {
+        pstep_halves(j, IC<0>{});
+        pstep_halves(j + 1, IC<1>{});
+        pstep_halves(j + 2, IC<2>{});
+        pstep_halves(j + 3, IC<3>{});
+      } else {
+        pstep(j, IC<0>{});
+        pstep(j + 1, IC<1>{});
+        pstep(j + 2, IC<2>{});
+        pstep(j + 3, IC<3>{});
+      }
     }
     // The four tiles from q0 on hold the diagonal of every wave: masked, one at a time;
     // tile jm's scores are already in sc0 / sc1.  A wave skips a tile whose keys all lie
