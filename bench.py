@@ -23,8 +23,12 @@ stream is fed one ``infini_attn_forward_segment`` call per segment (the streamin
 and the line also carries the device-memory evidence (used bytes after 1, 64, 256 and 512
 segments).
 
-Step time = median over the K timed steps (each bracketed by HIP events on the launch
-stream); the mean is reported next to it.
+Step time = the K timed steps back to back between one pair of HIP events on the launch
+stream, divided by K; the median of the same K steps each bracketed by its own events
+(each event record costs the GPU ~10 us) is reported next to it.  Before the warmup steps the GPU runs bf16
+matrix products for --spin-up-s seconds (0.5 by default): an idle MI355X raises its
+clocks over the first ~10 ms of sustained load, and without the spin-up the first steps
+after start run up to ~20% slower than the sustained rate that the line reports.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layer]
        [--per-segment] [--decode] [--backward] [--local-qk]
@@ -67,6 +71,8 @@ def parse():
                     help="also run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--per-segment", action="store_true",
                     help="streaming: one forward_segment call per segment of the stream (default workload: 1M tokens)")
+    ap.add_argument("--spin-up-s", type=float, default=0.5,
+                    help="seconds of bf16 matrix products before the warmup steps (clock ramp; 0: none)")
     ap.add_argument("--pool-segments", type=int, default=16,
                     help="distinct segments drawn for streams longer than this (used cyclically)")
     return ap.parse_args()
@@ -293,6 +299,7 @@ def main_decode(args):
         for t in range(N):
             layer.decode_step(Q[t], K[t], V[t], out=out, stream=stream)
 
+    spin_up(args.spin_up_s, torch.device("cuda", 0))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -325,6 +332,7 @@ def main_decode(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spin_up_s": args.spin_up_s,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -402,6 +410,7 @@ def main_backward(args):
         nonlocal outs
         outs = layer.backward(Q, K, V, dO, stream=stream)
 
+    spin_up(args.spin_up_s, torch.device("cuda", 0))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -433,6 +442,7 @@ def main_backward(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spin_up_s": args.spin_up_s,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -472,6 +482,23 @@ def main_backward(args):
                                          f"{el:.1f} s, scaled to all {w.heads} heads"}
     layer.close()
     print(json.dumps(rec), flush=True)
+
+
+def spin_up(seconds: float, dev) -> None:
+    """Bring the GPU from idle to its sustained clocks before the warmup steps: bf16
+    matrix products (not part of any step) for `seconds`."""
+    if seconds <= 0:
+        return
+    import torch
+    x = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            y = x @ x
+        torch.cuda.synchronize()
+    del x, y
+    torch.cuda.synchronize()
 
 
 def copy_probe(mib: int, dev) -> None:
@@ -519,19 +546,31 @@ def device_inputs(w, dev, pool_segments: int):
 
 
 def timed_steps(step, steps: int, stream):
-    """K steps between two synchronisations, each step bracketed by HIP events on the launch
-    stream; returns (per-step milliseconds, wall milliseconds of the K steps)."""
+    """The timed region: K steps back to back between one pair of HIP events on the launch
+    stream, between two synchronisations.  Then the same K steps once more, each between an
+    event pair of its own, for the per-step spread: an event record between two kernels
+    costs the GPU ~10 us (kernel traces show 0 us between the kernels of a step and ~10 us
+    where an event sits), so the per-step times carry that cost and the region does not.
+    Returns (mean milliseconds per step of the region, per-step milliseconds of the second
+    pass, wall milliseconds of the region)."""
     import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_start.record(stream)
+    for _ in range(steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    region_ms = e_start.elapsed_time(e_end) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in evs:
         e0.record(stream)
         step()
         e1.record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    return [e0.elapsed_time(e1) for e0, e1 in evs], wall_ms
+    return region_ms, [e0.elapsed_time(e1) for e0, e1 in evs], wall_ms
 
 
 def median(xs):
@@ -578,6 +617,7 @@ def main_per_segment(args):
         layer.forward_stream(Q, K, V, out=out, stream=stream)
 
     step_segments(record_mem=True)
+    spin_up(args.spin_up_s, torch.device("cuda", 0))
     for _ in range(args.warmup):
         step_segments()
         step_stream()
@@ -585,14 +625,13 @@ def main_per_segment(args):
     steps = max(3, args.steps // 4)
     print(f"[bench] {w.name} per segment: timing {steps} streams of {S} forward_segment calls", file=sys.stderr,
           flush=True)
-    seg_ms, wall_ms = timed_steps(step_segments, steps, stream)
-    str_ms, _ = timed_steps(step_stream, steps, stream)
+    ms, seg_ms, wall_ms = timed_steps(step_segments, steps, stream)
+    str_region, str_ms, _ = timed_steps(step_stream, steps, stream)
     layer.profile_enable(True)
     step_segments()
     prof = layer.profile_read()
     layer.profile_enable(False)
     torch.cuda.synchronize()
-    ms = median(seg_ms)
     tokens = w.batch * w.n_tokens
     att_ms, att_n = prof["attention"]
     seg_flops = profiling.attention_kernel_flops(w.batch, w.heads, w.head_dim, N, N)
@@ -604,8 +643,9 @@ def main_per_segment(args):
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
+        "spin_up_s": args.spin_up_s,
         "ms_per_step": ms,
-        "mean_ms_per_step": sum(seg_ms) / len(seg_ms),
+        "median_ms_per_step_evented": median(seg_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -625,8 +665,9 @@ def main_per_segment(args):
             "algorithmic_flops": seg_flops,
             "avg_launch_us": att_ms / att_n * 1e3,
         },
-        "forward_stream_same_stream": {"ms_per_step": median(str_ms), "value": tokens / (median(str_ms) / 1e3),
-                                       "per_segment_over_windowed": median(seg_ms) / median(str_ms)},
+        "forward_stream_same_stream": {"ms_per_step": str_region, "value": tokens / (str_region / 1e3),
+                                       "median_ms_per_step_evented": median(str_ms),
+                                       "per_segment_over_windowed": ms / str_region},
         "kernels_avg_us": {k: (t / n * 1e3 if n else None) for k, (t, n) in prof.items()},
         "wall_ms_per_step": wall_ms / steps,
         "memory": {"device_bytes": layer.device_bytes(),
@@ -690,14 +731,14 @@ def main():
         else:
             layer.forward_stream(Q, K, V, out=out, stream=stream)
 
+    spin_up(args.spin_up_s, torch.device("cuda", 0))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: warmup {args.warmup} done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    # timed region: K steps between two synchronisations, each step between two events
-    step_ms, wall_ms = timed_steps(step, args.steps, stream)
-    ms = median(step_ms)
+    # timed region: K steps between two synchronisations and one pair of events
+    ms, step_ms, wall_ms = timed_steps(step, args.steps, stream)
 
     # the same K steps with every kernel bracketed by HIP events on the launch stream
     layer.profile_enable(True)
@@ -735,8 +776,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spin_up_s": args.spin_up_s,
         "ms_per_step": ms,
-        "mean_ms_per_step": sum(step_ms) / len(step_ms),
+        "median_ms_per_step_evented": median(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -747,7 +789,7 @@ def main():
                    "update": w.update, "local_qk": bool(args.local_qk),
                    "projections": bool(args.layer), "d_model": d_model if args.layer else None,
                    "inputs": "exact seeded draws" if args.layer else inputs_desc,
-                   "step_time": "median of the timed steps", "parallelism": "none"},
+                   "step_time": "K steps between one pair of events, mean", "parallelism": "none"},
         "pct_bf16_peak": 100.0 * flops_step / (ms / 1e3) / profiling.PEAK_BF16_FLOPS,
         "roofline": {
             "kernel": rooflines[dominant]["kernel"],

@@ -297,7 +297,9 @@ hipError_t timed(infini_attn* h, int kind, hipStream_t st, F&& launch) {
   if (!h->profiling) return launch();
   while (h->ev_pool.size() < h->ev_used + 2) {
     hipEvent_t e;
-    const hipError_t err = hipEventCreate(&e);
+    // timing only: no system-scope fence (cache writeback and invalidate) when the event
+    // is recorded, which would otherwise add to the bracketed kernel's time
+    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (err != hipSuccess) return err;
     h->ev_pool.push_back(e);
   }
