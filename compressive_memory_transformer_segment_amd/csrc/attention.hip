@@ -181,6 +181,12 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, 0 .. 7
   const int l32 = lane & 31, hl = lane >> 5;
+  // Query block of this wave in an item: queries 32 qb .. 32 qb + 31.  In the plain output
+  // mode the waves run the diagonal tiles each on its own, and waves w and w + 4 (one SIMD)
+  // take blocks w and 7 - w, so that every SIMD has the same diagonal work (block b needs
+  // diagonal key tiles 0 .. b / 2).
+  constexpr bool kFree = MODE == 0 && !SPLIT;
+  const int qb = kFree ? (wave < 4 ? wave : 11 - wave) : wave;
 
   // the next item of this workgroup at or after round r whose query tile holds tokens
   auto find = [&](int& r, int& u_, int& qt_, int& n_, int& c_) __attribute__((always_inline)) -> bool {
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
 
   // ---- prologue of the first item: its Q rows straight into the B-operand registers,
   // tiles 0, 1 and 2 into buffers 0, 1 and 2.
-  load_q(qloc, seg_row0(u), n, qt * kBMA + 32 * wave);
+  load_q(qloc, seg_row0(u), n, qt * kBMA + 32 * qb);
   {
     const int t0_ = item_t0(c), te_ = item_te(qt, n, c);
     issue_tile(seg_row0(u), n, t0_, buf0);
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     const int64_t row0 = seg_row0(u);
     const int nkv = kv_tiles(qt, n);
     const int jm = q0 / kBN;   // unmasked tiles (a multiple of 4); tiles jm .. jm + 3 hold the diagonal
-    const int qw0 = q0 + 32 * wave;
+    const int qw0 = q0 + 32 * qb;
     const int q = qw0 + l32;
     // The item's steps: unmasked tiles [t0, tu), then, if it holds the diagonal (the
     // query tile's last chunk), the four diagonal steps jm .. jm + 3; tend ends the step
@@ -511,7 +517,10 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     qk_part(kq, KH, sc0, sc1);   // tile 0
     float mxc = tile_max(sc0, sc1);
     // Tile 2 (issued last in the previous item) is complete here in every wave, ahead of
-    // its Q rows in the wave's load order; after the barrier it is visible to all.
+    // its Q rows in the wave's load order; after the barrier it is visible to all.  (With
+    // the free-running diagonal the previous item's last copies follow its Q rows: waited
+    // for here.)
+    if constexpr (kFree) wait_vm_le(0);
     __builtin_amdgcn_s_barrier();
     KGrp kg0;
     if (tu > t0) {   // tile t0 + 1, the first group's k-steps
@@ -687,10 +696,39 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       __builtin_amdgcn_s_barrier();
     };
     if (last) {
-      mstep(jm, IC<0>{}, true);
-      mstep(jm + 1, IC<1>{}, false);
-      mstep(jm + 2, IC<2>{}, false);
-      mstep(jm + 3, IC<3>{}, false);
+      if constexpr (kFree) {
+        // Tile jm serves every wave; the step waits for all copies (tiles jm + 1 .. jm + 3
+        // complete), and after its barrier buffer 0 takes the next item's first tile.  Then
+        // every wave runs its remaining diagonal tiles and its epilogue without barriers;
+        // the item ends with one, after which buffers 1 and 2 take the next item's tiles.
+        if (jm == t0) issue_mt();   // an item without unmasked tiles: M^T_{s-1} not yet copied
+        issue(jm + 3, buf3);
+        mask_half(sc0, jm * kBN);
+        mask_half(sc1, jm * kBN + 32);
+        maybe_rescale(tile_max(sc0, sc1));
+        finish_tile(buf0, sc0, sc1);
+        wait_vm_le(0);
+        __builtin_amdgcn_s_barrier();
+        issue(tend, buf0);
+        auto dtile = [&](auto ic) __attribute__((always_inline)) {
+          const int j = jm + decltype(ic)::value, kv0 = j * kBN;
+          if (j < nkv && kv0 <= qw0 + 31) {
+            qk_tile(bufp(ic), sc0, sc1);
+            mask_half(sc0, kv0);
+            mask_half(sc1, kv0 + 32);
+            maybe_rescale(tile_max(sc0, sc1));
+            finish_tile(bufp(ic), sc0, sc1);
+          }
+        };
+        dtile(IC<1>{});
+        dtile(IC<2>{});
+        dtile(IC<3>{});
+      } else {
+        mstep(jm, IC<0>{}, true);
+        mstep(jm + 1, IC<1>{}, false);
+        mstep(jm + 2, IC<2>{}, false);
+        mstep(jm + 3, IC<3>{}, false);
+      }
     }
     // (A chunk without the diagonal has computed scores of the next item's first tile in
     // its last step: they are not used.)
@@ -845,7 +883,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       sq[ks] = as_bf16x8(u32x4{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
                                pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7])});
     }
-    if (has_next) load_q(qloc, row0n, nn, qtn * kBMA + 32 * wave);
+    if (has_next) load_q(qloc, row0n, nn, qtn * kBMA + 32 * qb);
     den = sum_across_halves(den);
     const float inv_den = 1.f / (den + a.eps);
     const float g = a.gate_g[h], omg = a.gate_omg[h];
@@ -924,6 +962,14 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
       }
     }
     }   // finish
+    if constexpr (kFree) {
+      // every wave's copy into buffer 0 is complete (only the next Q rows and the output
+      // stores may follow it); after the barrier no wave reads buffers 1 .. 3 or M^T
+      wait_vm_le(KS + 2 * DB);
+      __builtin_amdgcn_s_barrier();
+      issue(tend + 1, buf1);
+      issue(tend + 2, buf2);
+    }
     if (!has_next) break;
     r = rn;
     u = un;
