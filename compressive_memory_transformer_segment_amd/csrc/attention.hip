@@ -720,6 +720,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
             finish_tile(bufp(ic), sc0, sc1);
           }
         };
+        if (qb >= 4) __builtin_amdgcn_s_setprio(2);
         dtile(IC<1>{});
         dtile(IC<2>{});
         dtile(IC<3>{});
@@ -963,6 +964,7 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     }
     }   // finish
     if constexpr (kFree) {
+      __builtin_amdgcn_s_setprio(0);
       // every wave's copy into buffer 0 is complete (only the next Q rows and the output
       // stores may follow it); after the barrier no wave reads buffers 1 .. 3 or M^T
       wait_vm_le(KS + 2 * DB);
