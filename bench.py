@@ -24,8 +24,8 @@ and the line also carries the device-memory evidence (used bytes after 1, 64, 25
 segments).
 
 Step time = the K timed steps back to back between one pair of HIP events on the launch
-stream, divided by K; the median of the same K steps each bracketed by its own events
-(each event record costs the GPU ~10 us) is reported next to it.  Before the warmup steps the GPU runs bf16
+stream, divided by K (whole-job time); the median of the same K steps run once more, each
+bracketed by its own events, is reported next to it.  Before the warmup steps the GPU runs bf16
 matrix products for --spin-up-s seconds (0.5 by default): an idle MI355X raises its
 clocks over the first ~10 ms of sustained load, and without the spin-up the first steps
 after start run up to ~20% slower than the sustained rate that the line reports.
@@ -547,10 +547,9 @@ def device_inputs(w, dev, pool_segments: int):
 
 def timed_steps(step, steps: int, stream):
     """The timed region: K steps back to back between one pair of HIP events on the launch
-    stream, between two synchronisations.  Then the same K steps once more, each between an
-    event pair of its own, for the per-step spread: an event record between two kernels
-    costs the GPU ~10 us (kernel traces show 0 us between the kernels of a step and ~10 us
-    where an event sits), so the per-step times carry that cost and the region does not.
+    stream, between two synchronisations (whole-job time, no event between steps).  Then the
+    same K steps once more, each between an event pair of its own, for the per-step spread
+    (those records leave ~10 us of idle GPU between steps, outside each step's bracket).
     Returns (mean milliseconds per step of the region, per-step milliseconds of the second
     pass, wall milliseconds of the region)."""
     import torch
