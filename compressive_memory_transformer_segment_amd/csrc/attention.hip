@@ -181,11 +181,11 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, 0 .. 7
   const int l32 = lane & 31, hl = lane >> 5;
-  // Query block of this wave in an item: queries 32 qb .. 32 qb + 31.  In the plain output
+  // Query block of this wave in an item: queries 32 qb .. 32 qb + 31.  Outside the split-key
   // mode the waves run the diagonal tiles each on its own, and waves w and w + 4 (one SIMD)
   // take blocks w and 7 - w, so that every SIMD has the same diagonal work (block b needs
   // diagonal key tiles 0 .. b / 2).
-  constexpr bool kFree = MODE == 0 && !SPLIT;
+  constexpr bool kFree = !SPLIT;
   const int qb = kFree ? (wave < 4 ? wave : 11 - wave) : wave;
 
   // the next item of this workgroup at or after round r whose query tile holds tokens
@@ -965,9 +965,10 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     }   // finish
     if constexpr (kFree) {
       __builtin_amdgcn_s_setprio(0);
-      // every wave's copy into buffer 0 is complete (only the next Q rows and the output
-      // stores may follow it); after the barrier no wave reads buffers 1 .. 3 or M^T
-      wait_vm_le(KS + 2 * DB);
+      // every wave's copy into buffer 0 is complete (in the plain output mode only the next
+      // Q rows and the output stores may follow it); after the barrier no wave reads
+      // buffers 1 .. 3 or M^T
+      wait_vm_le(MODE == 0 ? KS + 2 * DB : 0);
       __builtin_amdgcn_s_barrier();
       issue(tend + 1, buf1);
       issue(tend + 2, buf2);

@@ -33,7 +33,7 @@ constexpr int kGM = 256;                      // tokens per tile
 constexpr int kGN = 256;                      // output features per tile
 constexpr int kGK = 32;                       // k per stage
 constexpr int kStage = (kGN + kGM) * kGK;     // elements of one buffer: [W tile | A tile]
-constexpr int kGroupM = 4;                    // token tiles per group of the tile order
+constexpr int kGroupM = 2;                    // token tiles per group of the tile order
 constexpr int kWN = 2;                        // waves along the features
 constexpr int kWM = kWaves / kWN;             // waves along the tokens
 constexpr int kTI = kGN / kWN / 32;           // 32-feature blocks per wave
