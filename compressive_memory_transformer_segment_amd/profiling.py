@@ -95,7 +95,7 @@ def _short(name: str) -> str:
     if "direct_copy_kernel" in name:
         return "torch direct_copy_kernel (input staging)"
     if "distribution" in name:
-        return "torch random fill (operand of the clock spin-up)"
+        return "torch random fill (bench inputs, spin-up operand)"
     return (name.split("(")[0] or "(unnamed)")[:80]
 
 
