@@ -144,6 +144,12 @@ __device__ __forceinline__ void buffer_st8_dev(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ u32x2 buffer_ld8_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voffset), 0, kCpolDevice));
 }
+__device__ __forceinline__ void buffer_st4_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voffset), 0, kCpolDevice);
+}
+__device__ __forceinline__ float buffer_ld4_dev(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voffset), 0, kCpolDevice));
+}
 
 // Buffer -> LDS copy of 16 bytes per lane (gfx950): lane i's bytes land at lds_base + 16 i
 // (lds_base wave-uniform); offsets past the resource end write zeros.

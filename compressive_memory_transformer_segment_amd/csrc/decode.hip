@@ -22,6 +22,12 @@
 // bf16 inputs, the bf16 M_{s-1}^T that the forward pass's retrieval uses (the chain keeps it
 // next to the fp32 state; one row of 2d bytes per value feature, split over 256 / d
 // threads), and with f32 inputs the fp32 M_{s-1} row by row with 16-byte loads.
+// With few (batch, head) pairs one workgroup per pair leaves most compute units idle and
+// each workgroup streams up to N cached rows alone; the keys are then split into chunks of
+// whole key batches over several workgroups per pair (SPLIT).  Each writes its partial
+// softmax state with device-coherent stores and counts itself with one atomic; the one that
+// counts last merges the chunks in chunk order (the same arithmetic whichever workgroup it
+// is) with the retrieval that chunk 0 wrote, and stores the gated output.  Nothing waits.
 #include <type_traits>
 
 #include "common.hpp"
@@ -97,7 +103,7 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool SPLIT>
 __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   using T = std::conditional_t<BF16, uint16_t, float>;
   constexpr int LPK = D / 8;           // lanes per key
@@ -109,8 +115,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   __shared__ __align__(16) float sq[D];        // sigma(q)
   __shared__ __align__(16) float red[RS][D];   // retrieval partial sums
   __shared__ float zden[4];
+  __shared__ int s_count;
 
-  const int bh = static_cast<int>(blockIdx.x), h = bh % a.H;
+  const int bh = SPLIT ? static_cast<int>(blockIdx.x) / a.nsplit : static_cast<int>(blockIdx.x);
+  const int cs = SPLIT ? static_cast<int>(blockIdx.x) - bh * a.nsplit : 0;   // key chunk
+  const bool lead = cs == 0;   // appends the token and computes the retrieval
+  const int h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = wave * KPW + lane / LPK;   // lane group: keys grp, grp + NG, ...
   const int e = lane % LPK;                  // values 8e .. 8e + 7 of each key
@@ -126,6 +136,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   constexpr int R = BF16 ? 8 : 4;
   constexpr int BATCH = NG * R;
   const int nk = a.p + 1;
+  const int k_lo = SPLIT ? cs * a.chunk : 0;           // this workgroup's keys [k_lo, k_hi)
+  const int k_hi = SPLIT ? min(k_lo + a.chunk, nk) : nk;
   auto load_batch = [&](int r0, Raw8<BF16> (&kb)[R], Raw8<BF16> (&vb)[R]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
@@ -137,10 +149,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     }
   };
   Raw8<BF16> kA[R], vA[R], kB[R], vB[R];
-  load_batch(0, kA, vA);
+  load_batch(k_lo, kA, vA);
 
   // append the token to the cache (read back by later launches only) and form sigma(q)
-  if (tid < D) {
+  if (tid < D && lead) {
     kc[static_cast<int64_t>(a.p) * D + tid] = kg[tid];
     vc[static_cast<int64_t>(a.p) * D + tid] = vg[tid];
     float qf;
@@ -158,7 +170,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   float numt = 0.f;
   __syncthreads();   // sq
-  if (!a.zero_state) {
+  if (!lead) {
+    // (other chunks: no retrieval)
+  } else if (!a.zero_state) {
     if constexpr (BF16) {
       const int dv = tid % D, sl = tid / D;
       const uint16_t* row = static_cast<const uint16_t*>(a.mt) + (static_cast<int64_t>(bh) * D + dv) * D + sl * (D / NS);
@@ -194,6 +208,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   } else if (tid == 0) {
     zden[0] = 0.f;
   }
+  // (a chunk other than 0 stores zeros here, unused)
   if constexpr (BF16) {
     red[tid / D][tid % D] = numt;
   } else {
@@ -219,7 +234,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kk[i], s);
       s = group_sum<LPK>(s);
-      if (t < nk) {   // uniform across the lane group
+      if (t < k_hi) {   // uniform across the lane group
         float vv[8];
         unpack8<BF16>(vb[u], vv);
         const float m_new = fmaxf(m, s);
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
       }
     }
   };
-  for (int r0 = 0; r0 < nk; r0 += 2 * BATCH) {
+  for (int r0 = k_lo; r0 < k_hi; r0 += 2 * BATCH) {
     load_batch(r0 + BATCH, kB, vB);
     consume(r0, kA, vA);
     load_batch(r0 + 2 * BATCH, kA, vA);
@@ -247,6 +262,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   __syncthreads();
 
   // ---- merge the lane groups, gate, store
+  if constexpr (!SPLIT) {
   if (tid < D) {
     float mx = -INFINITY;
 #pragma unroll
@@ -268,18 +284,83 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     if constexpr (BF16) og[tid] = f32_to_bf16(o);
     else og[tid] = o;
   }
+  } else {
+    // this chunk's partial state into slot cs of the pair (and the retrieval, chunk 0)
+    constexpr uint32_t SW = D + 2;   // floats per slot: accumulators, maximum, row sum
+    const auto rs = buffer_rsrc(a.sp_part + static_cast<int64_t>(bh) * kDecSlots * SW, kDecSlots * SW * 4u);
+    if (tid < D) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) mx = fmaxf(mx, part_m[g]);   // finite: group 0 holds key k_lo
+      float nd = 0.f, dd = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float w = __builtin_amdgcn_exp2f(part_m[g] - mx);
+        nd = fmaf(w, part_acc[g][tid], nd);
+        dd = fmaf(w, part_l[g], dd);
+      }
+      buffer_st4_dev(rs, (cs * SW + tid) * 4u, nd);
+      if (tid == 0) {
+        buffer_st4_dev(rs, (cs * SW + D) * 4u, mx);
+        buffer_st4_dev(rs, (cs * SW + D + 1) * 4u, dd);
+      }
+      if (lead) {
+        float nm = 0.f;
+#pragma unroll
+        for (int sl = 0; sl < (BF16 ? NS : RS); ++sl) nm += red[sl][tid];
+        buffer_st4_dev(rs, ((kDecSlots - 1) * SW + tid) * 4u, nm);
+        if (tid == 0) buffer_st4_dev(rs, ((kDecSlots - 1) * SW + D) * 4u, zden[0]);
+      }
+    }
+    wait_vm_lgkm0<0>();   // this thread's stores have completed
+    __syncthreads();      // ... every thread's
+    if (tid == 0) s_count = __hip_atomic_fetch_add(a.sp_cnt + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_count != a.nsplit - 1) return;   // another chunk's workgroup merges
+    if (tid < D) {
+      float mx = -INFINITY;
+      for (int c = 0; c < a.nsplit; ++c) mx = fmaxf(mx, buffer_ld4_dev(rs, (c * SW + D) * 4u));
+      float nd = 0.f, dd = 0.f;
+      for (int c = 0; c < a.nsplit; ++c) {
+        const float w = __builtin_amdgcn_exp2f(buffer_ld4_dev(rs, (c * SW + D) * 4u) - mx);
+        nd = fmaf(w, buffer_ld4_dev(rs, (c * SW + tid) * 4u), nd);
+        dd = fmaf(w, buffer_ld4_dev(rs, (c * SW + D + 1) * 4u), dd);
+      }
+      const float a_dot = nd / dd;
+      const float nm = buffer_ld4_dev(rs, ((kDecSlots - 1) * SW + tid) * 4u);
+      const float zd = buffer_ld4_dev(rs, ((kDecSlots - 1) * SW + D) * 4u);
+      const float a_mem = nm / (zd + a.eps);
+      const float o = a.gate_g[h] * a_mem + a.gate_omg[h] * a_dot;
+      T* og = static_cast<T*>(a.out) + static_cast<int64_t>(bh) * D;
+      if constexpr (BF16) og[tid] = f32_to_bf16(o);
+      else og[tid] = o;
+    }
+    if (tid == 0) __hip_atomic_store(a.sp_cnt + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kDecThreads);
+  const bool split = a.nsplit > 1;
+  if (split && (!a.sp_part || !a.sp_cnt || a.nsplit > kDecSplitMax || a.chunk % 128 != 0 ||
+                int64_t(a.chunk) * (a.nsplit - 1) >= a.p + 1))
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.B * a.H * (split ? a.nsplit : 1))), block(kDecThreads);
+  auto go = [&](auto d, auto bf) {
+    constexpr int D = decltype(d)::value;
+    constexpr bool BF = decltype(bf)::value;
+    if (split) hipLaunchKernelGGL((k_decode<D, BF, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_decode<D, BF, false>), grid, block, 0, st, a);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
   if (a.D == 128) {
-    if (a.bf16) hipLaunchKernelGGL((k_decode<128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_decode<128, false>), grid, block, 0, st, a);
+    if (a.bf16) go(I128{}, std::true_type{});
+    else go(I128{}, std::false_type{});
   } else if (a.D == 64) {
-    if (a.bf16) hipLaunchKernelGGL((k_decode<64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_decode<64, false>), grid, block, 0, st, a);
+    if (a.bf16) go(I64{}, std::true_type{});
+    else go(I64{}, std::false_type{});
   } else {
     return hipErrorInvalidValue;
   }

@@ -114,7 +114,19 @@ struct DecodeArgs {
   bool zero_state;        // M_{s-1}, z_{s-1} are zero (read as 0)
   float scale_log2;
   float eps;
+  // Split keys (few (batch, head) pairs): nsplit > 1 workgroups per pair, workgroup c
+  // taking keys [c chunk, (c + 1) chunk) of the p + 1; each writes its partial softmax state
+  // to sp_part (per pair kDecSlots slots of D + 2 floats: D accumulators, the maximum, the
+  // row sum; slot kDecSlots - 1: the retrieval numerator and denominator), counts itself in
+  // sp_cnt[pair], and the last to count merges the slots in order and writes the output.
+  float* sp_part;
+  int* sp_cnt;            // [B, H], zero between launches (the merging workgroup resets it)
+  int nsplit;
+  int chunk;              // a multiple of 128
 };
+
+constexpr int kDecSplitMax = 16;               // key chunks per pair at most
+constexpr int kDecSlots = kDecSplitMax + 1;    // partial slots per pair (+ the retrieval)
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 

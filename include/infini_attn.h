@@ -166,7 +166,7 @@ int infini_attn_set_beta(infini_attn_t h, const float* beta_host);
 
 /* Device bytes the handle holds: state + gate values + workspace, plus the layer scratch
  * once forward_layer has run (at most one window's worth) and the decode cache once
- * decode_step has run (one segment).  Independent of how many tokens have been processed:
+ * decode_step has run (one segment, plus the split-key partial slots with few pairs).  Independent of how many tokens have been processed:
  * the bounded-memory property of the compressive memory (summary page, "Multi-Head
  * Infini-Attention", memory footprint per layer: H (d_key d_value + d_key) numbers of
  * state, here in fp32, 66,048 bytes per head at d = 128). */
@@ -223,7 +223,11 @@ int infini_attn_forward_layer(infini_attn_t h, const void* x, const void* w_qkv,
  * flushed, the same state.
  *
  * decode_step: q, k, v, out are [B, H, d] (this token of every sequence), io_dtype; q, k,
- *   v 16-byte aligned; out must not overlap them.
+ *   v 16-byte aligned; out must not overlap them.  With fewer than 128 (batch, head) pairs
+ *   the keys of a long open segment are split over several workgroups per pair, whose
+ *   partial results the handle keeps in a library-owned buffer (B * H * 17 * (d + 2) floats
+ *   and B * H counters, allocated on the first step that splits; INFINI_ERR_OOM if that
+ *   fails).
  * decode_flush: writes an open partial segment to the memory (as forward_stream does with a
  *   short last segment); no-op when none is open.
  * decode_position: tokens of the open segment (0 .. N-1).

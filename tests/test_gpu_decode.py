@@ -37,6 +37,9 @@ CASES = [
     ("bf16-linear-n300", 1, 2, 128, 300, 310, "bf16", "linear"),   # several key rounds per token
     ("f32-linear-d128", 1, 2, 128, 40, 2 * 40 + 9, "f32", "linear"),
     ("f32-delta-d64", 2, 1, 64, 32, 3 * 32, "f32", "delta"),
+    # few (batch, head) pairs and more than 128 cached keys: the keys split over workgroups
+    ("bf16-delta-d64-n260-split", 1, 2, 64, 260, 270, "bf16", "delta"),
+    ("f32-linear-n300-split", 1, 2, 128, 300, 310, "f32", "linear"),
 ]
 
 
