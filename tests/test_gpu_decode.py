@@ -146,3 +146,23 @@ def test_full_size_decode_sampled_against_oracle():
                 ref, _, _ = orc.decode_token(Q[b, h, t], K[b, h, t], V[b, h, t], K[b, h, lo:t], V[b, h, lo:t], Ms, zs,
                                              beta[h], w.eps, scale)
                 gu.check_output(out[b, h, t][None], ref[None], tol, f"b{b} h{h} t{t}")
+
+
+def test_split_decode_is_deterministic():
+    """One sequence, 2 heads, d=128, a 700-token segment: every token past the 256th splits
+    its keys over several workgroups, whose partial states are merged in chunk order by
+    whichever finishes last; two runs give the same bits."""
+    gu.require_gpu()
+    base = wl.WORKLOADS[wl.THROUGHPUT_WORKLOAD]
+    N = 700
+    w = wl.Workload("decode-split-det", 1, 2, base.head_dim, N, N, "bf16", "linear", seed=53)
+    gu.note(f"[decode] split determinism: {w.name}")
+    Q, K, V = wl.stream_inputs(w)
+    beta = wl.beta_for(w)
+    runs = []
+    for _ in range(2):
+        with binding.InfiniAttention(1, w.heads, w.head_dim, N, update="linear", eps=w.eps, beta=beta) as layer:
+            runs.append(_decode_all(layer, Q, K, V, "bf16", flush=False))
+    assert np.array_equal(runs[0], runs[1])
+    O_ref, _, _, _ = orc.decode_stream(Q, K, V, beta, N, "linear", eps=w.eps)
+    gu.check_output(runs[0], O_ref, gu.tol_for("bf16"))
