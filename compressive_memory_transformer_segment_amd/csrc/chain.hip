@@ -20,20 +20,24 @@ namespace infini {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kChainFillWorkgroups = 256;   // below this many 16-row workgroups, use 8 rows
 
-// Linear rule.  A workgroup owns 16 rows of M^T (value features rb .. rb + 15) of one
+// Linear rule.  A workgroup owns RB rows of M^T (value features rb .. rb + RB - 1) of one
 // (b,h); thread (r, cg) owns row rb + r, columns EPT cg .. EPT cg + EPT - 1 (EPT = D / 16),
 // so a wave reads four whole rows of every U^T partial.  M ([d_key][d_value]) is read
 // and written once per window through an LDS transpose, with 16-byte accesses that cover
-// the workgroup's 64-byte pieces of M's rows.
-template <int D, int CHK, bool BF16>
-__global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
-  constexpr int RB = 16;                  // rows of M^T per workgroup
+// the workgroup's 4 RB-byte pieces of M's rows.  RB = 16 (256 threads), or 8 (128 threads:
+// twice the workgroups, for few (b,h) pairs, where each workgroup's stream of partials
+// sets the time).
+template <int D, int CHK, bool BF16, int RB>
+__global__ __launch_bounds__(16 * RB) void k_chain_linear(const WindowArgs a) {
+  constexpr int NT = 16 * RB;             // threads
   constexpr int EPT = D / 16;             // elements per thread
   constexpr int CG = D / EPT;             // thread columns per row (16)
+  constexpr int TPR = RB / 4;             // threads per row of M in the transposing accesses
+  constexpr int RPP = NT / TPR;           // rows of M per pass of those accesses
   constexpr int kBatch = CHK >= 2 ? 16 / CHK : 8;    // segments whose partials are loaded together
-  static_assert(RB * CG == kThreads, "one thread per (row, column group)");
+  static_assert(RB * CG == NT && D % RPP == 0 && NT >= D, "one thread per (row, column group)");
   __shared__ float tr[D][RB + 1];         // M[i][rb + c] at tr[i][c]
   const int BH = a.B * a.H;
   const int bh = blockIdx.x / (D / RB);
@@ -50,13 +54,13 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) m[e] = 0.f;
   } else {
-    // thread t: row t / 4 (+ 64 k) of M, columns rb + 4 (t % 4) .. +3
+    // thread t: row t / TPR (+ RPP k) of M, columns rb + 4 (t % TPR) .. +3
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      const int i = tid / 4 + 64 * k;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(Mb + static_cast<int64_t>(i) * D + 4 * (tid % 4));
+    for (int k = 0; k < D / RPP; ++k) {
+      const int i = tid / TPR + RPP * k;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(Mb + static_cast<int64_t>(i) * D + 4 * (tid % TPR));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) tr[i][4 * (tid % 4) + c] = v[c];
+      for (int c = 0; c < 4; ++c) tr[i][4 * (tid % TPR) + c] = v[c];
     }
     __syncthreads();
 #pragma unroll
@@ -141,12 +145,12 @@ __global__ __launch_bounds__(kThreads) void k_chain_linear(const WindowArgs a) {
   for (int e = 0; e < EPT; ++e) tr[i0 + e][r] = m[e];
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) {
-    const int i = tid / 4 + 64 * k;
+  for (int k = 0; k < D / RPP; ++k) {
+    const int i = tid / TPR + RPP * k;
     f32x4 v;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = tr[i][4 * (tid % 4) + c];
-    *reinterpret_cast<f32x4*>(Mb + static_cast<int64_t>(i) * D + 4 * (tid % 4)) = v;
+    for (int c = 0; c < 4; ++c) v[c] = tr[i][4 * (tid % TPR) + c];
+    *reinterpret_cast<f32x4*>(Mb + static_cast<int64_t>(i) * D + 4 * (tid % TPR)) = v;
   }
 }
 
@@ -385,12 +389,18 @@ hipError_t launch_chain_d(const WindowArgs& a, hipStream_t st) {
     else if (a.chk <= 4) go(std::integral_constant<int, 4>{}, std::true_type{});
     else go(std::integral_constant<int, 8>{}, std::true_type{});
   } else {
-    const dim3 grid(BH * (D / 16));
-    if (!a.bf16) hipLaunchKernelGGL((k_chain_linear<D, 1, false>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk == 1) hipLaunchKernelGGL((k_chain_linear<D, 1, true>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk == 2) hipLaunchKernelGGL((k_chain_linear<D, 2, true>), grid, dim3(kThreads), 0, st, a);
-    else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_linear<D, 4, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_chain_linear<D, 8, true>), grid, dim3(kThreads), 0, st, a);
+    // 8 rows per workgroup (128 threads) while (b,h) pairs x D / 16 leave compute units idle
+    auto go = [&](auto rbc) {
+      constexpr int RB = decltype(rbc)::value;
+      const dim3 grid(BH * (D / RB)), block(16 * RB);
+      if (!a.bf16) hipLaunchKernelGGL((k_chain_linear<D, 1, false, RB>), grid, block, 0, st, a);
+      else if (a.chk == 1) hipLaunchKernelGGL((k_chain_linear<D, 1, true, RB>), grid, block, 0, st, a);
+      else if (a.chk == 2) hipLaunchKernelGGL((k_chain_linear<D, 2, true, RB>), grid, block, 0, st, a);
+      else if (a.chk <= 4) hipLaunchKernelGGL((k_chain_linear<D, 4, true, RB>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_chain_linear<D, 8, true, RB>), grid, block, 0, st, a);
+    };
+    if (BH * (D / 16) < kChainFillWorkgroups && D >= 64 && 16 * 8 >= D) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, 16>{});
   }
   return hipGetLastError();
 }
