@@ -720,6 +720,8 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
             finish_tile(bufp(ic), sc0, sc1);
           }
         };
+        // the wave of each SIMD with the longer rest (blocks 4 .. 7: two or three more tiles,
+        // against none or one) issues first until its item ends
         if (qb >= 4) __builtin_amdgcn_s_setprio(2);
         dtile(IC<1>{});
         dtile(IC<2>{});
@@ -735,8 +737,10 @@ __global__ __launch_bounds__(kThreadsA, 1) __attribute__((amdgpu_waves_per_eu(2,
     // its last step: they are not used.)
 
     // ---------------------------------------------------------------- epilogue
-    // M^T_{s-1} is in bufm.  The next item's first tiles are in buffers 0 .. 2; this
-    // item's Q registers are free once sigma(Q) is formed, and take the next item's Q.
+    // M^T_{s-1} is in bufm.  The next item's first tiles are in buffers 0 .. 2 (with the
+    // free-running diagonal only its first, in buffer 0: the other two are copied after the
+    // item's closing barrier); this item's Q registers are free once sigma(Q) is formed, and
+    // take the next item's Q.
     bool finish = true;
     if constexpr (SPLIT) {
       const int nchunks = sd.kc.div(nkv + kc - 1);
