@@ -65,9 +65,10 @@ __device__ void z_before(const WindowArgs& a, const UnitPos& p, float* zs) {
 }
 
 // Key sums only (the delta rule needs z_{s-1} before its state pass): one workgroup per
-// (unit, chunk), 64-token sub-tiles of K loaded one ahead of the one being summed; each
-// thread sums sigma(K) over its rows and 8 features, then the row groups are reduced in
-// group order.
+// (unit, chunk), 64-token sub-tiles of K loaded three ahead of the one being summed (four
+// register sets; the sub-tile loop is unrolled by four, so each set is a fixed register
+// range and the compiler waits only for the oldest); each thread sums sigma(K) over its rows
+// and 8 features, then the row groups are reduced in group order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_keysum_bf16(const WindowArgs a) {
   constexpr int DQ = D / 8;              // threads per token row (8 features each)
@@ -83,34 +84,47 @@ __global__ __launch_bounds__(kThreads) void k_keysum_bf16(const WindowArgs a) {
   const int64_t seg_base = (static_cast<int64_t>(p.bh) * a.T + p.tok0) * D;
   const int t_begin = c * a.ch;
   const int t_end = min(t_begin + a.ch, p.n);
-  // rows past the chunk end read as zeros; they are skipped below
+  // rows past the chunk end read as zeros (the buffer range); they are skipped below
   const auto krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + seg_base, static_cast<uint32_t>(max(t_end, 0)) * D * 2);
 
   float zacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
-  u32x4 kcur[RPT];
   auto load = [&](int ts, u32x4 (&kd)[RPT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
       kd[r] = buffer_ld16(krs, (static_cast<uint32_t>(ts + tq * RPT + r) * D + dq * 8) * 2);
   };
-  if (t_begin < t_end) load(t_begin, kcur);
-  for (int ts = t_begin; ts < t_end; ts += kSub) {
-    u32x4 knext[RPT];
-    if (ts + kSub < t_end) load(ts + kSub, knext);
+  auto add = [&](int ts, const u32x4 (&kd)[RPT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       if (ts + tq * RPT + r < t_end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          zacc[2 * i] += elu_plus_one(bf16lo_to_f32(kcur[r][i]));
-          zacc[2 * i + 1] += elu_plus_one(bf16hi_to_f32(kcur[r][i]));
+          zacc[2 * i] += elu_plus_one(bf16lo_to_f32(kd[r][i]));
+          zacc[2 * i + 1] += elu_plus_one(bf16hi_to_f32(kd[r][i]));
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) kcur[r] = knext[r];
+  };
+  // sub-tiles past the chunk end load zeros (their rows are skipped): every load is issued
+  const int nsub = t_end > t_begin ? ((t_end - t_begin + 4 * kSub - 1) / (4 * kSub)) * 4 : 0;
+  u32x4 k0[RPT], k1[RPT], k2[RPT], k3[RPT];
+  if (nsub > 0) {
+    load(t_begin, k0);
+    load(t_begin + kSub, k1);
+    load(t_begin + 2 * kSub, k2);
+  }
+  for (int i = 0; i < nsub; i += 4) {
+    const int ts = t_begin + i * kSub;
+    load(ts + 3 * kSub, k3);
+    add(ts, k0);
+    load(ts + 4 * kSub, k0);
+    add(ts + kSub, k1);
+    load(ts + 5 * kSub, k1);
+    add(ts + 2 * kSub, k2);
+    load(ts + 6 * kSub, k2);
+    add(ts + 3 * kSub, k3);
   }
   const int64_t slot = static_cast<int64_t>(u) * a.chk + c;
 #pragma unroll
