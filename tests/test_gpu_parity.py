@@ -27,6 +27,9 @@ CASES = [
     ("bf16-linear-one-partial-segment", 1, 2, 128, 2048, 300, "bf16", "linear"),
     ("bf16-linear-one-token", 1, 1, 128, 2048, 1, "bf16", "linear"),
     ("bf16-delta-n2048-3seg", 1, 2, 128, 2048, 2 * 2048 + 1000, "bf16", "delta"),
+    # segments longer than the 2K of the pages' runs: 16 query tiles, 64 key tiles on the diagonal
+    ("bf16-linear-n4096-ragged", 1, 1, 128, 4096, 4096 + 1333, "bf16", "linear"),
+    ("bf16-delta-n4096-ragged", 1, 1, 128, 4096, 4096 + 1333, "bf16", "delta"),
     # enough (batch, head) pairs for the delta chain's 16-rows-per-workgroup form
     ("bf16-delta-d128-b4h8-wide-chain", 4, 8, 128, 128, 3 * 128 + 50, "bf16", "delta"),
     ("bf16-delta-d64-b8h8-wide-chain", 8, 8, 64, 64, 4 * 64 + 5, "bf16", "delta"),

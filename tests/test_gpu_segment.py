@@ -50,6 +50,9 @@ CASES = [
     ("b2-h2-d64-n1024-linear", 2, 2, 64, 1024, (1024, 700, 1024), "linear"),
     ("b2-h2-d64-n1024-delta", 2, 2, 64, 1024, (1024, 1024, 333), "delta"),
     ("h3-d128-n2048-ragged", 1, 3, 128, 2048, (1, 65, 300, 2047, 2048), "linear"),
+    # 4K segments: split-key calls with 8 key chunks on the last query tiles
+    ("h2-d128-n4096-linear", 1, 2, 128, 4096, (4096, 2500), "linear"),
+    ("h2-d128-n4096-delta", 1, 2, 128, 4096, (4096, 4096, 1500), "delta"),
 ]
 
 
