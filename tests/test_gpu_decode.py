@@ -40,6 +40,9 @@ CASES = [
     # few (batch, head) pairs and more than 128 cached keys: the keys split over workgroups
     ("bf16-delta-d64-n260-split", 1, 2, 64, 260, 270, "bf16", "delta"),
     ("f32-linear-n300-split", 1, 2, 128, 300, 310, "f32", "linear"),
+    # 4K segments: up to 16 chunks of 256 keys per pair, the most a token splits into
+    ("bf16-linear-n4096-split16", 1, 1, 128, 4096, 4096 + 300, "bf16", "linear"),
+    ("bf16-delta-n4096-split16", 1, 1, 128, 4096, 4096 + 40, "bf16", "delta"),
 ]
 
 
